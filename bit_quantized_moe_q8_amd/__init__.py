@@ -1,0 +1,311 @@
+"""Python binding of libpq (include/pq.h): packed 1-bit-class MoE expert kernels for MI355X.
+
+Argument marshalling only: each function checks tensor dtypes, devices and
+contiguity, then calls the C entry point of the same name on torch's current
+HIP stream.  Every step of the computation runs in the library's HIP kernels;
+there is no host fallback, and importing this module fails if libpq.so has not
+been built (``python -m bit_quantized_moe_q8_amd._build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpq.so")
+
+PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE, PQ_ERR_ALIGN, PQ_ERR_UNSUPPORTED, PQ_ERR_HIP = range(6)
+PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16 = 0, 1, 2
+
+EXPORTS = (
+    "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert",
+    "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_gemm_dequant_tile",
+    "pq_moe_combine", "pq_status_str", "pq_abi_version",
+)
+
+
+class PQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%d)" % (fn, status_str(status), status))
+        self.status = status
+
+
+class TernaryW(ctypes.Structure):
+    _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("n_experts", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class Grid1W(ctypes.Structure):
+    _fields_ = [("qs", ctypes.c_void_p), ("qh", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("grid", ctypes.c_void_p),
+                ("n_experts", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class Groups(ctypes.Structure):
+    _fields_ = [("expert_offsets", ctypes.c_void_p), ("sorted_assign", ctypes.c_void_p),
+                ("active_experts", ctypes.c_void_p), ("n_active", ctypes.c_void_p),
+                ("n_tokens", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("isums", ctypes.c_void_p), ("isums_up", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("u", ctypes.c_void_p), ("h", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpq.so is not built; run: python -m bit_quantized_moe_q8_amd._build")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i32 = ctypes.c_void_p, ctypes.c_int32
+    sig = {
+        "pq_quantize_act_q8": [p, i32, i32, p, p, p],
+        "pq_moe_route_topk": [p, i32, i32, i32, p, p, p],
+        "pq_group_tokens_by_expert": [p, i32, i32, i32, p, p, p, p, p],
+        "pq_moe_matvec_ternary": [ctypes.POINTER(TernaryW), ctypes.POINTER(TernaryW),
+                                  ctypes.POINTER(Groups), p, p, i32, i32, p, p,
+                                  ctypes.POINTER(Debug), p],
+        "pq_moe_matvec_grid1": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
+                                ctypes.POINTER(Groups), p, p, i32, i32, p, p,
+                                ctypes.POINTER(Debug), p],
+        "pq_moe_gemm_dequant_tile": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
+                                     ctypes.POINTER(Groups), p, i32, i32, p,
+                                     ctypes.POINTER(Debug), p],
+        "pq_moe_combine": [p, p, i32, i32, i32, p, p],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.pq_status_str.argtypes = [ctypes.c_int]
+    L.pq_status_str.restype = ctypes.c_char_p
+    L.pq_abi_version.restype = ctypes.c_int32
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def gemm_available() -> bool:
+    """True once the prefill GEMM kernel is part of the build."""
+    return GEMM_READY
+
+
+GEMM_READY = False
+
+
+def status_str(status: int) -> str:
+    return _lib.pq_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.pq_abi_version())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn: str, rc: int):
+    if rc != PQ_OK:
+        raise PQError(fn, rc)
+
+
+def _dt(t, *dtypes):
+    if t.dtype not in dtypes:
+        raise TypeError("expected dtype in %s, got %s" % (dtypes, t.dtype))
+
+
+@dataclass
+class TernaryWeights:
+    """Packed ternary expert tensor: qs uint8 [E][rows][cols/4], d fp16 bits [E][rows][cols/256]."""
+    qs: torch.Tensor
+    d: torch.Tensor
+
+    @property
+    def shape(self):
+        E, rows, q = self.qs.shape
+        return E, rows, q * 4
+
+    def cstruct(self) -> TernaryW:
+        _dt(self.qs, torch.uint8)
+        _dt(self.d, torch.int16, torch.float16, torch.uint16)
+        E, rows, cols = self.shape
+        return TernaryW(_ptr(self.qs), _ptr(self.d), E, rows, cols)
+
+
+@dataclass
+class Grid1Weights:
+    """Packed grid1 expert tensor: qs uint8 [E][rows][cols/8], qh [E][rows][cols/32],
+    d fp16 bits [E][rows][cols/256], grid int8 [2048][8]."""
+    qs: torch.Tensor
+    qh: torch.Tensor
+    d: torch.Tensor
+    grid: torch.Tensor
+
+    @property
+    def shape(self):
+        E, rows, q = self.qs.shape
+        return E, rows, q * 8
+
+    def cstruct(self) -> Grid1W:
+        _dt(self.qs, torch.uint8)
+        _dt(self.qh, torch.int16, torch.uint16)
+        _dt(self.d, torch.int16, torch.float16, torch.uint16)
+        _dt(self.grid, torch.int8)
+        E, rows, cols = self.shape
+        return Grid1W(_ptr(self.qs), _ptr(self.qh), _ptr(self.d), _ptr(self.grid), E, rows, cols)
+
+
+@dataclass
+class GroupBuffers:
+    """Grouping of assignments by expert (filled by group_tokens_by_expert)."""
+    expert_offsets: torch.Tensor  # int32 [E+1]
+    sorted_assign: torch.Tensor   # int32 [A]
+    active_experts: torch.Tensor  # int32 [E]
+    n_active: torch.Tensor        # int32 [1]
+    n_tokens: int
+    top_k: int
+    n_experts: int
+
+    @staticmethod
+    def empty(n_tokens: int, top_k: int, n_experts: int, device="cuda"):
+        i32 = torch.int32
+        return GroupBuffers(torch.empty(n_experts + 1, dtype=i32, device=device),
+                            torch.empty(max(n_tokens * top_k, 1), dtype=i32, device=device),
+                            torch.empty(n_experts, dtype=i32, device=device),
+                            torch.empty(1, dtype=i32, device=device),
+                            n_tokens, top_k, n_experts)
+
+    def cstruct(self) -> Groups:
+        return Groups(_ptr(self.expert_offsets), _ptr(self.sorted_assign),
+                      _ptr(self.active_experts), _ptr(self.n_active),
+                      self.n_tokens, self.top_k, self.n_experts)
+
+
+def _debug_struct(dbg):
+    if dbg is None:
+        return None
+    return ctypes.byref(Debug(*[_ptr(dbg.get(k)) for k in ("isums", "isums_up", "g", "u", "h")]))
+
+
+# ------------------------------------------------------------------ entry points
+
+def quantize_act_q8(x: torch.Tensor, xq: torch.Tensor = None, xd: torch.Tensor = None):
+    """pq_quantize_act_q8: x float32 [rows][cols] -> (xq int8 [rows][cols], xd float32 [rows][cols/32])."""
+    _dt(x, torch.float32)
+    rows, cols = x.shape
+    if xq is None:
+        xq = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if xd is None:
+        xd = torch.empty((rows, cols // 32), dtype=torch.float32, device=x.device)
+    _check("pq_quantize_act_q8", _lib.pq_quantize_act_q8(_ptr(x), rows, cols, _ptr(xq), _ptr(xd), _stream()))
+    return xq, xd
+
+
+def moe_route_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor = None, w: torch.Tensor = None):
+    """pq_moe_route_topk: logits float32 [T][E] -> (ids int32 [T][k], w float32 [T][k])."""
+    _dt(logits, torch.float32)
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _check("pq_moe_route_topk", _lib.pq_moe_route_topk(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(w), _stream()))
+    return ids, w
+
+
+def group_tokens_by_expert(ids: torch.Tensor, n_experts: int, groups: GroupBuffers = None) -> GroupBuffers:
+    """pq_group_tokens_by_expert: ids int32 [T][k] -> GroupBuffers."""
+    _dt(ids, torch.int32)
+    T, k = ids.shape
+    if groups is None:
+        groups = GroupBuffers.empty(T, k, n_experts, ids.device)
+    g = groups
+    _check("pq_group_tokens_by_expert", _lib.pq_group_tokens_by_expert(
+        _ptr(ids), T, k, n_experts, _ptr(g.expert_offsets), _ptr(g.sorted_assign),
+        _ptr(g.active_experts), _ptr(g.n_active), _stream()))
+    return groups
+
+
+def _matvec(fn_name, w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg):
+    _dt(xq, torch.int8)
+    _dt(xd, torch.float32)
+    E, rows, cols = w.shape
+    A = groups.n_tokens * groups.top_k
+    dev = xq.device
+    if out0 is None:
+        if epilogue == PQ_EPI_F32:
+            out0 = torch.empty((A, rows), dtype=torch.float32, device=dev)
+        else:
+            out0 = torch.empty((A, rows), dtype=torch.int8, device=dev)
+    if out1 is None and epilogue == PQ_EPI_SWIGLU_Q8:
+        out1 = torch.empty((A, rows // 32), dtype=torch.float32, device=dev)
+    ws = w.cstruct()
+    wu = w_up.cstruct() if w_up is not None else None
+    gs = groups.cstruct()
+    rc = getattr(_lib, fn_name)(ctypes.byref(ws), ctypes.byref(wu) if wu is not None else None,
+                                ctypes.byref(gs), _ptr(xq), _ptr(xd), int(act_by_token), int(epilogue),
+                                _ptr(out0), _ptr(out1), _debug_struct(dbg), _stream())
+    _check(fn_name, rc)
+    return out0, out1
+
+
+def moe_matvec_ternary(w: TernaryWeights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,
+                       epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
+    """pq_moe_matvec_ternary (see include/pq.h)."""
+    return _matvec("pq_moe_matvec_ternary", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
+
+
+def moe_matvec_grid1(w: Grid1Weights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,
+                     epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
+    """pq_moe_matvec_grid1 (see include/pq.h)."""
+    return _matvec("pq_moe_matvec_grid1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
+
+
+def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: torch.Tensor,
+                          act_by_token: bool, epilogue: int = PQ_EPI_F32, out0=None, dbg: dict = None):
+    """pq_moe_gemm_dequant_tile: x bf16 (torch.bfloat16 or int16 bits)."""
+    _dt(x_bf16, torch.bfloat16, torch.int16, torch.uint16)
+    E, rows, cols = w.shape
+    A = groups.n_tokens * groups.top_k
+    if out0 is None:
+        dt = torch.float32 if epilogue == PQ_EPI_F32 else torch.bfloat16
+        out0 = torch.empty((A, rows), dtype=dt, device=x_bf16.device)
+    ws = w.cstruct()
+    wu = w_up.cstruct() if w_up is not None else None
+    gs = groups.cstruct()
+    rc = _lib.pq_moe_gemm_dequant_tile(ctypes.byref(ws), ctypes.byref(wu) if wu is not None else None,
+                                       ctypes.byref(gs), _ptr(x_bf16), int(act_by_token), int(epilogue),
+                                       _ptr(out0), _debug_struct(dbg), _stream())
+    _check("pq_moe_gemm_dequant_tile", rc)
+    return out0
+
+
+def moe_combine(out_assign: torch.Tensor, topk_w: torch.Tensor, top_k: int, y: torch.Tensor = None):
+    """pq_moe_combine: out_assign float32 [T*k][rows], topk_w float32 [T][k] -> y float32 [T][rows]."""
+    _dt(out_assign, torch.float32)
+    _dt(topk_w, torch.float32)
+    A, rows = out_assign.shape
+    T = A // top_k
+    if y is None:
+        y = torch.empty((T, rows), dtype=torch.float32, device=out_assign.device)
+    _check("pq_moe_combine", _lib.pq_moe_combine(_ptr(out_assign), _ptr(topk_w), T, top_k, rows, _ptr(y), _stream()))
+    return y

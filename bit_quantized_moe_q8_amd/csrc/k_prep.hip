@@ -1,0 +1,251 @@
+// Small per-step kernels of the MoE expert path: q8 activation quantization,
+// top-k routing, stable grouping by expert, and the weighted combine.
+#include "pq_device.hpp"
+#include "pq_internal.hpp"
+
+namespace pqk {
+
+// ---------------------------------------------------------------------------
+// q8 activations (Parakon Runtime README, "How it works": int8 activations).
+// Eight lanes per 32-value block, four floats per lane (one 16-byte load):
+// block max via three xor shuffles, d = max/127, q = round_half_away(x/d).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_q8(const float* __restrict__ x,
+                                                     int64_t n_blocks,
+                                                     int8_t* __restrict__ xq,
+                                                     float* __restrict__ xd) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t blk = t >> 3;
+    const bool ok = blk < n_blocks;
+    float4 v = ok ? reinterpret_cast<const float4*>(x)[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    const float d = a / 127.0f;
+    if (!ok) return;
+    const uint32_t q = (static_cast<uint32_t>(q8_value(v.x, d)) & 0xffu) |
+                       ((static_cast<uint32_t>(q8_value(v.y, d)) & 0xffu) << 8) |
+                       ((static_cast<uint32_t>(q8_value(v.z, d)) & 0xffu) << 16) |
+                       ((static_cast<uint32_t>(q8_value(v.w, d)) & 0xffu) << 24);
+    reinterpret_cast<uint32_t*>(xq)[t] = q;
+    if ((t & 7) == 0) xd[blk] = d;
+}
+
+hipError_t launch_quantize_q8(const float* x, int64_t n_blocks, int8_t* xq, float* xd,
+                              hipStream_t s) {
+    if (n_blocks == 0) return hipSuccess;
+    const int64_t threads = n_blocks * 8;
+    const unsigned grid = static_cast<unsigned>((threads + 255) / 256);
+    hipLaunchKernelGGL(k_quantize_q8, dim3(grid), dim3(256), 0, s, x, n_blocks, xq, xd);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router top-k + softmax over the selected logits (no dropping: llama-modchip
+// summary, "Key highlights").  One wave per token; each lane holds the logits
+// e = lane + 64 j.  k rounds of a wave arg-max (ties -> lower expert id).
+// ---------------------------------------------------------------------------
+constexpr int kRouteMaxPerLane = 16;  // n_experts <= 1024
+
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
+                                                    int E, int k, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;  // whole wave leaves; no workgroup barrier below
+    const float* l = logits + static_cast<int64_t>(t) * E;
+    float v[kRouteMaxPerLane];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int j = 0; j < kRouteMaxPerLane; ++j) {
+        const int e = lane + 64 * j;
+        v[j] = (e < E) ? l[e] : 0.0f;
+        if (e < E) avail |= 1u << j;
+    }
+    float my_v = 0.0f;
+    int my_i = 0;
+    for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxPerLane; ++j) {
+            if (((avail >> j) & 1u) && (bi < 0 || v[j] > bv)) {
+                bv = v[j];
+                bi = lane + 64 * j;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+        if (lane == r) {
+            my_v = bv;
+            my_i = bi;
+        }
+    }
+    const float l0 = __shfl(my_v, 0);
+    const float ex = (lane < k) ? expf(my_v - l0) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane < k) {
+        ids[static_cast<int64_t>(t) * k + lane] = my_i;
+        w[static_cast<int64_t>(t) * k + lane] = ex / sum;
+    }
+}
+
+hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, int top_k,
+                             int32_t* ids, float* w, hipStream_t s) {
+    if (n_tokens == 0) return hipSuccess;
+    const unsigned grid = static_cast<unsigned>((n_tokens + 3) / 4);
+    hipLaunchKernelGGL(k_route_topk, dim3(grid), dim3(256), 0, s, logits, n_tokens, n_experts,
+                       top_k, ids, w);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Stable grouping by expert (grouped MoE path: pxq_llama README, "What's
+// PXQ?").  One workgroup of 8 waves.  Wave w owns the contiguous assignment
+// range [w*C, (w+1)*C):
+//   1. per-wave histograms hist[w][e] in LDS;
+//   2. per expert: exclusive prefix over waves, then an exclusive scan over
+//      experts gives expert_offsets, and hist[w][e] becomes the first output
+//      slot of wave w's assignments of expert e;
+//   3. each wave walks its range 64 at a time in order; lanes with equal keys
+//      are found with one ballot per key bit, the rank among them is a
+//      popcount of the lower lanes, and the highest lane of each key advances
+//      hist[w][e].  Ranks follow assignment order, so the sort is stable.
+// ---------------------------------------------------------------------------
+constexpr int kGroupWaves = 8;
+constexpr int kGroupThreads = kGroupWaves * 64;
+constexpr int kGroupMaxExperts = 1024;
+
+__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* wave_tot) {
+    // kGroupThreads threads, each scanning ceil(1024/512) = 2 consecutive values
+    // is avoided: caller passes one value per thread for e = tid and e = tid + 512.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += wave_tot[i];
+    __syncthreads();
+    return base + incl - v;
+}
+
+__global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ ids, int A,
+                                                         int E, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted,
+                                                         int32_t* __restrict__ active,
+                                                         int32_t* __restrict__ n_active) {
+    __shared__ int hist[kGroupWaves * kGroupMaxExperts];
+    __shared__ int wave_tot[kGroupWaves];
+    __shared__ int carry[2];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+    for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) hist[i] = 0;
+    __syncthreads();
+    const int chunk = (A + kGroupWaves - 1) / kGroupWaves;
+    const int beg = min(wave * chunk, A), end = min(beg + chunk, A);
+    for (int a = beg + lane; a < end; a += 64) atomicAdd(&hist[wave * E + ids[a]], 1);
+    __syncthreads();
+
+    // Experts e = tid + 512*half, processed in two halves to cover E <= 1024.
+    int run_off = 0, run_act = 0;
+    for (int half = 0; half < 2; ++half) {
+        const int e = tid + half * kGroupThreads;
+        int cnt = 0;
+        if (e < E) {
+            for (int w = 0; w < kGroupWaves; ++w) {
+                const int h = hist[w * E + e];
+                hist[w * E + e] = cnt;
+                cnt += h;
+            }
+        }
+        const int off = run_off + block_exclusive_scan_1024(cnt, wave_tot);
+        const int act = run_act + block_exclusive_scan_1024(cnt > 0 ? 1 : 0, wave_tot);
+        if (e < E) {
+            offsets[e] = off;
+            for (int w = 0; w < kGroupWaves; ++w) hist[w * E + e] += off;
+            if (cnt > 0) active[act] = e;
+        }
+        if (tid == kGroupThreads - 1) {
+            carry[0] = off + cnt;
+            carry[1] = act + (cnt > 0 ? 1 : 0);
+        }
+        __syncthreads();
+        run_off = carry[0];
+        run_act = carry[1];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        offsets[E] = run_off;
+        *n_active = run_act;
+    }
+
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = beg; base < end; base += 64) {
+        const int a = base + lane;
+        const bool ok = a < end;
+        const int key = ok ? ids[a] : 0;
+        uint64_t m = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (key >> b) & 1;
+            const uint64_t bb = __ballot(ok && bit);
+            m &= bit ? bb : ~bb;
+        }
+        if (ok) {
+            const int rank = __popcll(m & below);
+            const int pos = hist[wave * E + key] + rank;
+            sorted[pos] = a;
+            const int leader = 63 - __clzll(m);
+            if (leader == lane) hist[wave * E + key] += __popcll(m);
+        }
+    }
+}
+
+hipError_t launch_group(const int32_t* ids, int n_assign, int n_experts, int32_t* offsets,
+                        int32_t* sorted, int32_t* active, int32_t* n_active, hipStream_t s) {
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), 0, s, ids, n_assign, n_experts,
+                       offsets, sorted, active, n_active);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weighted combine in slot order: y[t][n] = sum_j w[t][j] * out[t*k+j][n].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ out,
+                                                 const float* __restrict__ w, int T, int k,
+                                                 int rows, float* __restrict__ y) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= static_cast<int64_t>(T) * rows) return;
+    const int64_t t = i / rows, n = i % rows;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) acc += w[t * k + j] * out[(t * k + j) * rows + n];
+    y[i] = acc;
+}
+
+hipError_t launch_combine(const float* out, const float* w, int n_tokens, int top_k, int rows,
+                          float* y, hipStream_t s) {
+    const int64_t n = static_cast<int64_t>(n_tokens) * rows;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                       out, w, n_tokens, top_k, rows, y);
+    return hipGetLastError();
+}
+
+}  // namespace pqk

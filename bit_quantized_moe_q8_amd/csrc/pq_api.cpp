@@ -1,0 +1,318 @@
+// C-ABI entry points of libpq (declared in include/pq.h): argument checks on
+// the host, then kernel launches on the caller's stream.  Every check runs
+// before the first HIP call; no entry point allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/pq.h"
+#include "pq_internal.hpp"
+
+namespace pqk {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+}  // namespace
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        g_cu_count[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+}  // namespace pqk
+
+namespace {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int64_t kMaxAssign = int64_t(1) << 20;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+pq_status from_hip(hipError_t e) { return e == hipSuccess ? PQ_OK : PQ_ERR_HIP; }
+
+hipStream_t as_stream(pq_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+pq_status check_groups(const pq_groups* g) {
+    if (!g || !g->expert_offsets || !g->sorted_assign || !g->active_experts || !g->n_active)
+        return PQ_ERR_NULL;
+    if (g->n_experts < 1 || g->n_experts > kMaxExperts) return PQ_ERR_SHAPE;
+    if (g->top_k < 1 || g->top_k > kMaxTopK || g->top_k > g->n_experts) return PQ_ERR_SHAPE;
+    if (g->n_tokens < 0 || int64_t(g->n_tokens) * g->top_k > kMaxAssign) return PQ_ERR_SHAPE;
+    return PQ_OK;
+}
+
+pq_status check_dims(int n_experts, int rows, int cols, const pq_groups* g) {
+    if (n_experts != g->n_experts) return PQ_ERR_SHAPE;
+    if (rows < 1 || cols < 256 || cols % 256 != 0) return PQ_ERR_SHAPE;
+    if (int64_t(rows) * cols > (int64_t(1) << 31)) return PQ_ERR_SHAPE;
+    return PQ_OK;
+}
+
+void fill_groups(pqk::ExpertArgs& a, const pq_groups* g) {
+    a.offsets = g->expert_offsets;
+    a.sorted = g->sorted_assign;
+    a.active = g->active_experts;
+    a.n_active = g->n_active;
+    a.n_tokens = g->n_tokens;
+    a.top_k = g->top_k;
+    a.n_experts = g->n_experts;
+}
+
+void fill_debug(pqk::ExpertArgs& a, const pq_debug* dbg) {
+    a.debug = dbg != nullptr;
+    a.dbg_isums[0] = dbg ? dbg->isums : nullptr;
+    a.dbg_isums[1] = dbg ? dbg->isums_up : nullptr;
+    a.dbg_g = dbg ? dbg->g : nullptr;
+    a.dbg_u = dbg ? dbg->u : nullptr;
+    a.dbg_h = dbg ? dbg->h : nullptr;
+}
+
+pq_status check_epilogue_outputs(int epilogue, const void* up, int rows, void* out0, void* out1,
+                                 bool decode) {
+    if (!out0) return PQ_ERR_NULL;
+    if (epilogue == PQ_EPI_F32) {
+        if (!aligned(out0, 4)) return PQ_ERR_ALIGN;
+        return PQ_OK;
+    }
+    if ((decode && epilogue != PQ_EPI_SWIGLU_Q8) || (!decode && epilogue != PQ_EPI_SWIGLU_BF16))
+        return PQ_ERR_UNSUPPORTED;
+    if (!up) return PQ_ERR_NULL;
+    if (rows % 32 != 0) return PQ_ERR_SHAPE;
+    if (decode) {
+        if (!out1) return PQ_ERR_NULL;
+        if (!aligned(out1, 4)) return PQ_ERR_ALIGN;
+    } else if (!aligned(out0, 2)) {
+        return PQ_ERR_ALIGN;
+    }
+    return PQ_OK;
+}
+
+template <typename F>
+pq_status guarded(F&& f) {
+    try {
+        return f();
+    } catch (...) {
+        return PQ_ERR_HIP;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pq_abi_version(void) { return PQ_ABI_VERSION; }
+
+const char* pq_status_str(pq_status s) {
+    switch (s) {
+        case PQ_OK: return "ok";
+        case PQ_ERR_NULL: return "null pointer argument";
+        case PQ_ERR_SHAPE: return "size out of range or inconsistent";
+        case PQ_ERR_ALIGN: return "misaligned pointer";
+        case PQ_ERR_UNSUPPORTED: return "no kernel for these (valid) arguments";
+        case PQ_ERR_HIP: return "HIP runtime or launch failure";
+    }
+    return "unknown status";
+}
+
+pq_status pq_quantize_act_q8(const float* x, int32_t n_rows, int32_t cols, int8_t* xq, float* xd,
+                             pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (n_rows < 0 || cols < 32 || cols % 32 != 0) return PQ_ERR_SHAPE;
+        if (n_rows == 0) return PQ_OK;
+        if (!x || !xq || !xd) return PQ_ERR_NULL;
+        if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
+        const int64_t n_blocks = int64_t(n_rows) * (cols / 32);
+        return from_hip(pqk::launch_quantize_q8(x, n_blocks, xq, xd, as_stream(stream)));
+    });
+}
+
+pq_status pq_moe_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts,
+                            int32_t top_k, int32_t* topk_ids, float* topk_w, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (n_tokens < 0 || n_experts < 1 || n_experts > kMaxExperts) return PQ_ERR_SHAPE;
+        if (top_k < 1 || top_k > kMaxTopK || top_k > n_experts) return PQ_ERR_SHAPE;
+        if (n_tokens == 0) return PQ_OK;
+        if (!logits || !topk_ids || !topk_w) return PQ_ERR_NULL;
+        if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return PQ_ERR_ALIGN;
+        return from_hip(pqk::launch_route_topk(logits, n_tokens, n_experts, top_k, topk_ids,
+                                               topk_w, as_stream(stream)));
+    });
+}
+
+pq_status pq_group_tokens_by_expert(const int32_t* topk_ids, int32_t n_tokens, int32_t top_k,
+                                    int32_t n_experts, int32_t* expert_offsets,
+                                    int32_t* sorted_assign, int32_t* active_experts,
+                                    int32_t* n_active, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (n_tokens < 0 || n_experts < 1 || n_experts > kMaxExperts) return PQ_ERR_SHAPE;
+        if (top_k < 1 || top_k > kMaxTopK || top_k > n_experts) return PQ_ERR_SHAPE;
+        const int64_t A = int64_t(n_tokens) * top_k;
+        if (A > kMaxAssign) return PQ_ERR_SHAPE;
+        if (!expert_offsets || !active_experts || !n_active) return PQ_ERR_NULL;
+        if (A > 0 && (!topk_ids || !sorted_assign)) return PQ_ERR_NULL;
+        if (!aligned(expert_offsets, 4) || !aligned(active_experts, 4) || !aligned(n_active, 4) ||
+            !aligned(topk_ids, 4) || !aligned(sorted_assign, 4))
+            return PQ_ERR_ALIGN;
+        return from_hip(pqk::launch_group(topk_ids, int(A), n_experts, expert_offsets,
+                                          sorted_assign, active_experts, n_active,
+                                          as_stream(stream)));
+    });
+}
+
+pq_status pq_moe_matvec_ternary(const pq_ternary_w* w, const pq_ternary_w* w_up,
+                                const pq_groups* g, const int8_t* xq, const float* xd,
+                                int32_t act_by_token, int32_t epilogue, void* out0, void* out1,
+                                const pq_debug* dbg, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->qs || !w->d) return PQ_ERR_NULL;
+        pq_status st = check_groups(g);
+        if (st != PQ_OK) return st;
+        if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
+        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
+            return st;
+        if (epilogue == PQ_EPI_SWIGLU_Q8) {
+            if (!w_up->qs || !w_up->d) return PQ_ERR_NULL;
+            if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
+                return PQ_ERR_SHAPE;
+            if (!aligned(w_up->qs, 16) || !aligned(w_up->d, 2)) return PQ_ERR_ALIGN;
+        }
+        if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+        if (!pqk::matvec_supported(pqk::kTernary, w->cols)) return PQ_ERR_UNSUPPORTED;
+        if (g->n_tokens == 0) return PQ_OK;
+        if (!xq || !xd) return PQ_ERR_NULL;
+        if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
+        pqk::ExpertArgs a{};
+        a.qs[0] = w->qs;
+        a.d[0] = w->d;
+        a.qs[1] = w_up ? w_up->qs : nullptr;
+        a.d[1] = w_up ? w_up->d : nullptr;
+        a.rows = w->rows;
+        a.cols = w->cols;
+        fill_groups(a, g);
+        a.act_by_token = act_by_token ? 1 : 0;
+        a.xq = xq;
+        a.xd = xd;
+        a.out0 = out0;
+        a.out1 = out1;
+        fill_debug(a, dbg);
+        return from_hip(pqk::launch_matvec(pqk::kTernary, static_cast<pqk::Epi>(epilogue), a,
+                                           as_stream(stream)));
+    });
+}
+
+pq_status pq_moe_matvec_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, const pq_groups* g,
+                              const int8_t* xq, const float* xd, int32_t act_by_token,
+                              int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
+                              pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->qs || !w->qh || !w->d || !w->grid) return PQ_ERR_NULL;
+        pq_status st = check_groups(g);
+        if (st != PQ_OK) return st;
+        if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
+        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
+            return st;
+        if (epilogue == PQ_EPI_SWIGLU_Q8) {
+            if (!w_up->qs || !w_up->qh || !w_up->d) return PQ_ERR_NULL;
+            if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
+                return PQ_ERR_SHAPE;
+            if (!aligned(w_up->qs, 16) || !aligned(w_up->qh, 8) || !aligned(w_up->d, 2))
+                return PQ_ERR_ALIGN;
+        }
+        if (!aligned(w->qs, 16) || !aligned(w->qh, 8) || !aligned(w->d, 2) ||
+            !aligned(w->grid, 16))
+            return PQ_ERR_ALIGN;
+        if (!pqk::matvec_supported(pqk::kGrid1, w->cols)) return PQ_ERR_UNSUPPORTED;
+        if (g->n_tokens == 0) return PQ_OK;
+        if (!xq || !xd) return PQ_ERR_NULL;
+        if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
+        pqk::ExpertArgs a{};
+        a.qs[0] = w->qs;
+        a.qh[0] = w->qh;
+        a.d[0] = w->d;
+        a.qs[1] = w_up ? w_up->qs : nullptr;
+        a.qh[1] = w_up ? w_up->qh : nullptr;
+        a.d[1] = w_up ? w_up->d : nullptr;
+        a.grid = w->grid;
+        a.rows = w->rows;
+        a.cols = w->cols;
+        fill_groups(a, g);
+        a.act_by_token = act_by_token ? 1 : 0;
+        a.xq = xq;
+        a.xd = xd;
+        a.out0 = out0;
+        a.out1 = out1;
+        fill_debug(a, dbg);
+        return from_hip(pqk::launch_matvec(pqk::kGrid1, static_cast<pqk::Epi>(epilogue), a,
+                                           as_stream(stream)));
+    });
+}
+
+pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w* w, const pq_grid1_w* w_up,
+                                   const pq_groups* g, const uint16_t* x, int32_t act_by_token,
+                                   int32_t epilogue, void* out0, const pq_debug* dbg,
+                                   pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->qs || !w->qh || !w->d || !w->grid) return PQ_ERR_NULL;
+        pq_status st = check_groups(g);
+        if (st != PQ_OK) return st;
+        if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
+        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, nullptr, false)) != PQ_OK)
+            return st;
+        if (epilogue == PQ_EPI_SWIGLU_BF16) {
+            if (!w_up->qs || !w_up->qh || !w_up->d) return PQ_ERR_NULL;
+            if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
+                return PQ_ERR_SHAPE;
+            if (!aligned(w_up->qs, 16) || !aligned(w_up->qh, 8) || !aligned(w_up->d, 2))
+                return PQ_ERR_ALIGN;
+        }
+        if (!aligned(w->qs, 16) || !aligned(w->qh, 8) || !aligned(w->d, 2) ||
+            !aligned(w->grid, 16))
+            return PQ_ERR_ALIGN;
+        if (!pqk::gemm_supported(w->rows, w->cols, epilogue)) return PQ_ERR_UNSUPPORTED;
+        if (g->n_tokens == 0) return PQ_OK;
+        if (!x) return PQ_ERR_NULL;
+        if (!aligned(x, 16)) return PQ_ERR_ALIGN;
+        pqk::ExpertArgs a{};
+        a.qs[0] = w->qs;
+        a.qh[0] = w->qh;
+        a.d[0] = w->d;
+        a.qs[1] = w_up ? w_up->qs : nullptr;
+        a.qh[1] = w_up ? w_up->qh : nullptr;
+        a.d[1] = w_up ? w_up->d : nullptr;
+        a.grid = w->grid;
+        a.rows = w->rows;
+        a.cols = w->cols;
+        fill_groups(a, g);
+        a.act_by_token = act_by_token ? 1 : 0;
+        a.xb = x;
+        a.out0 = out0;
+        fill_debug(a, dbg);
+        return from_hip(pqk::launch_gemm(static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
+    });
+}
+
+pq_status pq_moe_combine(const float* out_assign, const float* topk_w, int32_t n_tokens,
+                         int32_t top_k, int32_t rows, float* y, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (n_tokens < 0 || top_k < 1 || top_k > kMaxTopK || rows < 1) return PQ_ERR_SHAPE;
+        if (int64_t(n_tokens) * top_k * rows > (int64_t(1) << 40)) return PQ_ERR_SHAPE;
+        if (n_tokens == 0) return PQ_OK;
+        if (!out_assign || !topk_w || !y) return PQ_ERR_NULL;
+        if (!aligned(out_assign, 4) || !aligned(topk_w, 4) || !aligned(y, 4)) return PQ_ERR_ALIGN;
+        return from_hip(
+            pqk::launch_combine(out_assign, topk_w, n_tokens, top_k, rows, y, as_stream(stream)));
+    });
+}
+
+}  // extern "C"

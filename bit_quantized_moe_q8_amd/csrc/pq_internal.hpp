@@ -1,0 +1,62 @@
+// Internal interface between the C-ABI layer (pq_api.cpp) and the kernel
+// translation units.  Not installed; the public interface is include/pq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pqk {
+
+constexpr int kGridEntries = 2048;  // grid1 codebook entries of 8 int8 values
+
+// Number of compute units of the current device (cached per device).
+int cu_count();
+
+hipError_t launch_quantize_q8(const float* x, int64_t n_blocks, int8_t* xq, float* xd,
+                              hipStream_t s);
+
+hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, int top_k,
+                             int32_t* ids, float* w, hipStream_t s);
+
+hipError_t launch_group(const int32_t* ids, int n_assign, int n_experts, int32_t* offsets,
+                        int32_t* sorted, int32_t* active, int32_t* n_active, hipStream_t s);
+
+hipError_t launch_combine(const float* out, const float* w, int n_tokens, int top_k, int rows,
+                          float* y, hipStream_t s);
+
+enum Fmt { kTernary = 0, kGrid1 = 1 };
+enum Epi { kEpiF32 = 0, kEpiSwigluQ8 = 1, kEpiSwigluBf16 = 2 };
+
+// Everything an expert kernel needs; index 0 is `w`, index 1 is `w_up`.
+struct ExpertArgs {
+    const uint8_t* qs[2];
+    const uint16_t* qh[2];
+    const uint16_t* d[2];
+    const int8_t* grid;
+    int rows, cols, n_experts;
+    const int32_t* offsets;
+    const int32_t* sorted;
+    const int32_t* active;
+    const int32_t* n_active;
+    int n_tokens, top_k, act_by_token;
+    const int8_t* xq;    // decode activations
+    const float* xd;
+    const uint16_t* xb;  // prefill activations (bf16 bits)
+    void* out0;
+    void* out1;
+    int32_t* dbg_isums[2];
+    float* dbg_g;
+    float* dbg_u;
+    float* dbg_h;
+    bool debug;
+};
+
+// Decode mat-vec; returns hipErrorInvalidValue when no kernel matches cols.
+hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
+bool matvec_supported(Fmt fmt, int cols);
+
+// Prefill dequant-per-tile GEMM (grid1, bf16 MFMA).
+hipError_t launch_gemm(Epi epi, const ExpertArgs& a, hipStream_t s);
+bool gemm_supported(int rows, int cols, int epi);
+
+}  // namespace pqk

@@ -1,0 +1,112 @@
+"""Sequencing of the library's entry points for one routed-expert MoE FFN layer.
+
+No arithmetic here: each step is one call into libpq on the current stream,
+writing into buffers allocated once per shape (so a timed loop allocates
+nothing).
+
+Decode (Parakon Runtime README, "How it works"):
+    q8(x) -> top-k route -> group by expert -> fused gate/up mat-vec with
+    SwiGLU + q8 epilogue -> down mat-vec -> weighted combine.
+Prefill (same section; dequant-per-tile GEMM for large batches):
+    route -> group -> fused gate/up GEMM with SwiGLU epilogue (bf16 h)
+    -> down GEMM -> weighted combine.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (PQ_EPI_F32, PQ_EPI_SWIGLU_BF16, PQ_EPI_SWIGLU_Q8, GroupBuffers,
+               Grid1Weights, TernaryWeights, group_tokens_by_expert, moe_combine,
+               moe_gemm_dequant_tile, moe_matvec_grid1, moe_matvec_ternary, moe_route_topk,
+               quantize_act_q8)
+
+
+class DecodeLayer:
+    """Buffers and call sequence of one decode MoE FFN layer of fixed shape."""
+
+    def __init__(self, fmt: str, n_tokens: int, hidden: int, inter: int, n_experts: int,
+                 top_k: int, device="cuda"):
+        self.fmt, self.T, self.H, self.I, self.E, self.k = fmt, n_tokens, hidden, inter, n_experts, top_k
+        A = n_tokens * top_k
+        f32, i8, i32 = torch.float32, torch.int8, torch.int32
+        self.xq = torch.empty((n_tokens, hidden), dtype=i8, device=device)
+        self.xd = torch.empty((n_tokens, hidden // 32), dtype=f32, device=device)
+        self.ids = torch.empty((n_tokens, top_k), dtype=i32, device=device)
+        self.w = torch.empty((n_tokens, top_k), dtype=f32, device=device)
+        self.groups = GroupBuffers.empty(n_tokens, top_k, n_experts, device)
+        self.hq = torch.empty((A, inter), dtype=i8, device=device)
+        self.hd = torch.empty((A, inter // 32), dtype=f32, device=device)
+        self.out = torch.empty((A, hidden), dtype=f32, device=device)
+        self.y = torch.empty((n_tokens, hidden), dtype=f32, device=device)
+        self._mv = moe_matvec_ternary if fmt == "ternary" else moe_matvec_grid1
+
+    def route(self, x: torch.Tensor, logits: torch.Tensor):
+        quantize_act_q8(x, self.xq, self.xd)
+        moe_route_topk(logits, self.k, self.ids, self.w)
+        group_tokens_by_expert(self.ids, self.E, self.groups)
+
+    def gate_up(self, gate, up, dbg=None):
+        self._mv(gate, up, self.groups, self.xq, self.xd, True, PQ_EPI_SWIGLU_Q8, self.hq, self.hd, dbg)
+
+    def down(self, down, dbg=None):
+        self._mv(down, None, self.groups, self.hq, self.hd, False, PQ_EPI_F32, self.out, None, dbg)
+
+    def combine(self):
+        moe_combine(self.out, self.w, self.k, self.y)
+
+    def __call__(self, x, logits, gate, up, down):
+        self.route(x, logits)
+        self.gate_up(gate, up)
+        self.down(down)
+        self.combine()
+        return self.y
+
+
+class PrefillLayer:
+    """Buffers and call sequence of one prefill MoE FFN layer (grid1 weights, bf16 x)."""
+
+    def __init__(self, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int,
+                 device="cuda"):
+        self.T, self.H, self.I, self.E, self.k = n_tokens, hidden, inter, n_experts, top_k
+        A = n_tokens * top_k
+        self.ids = torch.empty((n_tokens, top_k), dtype=torch.int32, device=device)
+        self.w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=device)
+        self.groups = GroupBuffers.empty(n_tokens, top_k, n_experts, device)
+        self.h = torch.empty((A, inter), dtype=torch.bfloat16, device=device)
+        self.out = torch.empty((A, hidden), dtype=torch.float32, device=device)
+        self.y = torch.empty((n_tokens, hidden), dtype=torch.float32, device=device)
+
+    def route(self, logits):
+        moe_route_topk(logits, self.k, self.ids, self.w)
+        group_tokens_by_expert(self.ids, self.E, self.groups)
+
+    def gate_up(self, x_bf16, gate: Grid1Weights, up: Grid1Weights, dbg=None):
+        moe_gemm_dequant_tile(gate, up, self.groups, x_bf16, True, PQ_EPI_SWIGLU_BF16, self.h, dbg)
+
+    def down(self, down: Grid1Weights, dbg=None):
+        moe_gemm_dequant_tile(down, None, self.groups, self.h, False, PQ_EPI_F32, self.out, dbg)
+
+    def combine(self):
+        moe_combine(self.out, self.w, self.k, self.y)
+
+    def __call__(self, x_bf16, logits, gate, up, down):
+        self.route(logits)
+        self.gate_up(x_bf16, gate, up)
+        self.down(down)
+        self.combine()
+        return self.y
+
+
+def weights_to_device(fmt: str, planes: dict, grid=None, device="cuda"):
+    """Host numpy planes (workloads module layout) -> device weight container."""
+    import numpy as np
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(device)
+
+    if fmt == "ternary":
+        return TernaryWeights(t(planes["qs"]), t(planes["d"]))
+    return Grid1Weights(t(planes["qs"]), t(planes["qh"]), t(planes["d"]), t(grid))

@@ -1,0 +1,229 @@
+/*
+ * pq.h -- C ABI of libpq: packed 1-bit-class MoE expert kernels for AMD
+ * Instinct MI355X (CDNA4, gfx950).
+ *
+ * The library runs the routed-expert FFN of a Mixture-of-Experts layer whose
+ * expert weights stay in packed 1-bit-class block formats in device memory
+ * and are read directly by the kernels; no dequantized copy of a weight
+ * matrix is ever written (Parakon Runtime README, "How it works": fused
+ * mat-vec kernels read the quantized blocks and accumulate against int8
+ * activations; large prompt batches use a dequant-per-tile GEMM).
+ *
+ * Conventions for every entry point
+ *  - Array arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains memory and keeps no state between
+ *    calls other than a per-device cache of the compute-unit count.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  No call synchronizes the stream or the device.
+ *  - All argument checks run on the host before the first HIP call; on a
+ *    failed check nothing is enqueued.  On any status other than PQ_OK the
+ *    contents of the output buffers are undefined.
+ *  - No C++ exception crosses this interface.
+ *  - Calls that share output buffers must be ordered by the caller; calls on
+ *    different streams with disjoint outputs may run concurrently.
+ *
+ * Tokens, experts, assignments
+ *  - T = n_tokens, E = n_experts, k = top_k; A = T*k assignments.  The
+ *    assignment of token t to its j-th selected expert has id a = t*k + j.
+ *  - Expert weight tensors are [E][rows][cols]; an expert computes
+ *    out[n] = sum_c W[n][c] * act[c] for each of its rows n.
+ *
+ * Packed formats (structure of arrays; each plane contiguous, row-major)
+ *  - ternary (2.0625 bits/weight): qs uint8 [E][rows][cols/4], four 2-bit
+ *    codes per byte, weight 4i+j of a row in bits 2j..2j+1 of byte i; code 0
+ *    -> 0, 1 -> +1, 2 -> -1 (code 3 is invalid; kernel output on code 3 is
+ *    unspecified).  d: IEEE fp16 bits [E][rows][cols/256], one scale per
+ *    256-weight row block.  Ternary routed experts: modelium.tech article on
+ *    Parallax 8B kappa, "What exactly is available".
+ *  - grid1 (1.5625 bits/weight): per 256-weight row block b, 32 groups of 8
+ *    weights; group g has the 11-bit codebook index
+ *    qs[32b+g] | ((qh[8b+g/4] >> 3*(g%4)) & 7) << 8, and weights
+ *    256b+8g+j = grid[index][j].  qs uint8 [E][rows][cols/8], qh uint16
+ *    [E][rows][cols/32] (bits 12..15 ignored), d fp16 bits [E][rows][cols/256],
+ *    grid int8 [2048][8] with entries in {-1,0,+1}.  1-bit codebook formats
+ *    after the dynamic 1-bit family: Parakon Runtime README, "How it works"
+ *    and "Attribution"; IQ1_S-class routed experts: llama-modchip summary.
+ *  - q8 activations: per 32 consecutive values of a row, d = max|x| / 127
+ *    (fp32, correctly rounded), q = round_half_away_from_zero(x / d) clamped to
+ *    [-127, 127] as int8; max|x| = 0 gives d = 0 and q = 0.  xq int8
+ *    [rows][cols], xd float [rows][cols/32].
+ *  - Mat-vec result per row n:  sum_b d_w[n][b] * sum_{s in b} xd[s] *
+ *    isum[n][s], with isum[n][s] = sum_{j<32} w[n][32s+j] * xq[32s+j] an exact
+ *    int32 block sum; fp32 output.
+ */
+#ifndef PQ_H
+#define PQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQ_ABI_VERSION 1
+
+typedef enum pq_status {
+    PQ_OK = 0,
+    PQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    PQ_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    PQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+    PQ_ERR_UNSUPPORTED = 4, /* valid arguments this build has no kernel for */
+    PQ_ERR_HIP = 5          /* a HIP call or kernel launch failed */
+} pq_status;
+
+enum {
+    PQ_EPI_F32 = 0,        /* out0 = float [A][rows] */
+    PQ_EPI_SWIGLU_Q8 = 1,  /* out0 = int8 hq [A][rows], out1 = float hd [A][rows/32] */
+    PQ_EPI_SWIGLU_BF16 = 2 /* out0 = bf16 bits h [A][rows] */
+};
+
+/* hipStream_t, passed as an opaque pointer; NULL = null stream. */
+typedef void *pq_stream;
+
+/* Ternary expert tensor [n_experts][rows][cols]. qs: 16-byte aligned; d: 2-byte aligned. */
+typedef struct pq_ternary_w {
+    const uint8_t *qs;
+    const uint16_t *d;
+    int32_t n_experts, rows, cols;
+} pq_ternary_w;
+
+/* Grid1 expert tensor [n_experts][rows][cols]. qs 16-byte, qh 8-byte, d 2-byte,
+   grid 16-byte aligned. */
+typedef struct pq_grid1_w {
+    const uint8_t *qs;
+    const uint16_t *qh;
+    const uint16_t *d;
+    const int8_t *grid;
+    int32_t n_experts, rows, cols;
+} pq_grid1_w;
+
+/* Output of pq_group_tokens_by_expert, consumed by the expert kernels. */
+typedef struct pq_groups {
+    const int32_t *expert_offsets; /* [n_experts+1] */
+    const int32_t *sorted_assign;  /* [n_tokens*top_k] */
+    const int32_t *active_experts; /* [n_experts]; first *n_active entries valid */
+    const int32_t *n_active;       /* [1] */
+    int32_t n_tokens, top_k, n_experts;
+} pq_groups;
+
+/* Optional debug outputs of the expert kernels (a separate kernel variant is
+   used when dbg != NULL; the production variant writes none of these).  Each
+   pointer may be NULL.  isums: int32 [A][rows][cols/32] block sums of `w`,
+   isums_up: the same for `w_up`; g, u: fp32 [A][rows] outputs of `w` and
+   `w_up` before the epilogue; h: fp32 [A][rows] silu(g)*u before rounding or
+   quantization. */
+typedef struct pq_debug {
+    int32_t *isums;
+    int32_t *isums_up;
+    float *g;
+    float *u;
+    float *h;
+} pq_debug;
+
+/*
+ * q8 activation quantization (Parakon Runtime README, "How it works": int8
+ * activations for the dp4a-style decode path; rule as in the header above).
+ *   x  float [n_rows][cols] -> xq int8 [n_rows][cols], xd float [n_rows][cols/32]
+ * cols % 32 == 0; x and xq 16-byte aligned.  Inputs must be finite (output on
+ * non-finite input is unspecified).  n_rows == 0 is a no-op.
+ */
+pq_status pq_quantize_act_q8(const float *x, int32_t n_rows, int32_t cols,
+                             int8_t *xq, float *xd, pq_stream stream);
+
+/*
+ * Router: per token, the top_k largest of n_experts fp32 logits in descending
+ * order (equal logits: lower expert index first), then softmax over those
+ * top_k logits only: w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).  Every
+ * selected expert is evaluated; nothing is dropped (llama-modchip summary,
+ * "Key highlights").
+ *   logits float [n_tokens][n_experts] -> topk_ids int32 [n_tokens][top_k],
+ *   topk_w float [n_tokens][top_k].
+ * 1 <= top_k <= min(16, n_experts); n_experts <= 1024.  Logits must be finite.
+ */
+pq_status pq_moe_route_topk(const float *logits, int32_t n_tokens, int32_t n_experts,
+                            int32_t top_k, int32_t *topk_ids, float *topk_w,
+                            pq_stream stream);
+
+/*
+ * Stable grouping of the A = n_tokens*top_k assignments by expert (the grouped
+ * MoE path and ragged tails of the pxq_llama README, "What's PXQ?" and "Run").
+ *   expert_offsets [n_experts+1]: exclusive prefix sum of per-expert counts;
+ *   sorted_assign [A]: every assignment id, ordered by (expert, id);
+ *   active_experts [n_experts]: the experts with at least one assignment, in
+ *   increasing id order; *n_active: their number.
+ * topk_ids must hold values in [0, n_experts) (out-of-range ids give
+ * unspecified output).  n_experts <= 1024; A <= 1<<20.
+ */
+pq_status pq_group_tokens_by_expert(const int32_t *topk_ids, int32_t n_tokens, int32_t top_k,
+                                    int32_t n_experts, int32_t *expert_offsets,
+                                    int32_t *sorted_assign, int32_t *active_experts,
+                                    int32_t *n_active, pq_stream stream);
+
+/*
+ * Grouped expert mat-vec over packed ternary weights against q8 activations
+ * (Parakon Runtime README, "How it works": fused decode mat-vec reading the
+ * packed blocks directly with int8 dot products; gate/up fusion with SiLU:
+ * pxq_llama README, "Updates - 2026-07-28").
+ *
+ * For every assignment a (expert e = its group), with activation row
+ * r = act_by_token ? a / top_k : a  (xq [n_rows][cols], xd [n_rows][cols/32]):
+ *   PQ_EPI_F32:       out0 float [A][rows]: W_e . act_r
+ *   PQ_EPI_SWIGLU_Q8: needs w_up (same shape); g = W_e . act_r, u = Wup_e . act_r,
+ *                     h = silu(g) * u in fp32, then q8 of h per 32 rows:
+ *                     out0 int8 [A][rows], out1 float [A][rows/32]; rows % 32 == 0.
+ * cols % 256 == 0 and cols/64 in {2,4,8,12,16,32,64} (cols 256..4096 for
+ * those divisors); rows >= 1.  w->n_experts == g->n_experts.  dbg may be NULL.
+ */
+pq_status pq_moe_matvec_ternary(const pq_ternary_w *w, const pq_ternary_w *w_up,
+                                const pq_groups *g, const int8_t *xq, const float *xd,
+                                int32_t act_by_token, int32_t epilogue, void *out0,
+                                void *out1, const pq_debug *dbg, pq_stream stream);
+
+/*
+ * The same over grid1 weights (1-bit codebook format).  The codebook is staged
+ * in LDS once per workgroup.  cols % 256 == 0 and cols/128 in
+ * {2,4,8,12,16,32,64}.
+ */
+pq_status pq_moe_matvec_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
+                              const pq_groups *g, const int8_t *xq, const float *xd,
+                              int32_t act_by_token, int32_t epilogue, void *out0,
+                              void *out1, const pq_debug *dbg, pq_stream stream);
+
+/*
+ * Prefill: grouped dequant-per-tile GEMM over grid1 weights with bf16
+ * activations on MFMA (Parakon Runtime README, "How it works": prompt
+ * processing at large batch sizes uses a dequant-per-tile GEMM path).  Packed
+ * blocks are decoded to bf16 {-1,0,+1} on chip only; each 256-column block is
+ * accumulated in fp32 and scaled by its fp16 scale in fp32.
+ *   x: bf16 bits, [n_tokens][cols] if act_by_token else [A][cols]; 16-byte aligned.
+ *   PQ_EPI_F32:         out0 float [A][rows].
+ *   PQ_EPI_SWIGLU_BF16: needs w_up; out0 bf16 bits [A][rows] of
+ *                       round_to_nearest_even(silu(g) * u); rows % 32 == 0.
+ * cols % 256 == 0.  dbg may be NULL (g, u, h fields honoured).
+ */
+pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w *w, const pq_grid1_w *w_up,
+                                   const pq_groups *g, const uint16_t *x,
+                                   int32_t act_by_token, int32_t epilogue, void *out0,
+                                   const pq_debug *dbg, pq_stream stream);
+
+/*
+ * Weighted combine of the per-assignment expert outputs (the scatter of the
+ * pxq_llama README, "Run"): y[t][n] = sum_{j<top_k} topk_w[t][j] *
+ * out_assign[t*top_k+j][n], summed in slot order j = 0..top_k-1 (deterministic).
+ * out_assign float [n_tokens*top_k][rows]; y float [n_tokens][rows].
+ */
+pq_status pq_moe_combine(const float *out_assign, const float *topk_w, int32_t n_tokens,
+                         int32_t top_k, int32_t rows, float *y, pq_stream stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *pq_status_str(pq_status status);
+
+/* PQ_ABI_VERSION of the built library. */
+int32_t pq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ_H */

@@ -1,0 +1,296 @@
+"""GPU parity of the decode path (HIP kernels through the C ABI) against the CPU oracle.
+
+Bar: q8 codes/scales, routing ids, grouping and every int32 block sum
+bit-exact; fp32 outputs within |got - ref| <= 1e-5 * sum|terms| + 1e-6.
+The SwiGLU re-quantization is checked on the GPU's own fp32 h (bit-exact),
+because q8 is discontinuous; the free-running chain is checked where no
+near-tie flipped a q8 value.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_q8_amd as pq
+from bit_quantized_moe_q8_amd.layer import DecodeLayer, weights_to_device
+import oracle
+from oracle import moe
+import workloads as wl
+
+from gpu_util import (assert_equal, assert_tol, dev, decode_inputs, say, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------- q8
+
+@pytest.mark.parametrize("rows,cols,seed", [(1, 1024, 1), (8, 4096, 2), (64, 2048, 3), (3, 32, 4), (513, 768, 5)])
+def test_q8_bit_exact(rows, cols, seed):
+    say("q8", rows, cols, seed)
+    x = wl.activations_f32(seed, rows, cols)
+    xq, xd = pq.quantize_act_q8(to_dev(x))
+    q_ref, d_ref = oracle.quantize_q8(x)
+    assert_equal(to_host(xq), q_ref, "xq")
+    assert_equal(to_host(xd), d_ref, "xd")
+
+
+def test_q8_edge_blocks():
+    say("q8 edge blocks")
+    x = np.zeros((1, 32 * 8), np.float32)
+    x[0, 0:12] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -0.49, 126.5, -126.5, 0.0, 3.0, -1.0]
+    # block 1: all zero; block 2: tiny values; block 3: max shared by two elements
+    x[0, 64:96] = np.linspace(-1e-30, 1e-30, 32, dtype=np.float32)
+    x[0, 96:128] = 0.25
+    x[0, 97] = -3.0
+    x[0, 100] = 3.0
+    x[0, 128:160] = np.float32(1e30) * np.linspace(-1, 1, 32, dtype=np.float32)
+    x[0, 160:192] = np.arange(32, dtype=np.float32) - 15.5
+    x[0, 192:256] = wl.activations_f32(9, 1, 64)
+    xq, xd = pq.quantize_act_q8(to_dev(x))
+    q_ref, d_ref = oracle.quantize_q8(x)
+    assert_equal(to_host(xq), q_ref, "xq")
+    assert_equal(to_host(xd), d_ref, "xd")
+
+
+def test_q8_subnormal_blocks():
+    say("q8 subnormal blocks")
+    x = np.zeros((1, 96), np.float32)
+    x[0, 0:32] = np.float32(1e-40) * np.linspace(-1, 1, 32, dtype=np.float32)
+    x[0, 32:64] = np.float32(3e-39) * np.linspace(-1, 1, 32, dtype=np.float32)
+    x[0, 64:96] = np.float32(1.5e-36) * (np.arange(32, dtype=np.float32) - 16)
+    xq, xd = pq.quantize_act_q8(to_dev(x))
+    q_ref, d_ref = oracle.quantize_q8(x)
+    assert_equal(to_host(xq), q_ref, "xq")
+    assert_equal(to_host(xd), d_ref, "xd")
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,E,k,kind", [(1, 128, 8, "normal"), (8, 256, 8, "uniform"), (64, 256, 8, "zipf"),
+                                        (2048, 256, 8, "uniform"), (5, 1024, 16, "normal"), (3, 7, 7, "normal"),
+                                        (9, 64, 1, "normal")])
+def test_route_topk(T, E, k, kind):
+    say("route", T, E, k, kind)
+    logits = wl.router_logits(41, T, E, kind)
+    ids, w = pq.moe_route_topk(to_dev(logits), k)
+    ids_ref, w_ref = oracle.route_topk(logits, k)
+    assert_equal(to_host(ids), ids_ref, "ids")
+    assert_tol(to_host(w), w_ref, w_ref, "w")
+
+
+def test_route_ties():
+    say("route ties")
+    l = np.zeros((3, 96), np.float32)
+    l[1, [5, 70, 71, 90]] = 2.0
+    l[2] = np.repeat(np.float32([1.0, 2.0, 3.0]), 32)
+    ids, w = pq.moe_route_topk(to_dev(l), 8)
+    ids_ref, w_ref = oracle.route_topk(l, 8)
+    assert_equal(to_host(ids), ids_ref, "ids")
+    assert_tol(to_host(w), w_ref, w_ref, "w")
+
+
+# --------------------------------------------------------------- grouping
+
+@pytest.mark.parametrize("T,E,k,kind", [(1, 128, 8, "normal"), (8, 256, 8, "uniform"), (64, 256, 8, "zipf"),
+                                        (2048, 256, 8, "uniform"), (1000, 1024, 16, "normal"), (1, 1, 1, "normal")])
+def test_group_bit_exact(T, E, k, kind):
+    say("group", T, E, k, kind)
+    ids, _ = oracle.route_topk(wl.router_logits(42, T, E, kind), k)
+    g = pq.group_tokens_by_expert(to_dev(ids), E)
+    off, srt, act = oracle.group(ids, E)
+    assert_equal(to_host(g.expert_offsets), off, "offsets")
+    assert_equal(to_host(g.sorted_assign)[: ids.size], srt, "sorted")
+    assert int(to_host(g.n_active)[0]) == act.size
+    assert_equal(to_host(g.active_experts)[: act.size], act, "active")
+
+
+def test_group_all_to_one_expert_and_twice_identical():
+    say("group skewed")
+    E = 64
+    ids = np.full((4096, 4), 17, np.int32)
+    ids[::7, 2] = 3
+    ids[5, 0] = 63
+    g1 = pq.group_tokens_by_expert(to_dev(ids), E)
+    g2 = pq.group_tokens_by_expert(to_dev(ids), E)
+    off, srt, act = oracle.group(ids, E)
+    for g in (g1, g2):
+        assert_equal(to_host(g.expert_offsets), off, "offsets")
+        assert_equal(to_host(g.sorted_assign), srt, "sorted")
+        assert_equal(to_host(g.active_experts)[: act.size], act, "active")
+
+
+# ------------------------------------------------------- single mat-vecs
+
+def _single(fmt, E, N, K, T, k, act_by_token, seed, want_dbg=True):
+    """Grouped F32 mat-vec on random routing; compare isums exactly and y within tolerance."""
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    planes = wl.stack_experts(fmt, seed, "w", E, N, K)
+    grid = wl.codebook(seed) if fmt == "grid1" else None
+    n_rows = T if act_by_token else T * k
+    xq, xd = oracle.quantize_q8(wl.activations_f32(seed, n_rows, K))
+    g = pq.group_tokens_by_expert(to_dev(ids), E)
+    W = weights_to_device(fmt, planes, grid)
+    A = T * k
+    isums = torch.zeros((A, N, K // 32), dtype=torch.int32, device=dev()) if want_dbg else None
+    mv = pq.moe_matvec_ternary if fmt == "ternary" else pq.moe_matvec_grid1
+    out, _ = mv(W, None, g, to_dev(xq), to_dev(xd), act_by_token, pq.PQ_EPI_F32,
+                dbg={"isums": isums} if want_dbg else None)
+    rows_of = (np.arange(A) // k) if act_by_token else np.arange(A)
+    y_ref, t_ref, i_ref = moe.grouped_matvec_q8(fmt, planes, grid, ids, xq, xd, rows_of, K, want_dbg)
+    if want_dbg:
+        assert_equal(to_host(isums), i_ref, "isums")
+    assert_tol(to_host(out), y_ref, t_ref, "y")
+    return to_host(out)
+
+
+def test_ternary_matvec_1024_single_matrix():
+    """One 1024x1024 ternary matrix, one token: E=1, T=1, k=1."""
+    say("ternary 1024x1024 single")
+    inp = wl.make_workload("ternary_matvec_1024")
+    planes = inp["w"]
+    xq_d, xd_d = pq.quantize_act_q8(to_dev(inp["x"]))
+    xq, xd = oracle.quantize_q8(inp["x"])
+    assert_equal(to_host(xq_d), xq, "xq")
+    assert_equal(to_host(xd_d), xd, "xd")
+    g = pq.group_tokens_by_expert(to_dev(np.zeros((1, 1), np.int32)), 1)
+    isums = torch.zeros((1, 1024, 32), dtype=torch.int32, device=dev())
+    W = weights_to_device("ternary", planes)
+    out, _ = pq.moe_matvec_ternary(W, None, g, xq_d, xd_d, True, pq.PQ_EPI_F32, dbg={"isums": isums})
+    w = oracle.unpack_ternary(planes["qs"][0], 1024)
+    y_ref, t_ref, i_ref = oracle.matvec_q8(w, planes["d"][0], xq[0], xd[0])
+    assert_equal(to_host(isums)[0], i_ref, "isums")
+    assert_tol(to_host(out)[0], y_ref, t_ref, "y")
+    # the production variant (no debug outputs) gives the same bits
+    out2, _ = pq.moe_matvec_ternary(W, None, g, xq_d, xd_d, True, pq.PQ_EPI_F32)
+    assert_equal(to_host(out2), to_host(out), "debug vs production variant")
+
+
+@pytest.mark.parametrize("fmt,E,N,K,T,k,abt", [
+    ("ternary", 4, 96, 256, 1, 2, True),      # smallest K, ragged rows (3 tiles)
+    ("ternary", 8, 100, 768, 3, 2, True),     # 12 lanes per row, ragged tail tile
+    ("ternary", 8, 64, 1024, 5, 3, False),    # activation row per assignment
+    ("ternary", 16, 70, 2048, 9, 4, True),    # 4 tokens per pass, ragged
+    ("ternary", 3, 33, 4096, 2, 3, True),     # 64 lanes per row
+    ("grid1", 4, 96, 256, 1, 2, True),
+    ("grid1", 8, 40, 1536, 3, 2, False),
+    ("grid1", 8, 64, 1024, 6, 3, True),
+    ("grid1", 16, 50, 4096, 9, 4, True),
+])
+def test_grouped_matvec(fmt, E, N, K, T, k, abt):
+    say("matvec", fmt, E, N, K, T, k, abt)
+    _single(fmt, E, N, K, T, k, abt, seed=zlib.crc32(repr((fmt, E, N, K, T)).encode()) % 1000)
+
+
+def test_matvec_one_expert_many_tokens():
+    """All tokens on one expert (many passes of the token loop)."""
+    say("matvec one expert")
+    for fmt in ("ternary", "grid1"):
+        _single(fmt, 1, 64, 1024, 37, 1, True, seed=7)
+
+
+# ----------------------------------------------------------- decode layers
+
+def _run_layer(name, **override):
+    inp = decode_inputs(name, **override)
+    cfg = inp["cfg"]
+    fmt, T, H, I, E, k = cfg["fmt"], cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
+    A = T * k
+    layer = DecodeLayer(fmt, T, H, I, E, k, dev())
+    grid = inp.get("grid")
+    W = {n: weights_to_device(fmt, inp[n], grid) for n in ("gate", "up", "down")}
+    x, logits = to_dev(inp["x"]), to_dev(inp["logits"])
+    dbg1 = {"isums": torch.zeros((A, I, H // 32), dtype=torch.int32, device=dev()),
+            "isums_up": torch.zeros((A, I, H // 32), dtype=torch.int32, device=dev()),
+            "g": torch.zeros((A, I), device=dev()), "u": torch.zeros((A, I), device=dev()),
+            "h": torch.zeros((A, I), device=dev())}
+    dbg2 = {"isums": torch.zeros((A, H, I // 32), dtype=torch.int32, device=dev())}
+    layer.route(x, logits)
+    layer.gate_up(W["gate"], W["up"], dbg1)
+    layer.down(W["down"], dbg2)
+    layer.combine()
+    torch.cuda.synchronize()
+    gpu = {k2: to_host(v) for k2, v in dict(xq=layer.xq, xd=layer.xd, ids=layer.ids, w=layer.w,
+                                            hq=layer.hq, hd=layer.hd, out=layer.out, y=layer.y).items()}
+    gpu.update({"dbg_" + k2: to_host(v) for k2, v in dbg1.items()})
+    gpu["dbg_isum_d"] = to_host(dbg2["isums"])
+    gpu["offsets"] = to_host(layer.groups.expert_offsets)
+    gpu["sorted"] = to_host(layer.groups.sorted_assign)[:A]
+    # second production run: integer and fp outputs must repeat bit for bit
+    layer(x, logits, W["gate"], W["up"], W["down"])
+    torch.cuda.synchronize()
+    gpu["hq2"], gpu["y2"] = to_host(layer.hq), to_host(layer.y)
+    return inp, gpu
+
+
+def _check_layer(inp, gpu):
+    cfg = inp["cfg"]
+    fmt, T, H, I, E, k = cfg["fmt"], cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
+    A = T * k
+    grid = inp.get("grid")
+    # stage 1: q8(x), routing, grouping
+    xq, xd = oracle.quantize_q8(inp["x"])
+    assert_equal(gpu["xq"], xq, "xq")
+    assert_equal(gpu["xd"], xd, "xd")
+    ids, w = oracle.route_topk(inp["logits"], k)
+    assert_equal(gpu["ids"], ids, "ids")
+    assert_tol(gpu["w"], w, w, "w")
+    off, srt, _ = oracle.group(ids, E)
+    assert_equal(gpu["offsets"], off, "offsets")
+    assert_equal(gpu["sorted"], srt, "sorted")
+    # stage 2: gate/up block sums and outputs
+    tok = np.arange(A) // k
+    g_ref, tg, ig = moe.grouped_matvec_q8(fmt, inp["gate"], grid, ids, xq, xd, tok, H)
+    u_ref, tu, iu = moe.grouped_matvec_q8(fmt, inp["up"], grid, ids, xq, xd, tok, H)
+    assert_equal(gpu["dbg_isums"], ig, "gate isums")
+    assert_equal(gpu["dbg_isums_up"], iu, "up isums")
+    assert_tol(gpu["dbg_g"], g_ref, tg, "g")
+    assert_tol(gpu["dbg_u"], u_ref, tu, "u")
+    # stage 3: h from the GPU's own g, u; q8 of the GPU's own h bit-exact
+    h_ref = oracle.swiglu(gpu["dbg_g"], gpu["dbg_u"])
+    assert_tol(gpu["dbg_h"], h_ref, np.abs(h_ref), "h")
+    hq_ref, hd_ref = oracle.quantize_q8(gpu["dbg_h"])
+    assert_equal(gpu["hq"], hq_ref, "hq")
+    assert_equal(gpu["hd"], hd_ref, "hd")
+    # stage 4: down on the GPU's own hq/hd
+    o_ref, to, io = moe.grouped_matvec_q8(fmt, inp["down"], grid, ids, gpu["hq"], gpu["hd"], np.arange(A), I)
+    assert_equal(gpu["dbg_isum_d"], io, "down isums")
+    assert_tol(gpu["out"], o_ref, to, "out")
+    # stage 5: combine on the GPU's own out and w
+    y_ref, ty = oracle.combine(gpu["out"], gpu["w"], k)
+    assert_tol(gpu["y"], y_ref, ty, "y (staged)")
+    # repeat run is bitwise identical
+    assert_equal(gpu["hq2"], gpu["hq"], "hq repeat")
+    assert_equal(gpu["y2"], gpu["y"], "y repeat")
+    # free-running oracle chain: tokens whose q8 h rows all agree must match y
+    ref = moe.decode_ffn(inp, want_isums=False)
+    same = (ref["hq"] == gpu["hq"]).reshape(T, k, I).all(axis=(1, 2))
+    flips = int((ref["hq"] != gpu["hq"]).sum())
+    say("  free-running q8(h) flips: %d of %d" % (flips, ref["hq"].size))
+    assert flips <= max(2, ref["hq"].size // 10000)
+    ty_free = np.einsum("tj,tjn->tn", np.abs(ref["w"]), ref["tout"].reshape(T, k, H))
+    assert_tol(gpu["y"][same], ref["y"][same], ty_free[same], "y (free-running)")
+
+
+@pytest.mark.parametrize("name,override", [
+    ("ternary_moe_decode_t1", {}),
+    ("grid1_moe_decode_t8", {}),
+    ("ternary_moe_decode_t64_zipf", {}),
+    ("ternary_moe_decode_t1", dict(T=4, E=16, H=768, I=256, top_k=4)),
+    ("grid1_moe_decode_t8", dict(T=3, E=8, H=1024, I=512, top_k=2)),
+])
+def test_decode_layer(name, override):
+    say("decode layer", name, override)
+    inp, gpu = _run_layer(name, **override)
+    _check_layer(inp, gpu)
+
+
+def test_combine():
+    say("combine")
+    rng = np.random.default_rng(5)
+    out = rng.standard_normal((7 * 3, 100)).astype(np.float32)
+    w = rng.random((7, 3)).astype(np.float32)
+    y = pq.moe_combine(to_dev(out), to_dev(w), 3)
+    y_ref, ty = oracle.combine(out, w, 3)
+    assert_tol(to_host(y), y_ref, ty, "y")
