@@ -98,7 +98,7 @@ def gemm_available() -> bool:
     return GEMM_READY
 
 
-GEMM_READY = False
+GEMM_READY = True
 
 
 def status_str(status: int) -> str:

@@ -14,14 +14,15 @@
 //
 // Lane mapping.  A row is split into LPR chunks of 16 packed bytes (ternary:
 // 64 weights = 2 int8 blocks of 32; grid1: 16 groups = 128 weights = 4 blocks
-// of 32).  Lane l of a wave owns chunk l % LPR of row-slot l / LPR for every
+// of 32).  Lane l of a wave owns chunk l % LS of row-slot l / LS for every
 // row it touches, so its slice of the activation row is loaded once into
 // registers and reused for all rows (the pages stage the activation vector
 // on chip for the same reason: pxq_llama README, "Updates - 2026-07-28",
 // 2D decode driver).  Each lane issues all of its 16-byte weight loads for
 // the tile before consuming any, so a wave keeps ITERS x 16 B per lane in
-// flight.  Partial row sums are reduced over the LPR lanes of a row with
-// shuffles.
+// flight.  Row slots are LPR rounded up to a power of two lanes wide (a 12-chunk
+// row uses 12 of 16 lanes), so the partial row sums reduce with DPP lane moves
+// (quad_perm, row mirrors, row_bcast) instead of LDS permutes.
 //
 // Ternary arithmetic.  A dword P of 16 two-bit codes gives, for s = 0..3, the
 // selector (P >> 2s) & 0x03030303 whose byte b is the code of weight 4b+s;
@@ -63,7 +64,11 @@ struct FmtInfo<kGrid1> {
 template <int FMT, int LPR, int MT, int EPI, bool DBG>
 __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
     using FI = FmtInfo<FMT>;
-    constexpr int RPW = kWave / LPR;              // row slots per wave
+    // Row slots are LS lanes wide (LPR rounded up to a power of two, so that
+    // the row sums are DPP segment reductions); lanes chunk >= LPR idle.
+    constexpr int LS = (LPR <= 2) ? 2 : (LPR <= 4) ? 4 : (LPR <= 8) ? 8 : (LPR <= 16) ? 16
+                     : (LPR <= 32) ? 32 : 64;
+    constexpr int RPW = kWave / LS;               // row slots per wave
     constexpr int ROWS_IT = kWaves * RPW;         // rows per workgroup iteration
     constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
     constexpr int P = kTileRows * NMAT;           // physical rows per tile
@@ -76,8 +81,8 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int slot_row = lane / LPR, chunk = lane % LPR;
-    const bool lane_on = slot_row < RPW;
+    const int slot_row = lane / LS, chunk = lane % LS;
+    const bool lane_on = chunk < LPR;
 
     const int rows = p.rows, cols = p.cols;
     const int tiles = (rows + kTileRows - 1) / kTileRows;
@@ -110,14 +115,15 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
         uint4 wq[ITERS];
         uint2 wh[ITERS];
         float dw[ITERS];
-        bool rv[ITERS];
+        bool rv[ITERS], rok[ITERS];  // lane loads for this row / row exists
         int rn[ITERS], rm[ITERS];
 #pragma unroll
         for (int it = 0; it < ITERS; ++it) {
             const int pr = it * ROWS_IT + wave * RPW + slot_row;
             const int mat = (NMAT == 2) ? (pr / kTileRows) : 0;
             const int n = n0 + pr % kTileRows;
-            rv[it] = lane_on && pr < P && n < rows;
+            rok[it] = pr < P && n < rows;
+            rv[it] = lane_on && rok[it];
             rn[it] = n;
             rm[it] = mat;
             wq[it] = make_uint4(0, 0, 0, 0);
@@ -234,29 +240,20 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
                 }
             }
 
-            // ---- sum over the LPR lanes of each row (result in the chunk-0 lane)
+            // ---- sum over the lanes of each row slot (result in its last lane)
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
 #pragma unroll
-                for (int j = 0; j < MT; ++j) {
-                    float v = part[it][j];
-#pragma unroll
-                    for (int off = 32; off >= 1; off >>= 1) {
-                        if (off < LPR) {
-                            const float o = __shfl_down(v, off);
-                            if (chunk + off < LPR) v += o;
-                        }
-                    }
-                    part[it][j] = v;
-                }
+                for (int j = 0; j < MT; ++j) part[it][j] = seg_sum<LS>(lane_on ? part[it][j] : 0.0f);
             }
+            const bool out_lane = chunk == LS - 1;
 
             // ---- epilogue
             if constexpr (EPI == kEpiF32) {
                 float* out = static_cast<float*>(p.out0);
 #pragma unroll
                 for (int it = 0; it < ITERS; ++it) {
-                    if (rv[it] && chunk == 0) {
+                    if (rok[it] && out_lane) {
 #pragma unroll
                         for (int j = 0; j < MT; ++j)
                             if (j < mcount)
@@ -266,19 +263,20 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
             } else {
 #pragma unroll
                 for (int it = 0; it < ITERS; ++it) {
-                    if (rv[it] && chunk == 0) {
+                    if (rok[it] && out_lane) {
 #pragma unroll
                         for (int j = 0; j < MT; ++j) s_gu[rm[it]][j][rn[it] - n0] = part[it][j];
                     }
                 }
                 __syncthreads();
-                if (tid < MT * kTileRows) {
+                if (wave < (MT * kTileRows + kWave - 1) / kWave) {
                     const int j = tid / kTileRows, i = tid % kTileRows;
-                    const float g = s_gu[0][j][i], u = s_gu[1][j][i];
+                    const bool jv = j < MT;
+                    const float g = jv ? s_gu[0][j][i] : 0.0f, u = jv ? s_gu[1][j][i] : 0.0f;
                     const float h = g / (1.0f + expf(-g)) * u;
-                    const float amax = wave_max32(fabsf(h));
+                    const float amax = half_wave_max(fabsf(h));
                     const float d = amax / 127.0f;
-                    if (j < mcount) {
+                    if (jv && j < mcount) {
                         const int a = p.sorted[beg + base + j];
                         const int64_t o = static_cast<int64_t>(a) * rows + n0 + i;
                         static_cast<int8_t*>(p.out0)[o] = static_cast<int8_t>(q8_value(h, d));

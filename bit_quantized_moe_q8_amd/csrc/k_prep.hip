@@ -43,68 +43,68 @@ hipError_t launch_quantize_q8(const float* x, int64_t n_blocks, int8_t* xq, floa
 
 // ---------------------------------------------------------------------------
 // Router top-k + softmax over the selected logits (no dropping: llama-modchip
-// summary, "Key highlights").  One wave per token; each lane holds the logits
-// e = lane + 64 j.  k rounds of a wave arg-max (ties -> lower expert id).
+// summary, "Key highlights").  One workgroup per token.  Each logit gets the
+// 64-bit key (order-preserving bits of the value, then the complement of its
+// expert id), so that a larger key means a larger logit or an equal logit
+// with a lower id; the rank of a logit is the number of larger keys, and the
+// logits with rank < k are the selection in output order.  One pass, no
+// serial arg-max rounds.  -0.0 is folded to +0.0 first (they compare equal).
 // ---------------------------------------------------------------------------
-constexpr int kRouteMaxPerLane = 16;  // n_experts <= 1024
+constexpr int kRouteMaxExperts = 1024;
+
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
+}
 
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= T) return;  // whole wave leaves; no workgroup barrier below
-    const float* l = logits + static_cast<int64_t>(t) * E;
-    float v[kRouteMaxPerLane];
-    uint32_t avail = 0;
-#pragma unroll
-    for (int j = 0; j < kRouteMaxPerLane; ++j) {
-        const int e = lane + 64 * j;
-        v[j] = (e < E) ? l[e] : 0.0f;
-        if (e < E) avail |= 1u << j;
-    }
-    float my_v = 0.0f;
-    int my_i = 0;
-    for (int r = 0; r < k; ++r) {
-        float bv = -INFINITY;
-        int bi = -1;
-#pragma unroll
-        for (int j = 0; j < kRouteMaxPerLane; ++j) {
-            if (((avail >> j) & 1u) && (bi < 0 || v[j] > bv)) {
-                bv = v[j];
-                bi = lane + 64 * j;
+    __shared__ uint64_t s_key[kRouteMaxExperts];
+    __shared__ float s_val[16];
+    __shared__ int s_idx[16];
+    const int tid = threadIdx.x;
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+        const float* l = logits + static_cast<int64_t>(t) * E;
+        for (int e = tid; e < E; e += 256) {
+            float v = l[e];
+            if (v == 0.0f) v = 0.0f;
+            s_key[e] = route_key(v, e);
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += 256) {
+            const uint64_t me = s_key[e];
+            int rank = 0;
+#pragma unroll 8
+            for (int j = 0; j < E; ++j) rank += (s_key[j] > me) ? 1 : 0;
+            if (rank < k) {
+                s_val[rank] = l[e];
+                s_idx[rank] = e;
             }
         }
+        __syncthreads();
+        if (tid < 64) {
+            const bool on = tid < k;
+            const float v = on ? s_val[tid] : 0.0f;
+            const float ex = on ? expf(v - s_val[0]) : 0.0f;
+            float sum = ex;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
-                bv = ov;
-                bi = oi;
+            for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+            if (on) {
+                ids[static_cast<int64_t>(t) * k + tid] = s_idx[tid];
+                w[static_cast<int64_t>(t) * k + tid] = ex / sum;
             }
         }
-        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
-        if (lane == r) {
-            my_v = bv;
-            my_i = bi;
-        }
-    }
-    const float l0 = __shfl(my_v, 0);
-    const float ex = (lane < k) ? expf(my_v - l0) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if (lane < k) {
-        ids[static_cast<int64_t>(t) * k + lane] = my_i;
-        w[static_cast<int64_t>(t) * k + lane] = ex / sum;
+        __syncthreads();
     }
 }
 
 hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, int top_k,
                              int32_t* ids, float* w, hipStream_t s) {
     if (n_tokens == 0) return hipSuccess;
-    const unsigned grid = static_cast<unsigned>((n_tokens + 3) / 4);
+    const int cap = cu_count() * 16;
+    const unsigned grid = static_cast<unsigned>(n_tokens < cap ? n_tokens : cap);
     hipLaunchKernelGGL(k_route_topk, dim3(grid), dim3(256), 0, s, logits, n_tokens, n_experts,
                        top_k, ids, w);
     return hipGetLastError();
@@ -127,9 +127,9 @@ constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * 64;
 constexpr int kGroupMaxExperts = 1024;
 
-__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* wave_tot) {
-    // kGroupThreads threads, each scanning ceil(1024/512) = 2 consecutive values
-    // is avoided: caller passes one value per thread for e = tid and e = tid + 512.
+// Exclusive scan of one int per thread over the kGroupThreads threads of the
+// workgroup (wave scans with shuffles, then the wave totals).
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int incl = v;
 #pragma unroll
@@ -174,8 +174,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
                 cnt += h;
             }
         }
-        const int off = run_off + block_exclusive_scan_1024(cnt, wave_tot);
-        const int act = run_act + block_exclusive_scan_1024(cnt > 0 ? 1 : 0, wave_tot);
+        const int off = run_off + block_exclusive_scan(cnt, wave_tot);
+        const int act = run_act + block_exclusive_scan(cnt > 0 ? 1 : 0, wave_tot);
         if (e < E) {
             offsets[e] = off;
             for (int w = 0; w < kGroupWaves; ++w) hist[w * E + e] += off;

@@ -55,17 +55,47 @@ __device__ __forceinline__ void transpose_bytes4(const uint32_t q[4], uint32_t t
     t[3] = byte_perm(u1, t1, 0x07060302u);
 }
 
-__device__ __forceinline__ float wave_sum32(float v) {
-    // sum over the 32-lane half of the wave that holds this lane
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+// DPP lane exchange: lanes of the 16-lane rows enabled in ROW_MASK read `v`
+// from the lane selected by CTRL; lanes of other rows get 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each 16
+constexpr int kDppBcast15 = 0x142;    // lane 15 of a row -> next row
+constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+
+// Sum over aligned segments of LS lanes (LS a power of two, <= 64) with DPP
+// moves only.  The full segment sum ends up in the last lane of each segment
+// (for LS <= 16 in every lane of it).
+template <int LS>
+__device__ __forceinline__ float seg_sum(float v) {
+    if constexpr (LS >= 2) v += dpp_f32<kDppQuadXor1>(v);
+    if constexpr (LS >= 4) v += dpp_f32<kDppQuadXor2>(v);
+    if constexpr (LS >= 8) v += dpp_f32<kDppHalfMirror>(v);
+    if constexpr (LS >= 16) v += dpp_f32<kDppMirror>(v);
+    if constexpr (LS >= 32) v += dpp_f32<kDppBcast15, 0xA>(v);
+    if constexpr (LS >= 64) v += dpp_f32<kDppBcast31, 0xC>(v);
     return v;
 }
 
-__device__ __forceinline__ float wave_max32(float v) {
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+// Maximum over each 32-lane half of the wave, returned in every lane of it.
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    // rows 1 and 3 now combine with rows 0 and 2 (values are >= 0 here, so
+    // the 0 returned to disabled rows is neutral)
+    v = fmaxf(v, dpp_f32<kDppBcast15, 0xA>(v));
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return (__lane_id() < 32) ? lo : hi;
 }
 
 // q8 of one value given the fp32 block max |x|: round half away from zero of

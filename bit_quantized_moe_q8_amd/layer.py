@@ -27,18 +27,28 @@ class DecodeLayer:
     def __init__(self, fmt: str, n_tokens: int, hidden: int, inter: int, n_experts: int,
                  top_k: int, device="cuda"):
         self.fmt, self.T, self.H, self.I, self.E, self.k = fmt, n_tokens, hidden, inter, n_experts, top_k
+        self.device = device
         A = n_tokens * top_k
-        f32, i8, i32 = torch.float32, torch.int8, torch.int32
-        self.xq = torch.empty((n_tokens, hidden), dtype=i8, device=device)
-        self.xd = torch.empty((n_tokens, hidden // 32), dtype=f32, device=device)
-        self.ids = torch.empty((n_tokens, top_k), dtype=i32, device=device)
-        self.w = torch.empty((n_tokens, top_k), dtype=f32, device=device)
-        self.groups = GroupBuffers.empty(n_tokens, top_k, n_experts, device)
+        f32, i8 = torch.float32, torch.int8
+        self.use_state(self.new_route_state())
         self.hq = torch.empty((A, inter), dtype=i8, device=device)
         self.hd = torch.empty((A, inter // 32), dtype=f32, device=device)
         self.out = torch.empty((A, hidden), dtype=f32, device=device)
         self.y = torch.empty((n_tokens, hidden), dtype=f32, device=device)
         self._mv = moe_matvec_ternary if fmt == "ternary" else moe_matvec_grid1
+
+    def new_route_state(self) -> dict:
+        """A separate set of q8 / routing / grouping buffers."""
+        f32, i8, i32 = torch.float32, torch.int8, torch.int32
+        T, dev = self.T, self.device
+        return {"xq": torch.empty((T, self.H), dtype=i8, device=dev),
+                "xd": torch.empty((T, self.H // 32), dtype=f32, device=dev),
+                "ids": torch.empty((T, self.k), dtype=i32, device=dev),
+                "w": torch.empty((T, self.k), dtype=f32, device=dev),
+                "groups": GroupBuffers.empty(T, self.k, self.E, dev)}
+
+    def use_state(self, st: dict):
+        self.xq, self.xd, self.ids, self.w, self.groups = st["xq"], st["xd"], st["ids"], st["w"], st["groups"]
 
     def route(self, x: torch.Tensor, logits: torch.Tensor):
         quantize_act_q8(x, self.xq, self.xd)
@@ -68,13 +78,21 @@ class PrefillLayer:
     def __init__(self, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int,
                  device="cuda"):
         self.T, self.H, self.I, self.E, self.k = n_tokens, hidden, inter, n_experts, top_k
+        self.device = device
         A = n_tokens * top_k
-        self.ids = torch.empty((n_tokens, top_k), dtype=torch.int32, device=device)
-        self.w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=device)
-        self.groups = GroupBuffers.empty(n_tokens, top_k, n_experts, device)
+        self.use_state(self.new_route_state())
         self.h = torch.empty((A, inter), dtype=torch.bfloat16, device=device)
         self.out = torch.empty((A, hidden), dtype=torch.float32, device=device)
         self.y = torch.empty((n_tokens, hidden), dtype=torch.float32, device=device)
+
+    def new_route_state(self) -> dict:
+        T, dev = self.T, self.device
+        return {"ids": torch.empty((T, self.k), dtype=torch.int32, device=dev),
+                "w": torch.empty((T, self.k), dtype=torch.float32, device=dev),
+                "groups": GroupBuffers.empty(T, self.k, self.E, dev)}
+
+    def use_state(self, st: dict):
+        self.ids, self.w, self.groups = st["ids"], st["w"], st["groups"]
 
     def route(self, logits):
         moe_route_topk(logits, self.k, self.ids, self.w)

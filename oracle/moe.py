@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (combine, group, matvec_bf16, matvec_q8, quantize_q8, route_topk,
+from . import (combine, float_to_bf16, group, matvec_bf16, matvec_q8, quantize_q8, route_topk,
                swiglu, unpack_grid1, unpack_ternary)
 
 
@@ -109,3 +109,29 @@ def tol_ok(got, ref, tsum, rel=1e-5, abs_=1e-6):
     """Elementwise |got - ref| <= rel * tsum + abs_  (the path's fp32 tolerance)."""
     got = np.asarray(got, np.float64)
     return np.abs(got - ref) <= rel * np.asarray(tsum) + abs_
+
+
+def prefill_ffn(inp: dict, assign_subset=None) -> dict:
+    """Free-running oracle chain of one prefill MoE FFN layer (grid1 weights, bf16 x).
+
+    assign_subset restricts the expert work to those assignments (the other
+    rows of g, u, h, out stay NaN)."""
+    cfg = inp["cfg"]
+    fmt, k, H, I, E = cfg["fmt"], cfg["top_k"], cfg["H"], cfg["I"], cfg["E"]
+    grid = inp.get("grid")
+    r = {}
+    r["ids"], r["w"] = route_topk(inp["logits"], k)
+    r["offsets"], r["sorted"], r["active"] = group(r["ids"], E)
+    A = r["ids"].size
+    tok = np.arange(A) // k
+    r["g"], r["tg"] = grouped_matvec_bf16(fmt, inp["gate"], grid, r["ids"], inp["x_bf16"], tok, H, assign_subset)
+    r["u"], r["tu"] = grouped_matvec_bf16(fmt, inp["up"], grid, r["ids"], inp["x_bf16"], tok, H, assign_subset)
+    rows = np.arange(A) if assign_subset is None else np.asarray(assign_subset)
+    h = np.full((A, I), np.nan)
+    h[rows] = swiglu(r["g"][rows].astype(np.float32), r["u"][rows].astype(np.float32))
+    r["h"] = h
+    hb = np.zeros((A, I), np.uint16)
+    hb[rows] = float_to_bf16(h[rows].astype(np.float32)).reshape(len(rows), I)
+    r["h_bf16"] = hb
+    r["out"], r["tout"] = grouped_matvec_bf16(fmt, inp["down"], grid, r["ids"], hb, np.arange(A), I, assign_subset)
+    return r
