@@ -13,9 +13,10 @@
 //
 // K loop, one 256-wide scale block at a time:
 //  - A (activations, gathered by assignment) is copied global -> LDS with
-//    global_load_lds_dwordx4, already in MFMA fragment order (fragment
-//    (ms, ks) = 64 lanes x 16 bytes), double-buffered so the next block's copy
-//    overlaps this block's MFMAs; every fragment read is conflict-free.
+//    global_load_lds_dwordx4, two whole 512-byte row segments per
+//    instruction, into a 3-deep ring so the copies of blocks kb+1 and kb+2
+//    overlap block kb's MFMAs; 16-byte slots are XOR-swizzled by row so
+//    every fragment read (16 rows x one 16-byte column) is conflict-free.
 //  - B (weights) is decoded on chip only: lane l of a wave takes column
 //    l % 16 and, in K step ks, the grid group 8*(l/16) + ks of the block; its
 //    11-bit index selects a 16-byte bf16 row of the codebook in LDS, which is
@@ -45,9 +46,14 @@ constexpr int kWaves = 4;
 constexpr int kMsMax = 4;                 // 16-row M subtiles per chunk
 constexpr int kChunkRows = 16 * kMsMax;   // 64
 constexpr int kKs = 8;                    // 32-wide K steps per 256 block
-constexpr int kMaxExperts = 1024;
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
+// operations of this wave are outstanding, without waiting on LDS or exports.
+constexpr int waitcnt_vm(int n) {
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
 
 __device__ __forceinline__ void copy16_to_lds(const void* g, uint4* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_wave_base), 16, 0, 0);
@@ -69,22 +75,269 @@ __device__ __forceinline__ int block_exclusive_scan256(int v, int* tmp) {
     return base + incl - v;
 }
 
+// LDS rings: A (activations) 2 slots, prefetched one K block ahead (the rows
+// are L2-resident: every row chunk is reused by all column tiles); the weight
+// group indices 3 slots, prefetched two blocks ahead (streamed once from
+// HBM).  The block scales are plain loads issued at the start of the block.  All slots are separate LDS arrays used in a fixed 6-step
+// rotation, so the compiler can tell the slots being copied into from the
+// slots being read and never waits for copies it does not need.
+constexpr int kASlotUnits = kMsMax * kKs * 64;   // 16-byte units per A slot (32 KB)
+constexpr int kPairs = 256;                        // (matrix, column) pairs per tile
+constexpr int kBQsUnits = kPairs * 2;              // 32 qs bytes per pair and block
+constexpr int kBQhUnits = kPairs;                  // 16 qh bytes per pair and block
+
+struct BSlot {
+    uint4* qs;      // [kPairs][32 B]
+    uint4* qh;      // [kPairs][16 B]
+};
+
+template <int NMAT, int NW>
+struct BCur {
+    uint2 q[NMAT][NW];
+    uint32_t h[NMAT][NW];
+};
+
+// One row chunk x one column tile, all K blocks, MS = 16-row subtiles in the
+// chunk (compile-time, so the inner loops have no branches).
+template <int EPI, bool DBG, int MS>
+__device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4* a1,
+                                          const BSlot& b0, const BSlot& b1, const BSlot& b2,
+                                          const uint4* s_cb, const int* s_row, const int* s_asg,
+                                          int e, int mrows, int nt) {
+    constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
+    constexpr int NW = (NMAT == 2) ? 2 : 4;
+    constexpr int TILE_N = kWaves * NW * 16;
+    static_assert(NMAT * TILE_N == kPairs, "tile / ring size mismatch");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
+    const int lg = lane >> 4, lc = lane & 15;
+    const int N = p.rows, K = p.cols, KB = K / 256;
+    const int qs_row = K / 8, qh_row = K / 32, d_row = K / 256;
+
+    // activation row of each A copy this lane issues (fixed for the item)
+    int arow[2 * MS];
+#pragma unroll
+    for (int ii = 0; ii < 2 * MS; ++ii) arow[ii] = s_row[2 * (wave + kWaves * ii) + (lane >> 5)];
+
+    int ncol[NW];
+    const uint16_t* dp[NMAT][NW];   // scale row of each of this lane's columns
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        ncol[w] = nt * TILE_N + (wave * NW + w) * 16 + lc;
+        const int nn = ncol[w] < N ? ncol[w] : N - 1;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+            dp[m][w] = p.d[m] + (static_cast<int64_t>(e) * N + nn) * d_row;
+    }
+
+    // A block -> slot: copy instruction i moves chunk rows 2i, 2i+1 whole
+    // (2 x 512 contiguous bytes); lane l takes row 2i + l/32 and 16-byte
+    // column c = (l % 32) ^ (row % 16), so LDS unit (row, c) sits at
+    // 64*(row/2) + 32*(row%2) + (c ^ (row%16)).
+    auto issue_a = [&](int kb, uint4* dst) {
+#pragma unroll
+        for (int ii = 0; ii < 2 * MS; ++ii) {   // MS*8 copies over 4 waves
+            const int i = wave + kWaves * ii;
+            const int row = 2 * i + (lane >> 5);
+            const int c = (lane & 31) ^ (row & 15);
+            const uint16_t* src = p.xb + static_cast<int64_t>(arow[ii]) * K + kb * 256 + c * 8;
+            copy16_to_lds(src, dst + 64 * i);
+        }
+    };
+    // Weight group indices of block kb for the tile's kPairs (matrix, column)
+    // pairs: pair pi = m * TILE_N + column offset; qs 2 x 16 bytes and qh 16
+    // bytes per pair, three 16-byte copies per wave (only the 16-byte form of
+    // the global -> LDS copy writes 16 bytes per lane; the narrow forms write
+    // one dword per lane).
+    auto issue_b = [&](int kb, const BSlot& dst) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {   // qs: 512 units, 128 per wave
+            const int u0 = (wave * 2 + r) * 64;            // uniform
+            const int m = (u0 >> 1) / TILE_N;               // uniform: 32 pairs per copy
+            const int pi = (u0 + lane) >> 1, half = lane & 1;
+            int n = nt * TILE_N + (pi % TILE_N);
+            n = n < N ? n : N - 1;
+            const uint8_t* base = (NMAT == 1 || m == 0) ? p.qs[0] : p.qs[1];
+            const uint8_t* src = base + (static_cast<int64_t>(e) * N + n) * qs_row + kb * 32 + half * 16;
+            copy16_to_lds(src, dst.qs + u0);
+        }
+        {
+            const int m = (wave * 64) / TILE_N;            // uniform
+            const int pi = wave * 64 + lane;                // qh: 256 units, 64 per wave
+            int n = nt * TILE_N + (pi % TILE_N);
+            n = n < N ? n : N - 1;
+            const uint16_t* hbase = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
+            const int64_t rowi = static_cast<int64_t>(e) * N + n;
+            copy16_to_lds(hbase + rowi * qh_row + kb * 8, dst.qh + wave * 64);
+        }
+    };
+
+    f32x4 tot[MS][NMAT][NW];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) tot[ms][m][w] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    issue_a(0, a0);
+    issue_b(0, b0);
+    issue_b(KB > 1 ? 1 : 0, b1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // One K block: copy A of block kb+1 into `an` and indices of block kb+2
+    // into `bn` (both clamped to the last block, so the instruction stream and
+    // the wait counts are the same every block), then compute block kb from
+    // `ac` / `bc`.
+    auto step = [&](int kb, const uint4* ac, uint4* an, const BSlot& bc, const BSlot& bn) {
+        // block scales of this lane's columns: plain loads, consumed after the MFMAs
+        uint16_t dbits[NMAT][NW];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) dbits[m][w] = dp[m][w][kb];
+        issue_a(kb + 1 < KB ? kb + 1 : KB - 1, an);
+        issue_b(kb + 2 < KB ? kb + 2 : KB - 1, bn);
+
+        BCur<NMAT, NW> cur;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int pi = m * TILE_N + (wave * NW + w) * 16 + lc;
+                cur.q[m][w] = reinterpret_cast<const uint2*>(bc.qs)[pi * 4 + lg];
+                cur.h[m][w] = reinterpret_cast<const uint32_t*>(bc.qh)[pi * 4 + lg];
+            }
+
+        auto frag_b = [&](int ks, bf16x8 (&bf)[NMAT][NW]) {
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const uint32_t qword = (ks < 4) ? cur.q[m][w].x : cur.q[m][w].y;
+                    const uint32_t lo8 = (qword >> (8 * (ks & 3))) & 0xffu;
+                    const uint32_t hi3 = (cur.h[m][w] >> (16 * (ks >> 2) + 3 * (ks & 3))) & 7u;
+                    bf[m][w] = __builtin_bit_cast(bf16x8, s_cb[lo8 | (hi3 << 8)]);
+                }
+        };
+        auto frag_a = [&](int ks, bf16x8 (&af)[MS]) {
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms) {
+                const int row = ms * 16 + lc;
+                const int c = 8 * lg + ks;
+                af[ms] = __builtin_bit_cast(
+                    bf16x8, ac[64 * (row >> 1) + 32 * (row & 1) + (c ^ (row & 15))]);
+            }
+        };
+
+        f32x4 blk[MS][NMAT][NW];
+        bf16x8 a_cur[MS], a_nxt[MS];
+        bf16x8 b_cur[NMAT][NW], b_nxt[NMAT][NW];
+        frag_a(0, a_cur);
+        frag_b(0, b_cur);
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+            if (ks + 1 < kKs) {
+                frag_a(ks + 1, a_nxt);
+                frag_b(ks + 1, b_nxt);
+            }
+            // keep the next step's LDS reads ahead of this step's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int w = 0; w < NW; ++w)
+                        blk[ms][m][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a_cur[ms], b_cur[m][w], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : blk[ms][m][w], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < kKs) {
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) a_cur[ms] = a_nxt[ms];
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) b_cur[m][w] = b_nxt[m][w];
+            }
+        }
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tot[ms][m][w][i] += half_bits_to_float(dbits[m][w]) * blk[ms][m][w][i];
+        // A of block kb+1 and the indices of block kb+1 (issued one block
+        // earlier) must have landed for every wave; only the 3 index copies
+        // of block kb+2, issued last, may stay outstanding (vector-memory
+        // operations retire in order).  The barrier also frees ac and bc.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
+        __syncthreads();
+    };
+
+    for (int kb0 = 0; kb0 < KB; kb0 += 6) {
+        step(kb0, a0, a1, b0, b2);
+        if (kb0 + 1 < KB) step(kb0 + 1, a1, a0, b1, b0);
+        if (kb0 + 2 < KB) step(kb0 + 2, a0, a1, b2, b1);
+        if (kb0 + 3 < KB) step(kb0 + 3, a1, a0, b0, b2);
+        if (kb0 + 4 < KB) step(kb0 + 4, a0, a1, b1, b0);
+        if (kb0 + 5 < KB) step(kb0 + 5, a1, a0, b2, b1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // clamped prefetches of the last blocks
+
+    // epilogue: lane holds rows 16*ms + 4*lg + i of column ncol[w]
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int n = ncol[w];
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ms * 16 + lg * 4 + i;
+                if (r >= mrows) continue;
+                const int64_t o = static_cast<int64_t>(s_asg[r]) * N + n;
+                if constexpr (EPI == kEpiF32) {
+                    static_cast<float*>(p.out0)[o] = tot[ms][0][w][i];
+                    if constexpr (DBG) {
+                        if (p.dbg_g) p.dbg_g[o] = tot[ms][0][w][i];
+                    }
+                } else {
+                    const float g = tot[ms][0][w][i], u = tot[ms][1][w][i];
+                    const float h = g / (1.0f + expf(-g)) * u;
+                    static_cast<uint16_t*>(p.out0)[o] = float_to_bf16_bits(h);
+                    if constexpr (DBG) {
+                        if (p.dbg_g) p.dbg_g[o] = g;
+                        if (p.dbg_u) p.dbg_u[o] = u;
+                        if (p.dbg_h) p.dbg_h[o] = h;
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int EPI, bool DBG>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
     constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
     constexpr int NW = (NMAT == 2) ? 2 : 4;       // 16-col subtiles per wave per matrix
     constexpr int TILE_N = kWaves * NW * 16;      // 128 (gate/up) or 256 (down)
 
-    __shared__ uint4 s_a[2][kMsMax][kKs][64];
+    __shared__ uint4 s_a0[kASlotUnits];
+    __shared__ uint4 s_a1[kASlotUnits];
+    __shared__ uint4 s_q0[kBQsUnits], s_q1[kBQsUnits], s_q2[kBQsUnits];
+    __shared__ uint4 s_h0[kBQhUnits], s_h1[kBQhUnits], s_h2[kBQhUnits];
     __shared__ uint4 s_cb[kGridEntries];
-    __shared__ int s_cstart[kMaxExperts + 1];
     __shared__ int s_row[kChunkRows];
     __shared__ int s_asg[kChunkRows];
-    __shared__ int s_tmp[kWaves];
+    __shared__ int s_info[4];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int E = p.n_experts, N = p.rows, K = p.cols;
-    const int KB = K / 256;
+    const int tid = threadIdx.x;
+    const int E = p.n_experts, N = p.rows;
+    const BSlot b0{s_q0, s_h0}, b1{s_q1, s_h1}, b2{s_q2, s_h2};
 
     // bf16 codebook: entry i = 8 values in {-1,0,1} -> 8 bf16 (exact).
     for (int i = tid; i < kGridEntries; i += kThreads) {
@@ -95,62 +348,55 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
             const uint32_t wv = (j < 2) ? raw.x : raw.y;
             const int v0 = static_cast<int8_t>((wv >> (16 * (j & 1))) & 0xffu);
             const int v1 = static_cast<int8_t>((wv >> (16 * (j & 1) + 8)) & 0xffu);
-            const uint32_t b0 = __builtin_bit_cast(uint32_t, static_cast<float>(v0)) >> 16;
-            const uint32_t b1 = __builtin_bit_cast(uint32_t, static_cast<float>(v1)) >> 16;
-            o[j] = b0 | (b1 << 16);
+            const uint32_t c0 = __builtin_bit_cast(uint32_t, static_cast<float>(v0)) >> 16;
+            const uint32_t c1 = __builtin_bit_cast(uint32_t, static_cast<float>(v1)) >> 16;
+            o[j] = c0 | (c1 << 16);
         }
         s_cb[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    // Chunks of up to 64 rows per expert; s_cstart = exclusive prefix.
+    // Total number of 64-row chunks over the experts.
     {
-        int cnt[4], sum = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = tid * 4 + j;
-            cnt[j] = 0;
-            if (e < E) {
-                const int m = p.offsets[e + 1] - p.offsets[e];
-                cnt[j] = (m + kChunkRows - 1) / kChunkRows;
-            }
-            sum += cnt[j];
+        int sum = 0;
+        for (int e = tid; e < E; e += kThreads) {
+            const int m = p.offsets[e + 1] - p.offsets[e];
+            sum += (m + kChunkRows - 1) / kChunkRows;
         }
-        int base = block_exclusive_scan256(sum, s_tmp);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = tid * 4 + j;
-            if (e < E) s_cstart[e] = base;
-            base += cnt[j];
-        }
-        if (tid == kThreads - 1) s_cstart[E] = base;   // total number of chunks
+        const int tot = block_exclusive_scan256(sum, s_info) + sum;
+        if (tid == kThreads - 1) s_info[0] = tot;
     }
     __syncthreads();
 
-    const int C = s_cstart[E];
+    const int C = s_info[0];
     const int NT = (N + TILE_N - 1) / TILE_N;
     const int per_xcd = ((C + 7) / 8) * NT;
     const int n_items = 8 * per_xcd;
 
-    const int64_t qs_row = K / 8, qh_row = K / 32, d_row = K / 256;
-    const int64_t qs_e = static_cast<int64_t>(N) * qs_row;
-    const int64_t qh_e = static_cast<int64_t>(N) * qh_row;
-    const int64_t d_e = static_cast<int64_t>(N) * d_row;
-    const int lg = lane >> 4;      // lane group: K range 64*lg .. 64*lg+63 of a block
-    const int lc = lane & 15;      // column inside a 16-col subtile / row inside an M subtile
-
+    // Chunks are numbered in expert order; the first thread locates chunk c
+    // by walking the experts (the walk resumes from the previous item's
+    // expert, since a workgroup's chunks increase).
+    int walk_e = 0, walk_c0 = 0;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int xcd = item & 7, j = item >> 3;
         const int c = xcd + 8 * (j / NT), nt = j % NT;
         if (c >= C) continue;   // uniform over the workgroup
-        // expert owning chunk c: the last e with s_cstart[e] <= c
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_cstart[mid] <= c) lo = mid; else hi = mid - 1;
+        if (tid == 0) {
+            int e = walk_e, c0 = walk_c0;
+            for (;;) {
+                const int m = p.offsets[e + 1] - p.offsets[e];
+                const int n = (m + kChunkRows - 1) / kChunkRows;
+                if (c < c0 + n) break;
+                c0 += n;
+                ++e;
+            }
+            walk_e = e;
+            walk_c0 = c0;
+            s_info[1] = e;
+            s_info[2] = p.offsets[e] + (c - c0) * kChunkRows;
         }
-        const int e = lo;
-        const int cbeg = p.offsets[e] + (c - s_cstart[e]) * kChunkRows;
+        __syncthreads();
+        const int e = s_info[1];
+        const int cbeg = s_info[2];
         const int mrows = min(kChunkRows, p.offsets[e + 1] - cbeg);
-        const int MS = (mrows + 15) >> 4;
         if (tid < kChunkRows) {
             const int r = tid < mrows ? tid : 0;
             const int a = p.sorted[cbeg + r];
@@ -158,152 +404,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
             s_row[tid] = p.act_by_token ? a / p.top_k : a;
         }
         __syncthreads();
-
-        // this lane's columns (clamped for the loads; outputs past N are dropped)
-        int ncol[NW], nrow[NW];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const int n = nt * TILE_N + (wave * NW + w) * 16 + lc;
-            ncol[w] = n;
-            nrow[w] = n < N ? n : N - 1;
+        switch ((mrows + 15) >> 4) {
+            case 1: gemm_item<EPI, DBG, 1>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 2: gemm_item<EPI, DBG, 2>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 3: gemm_item<EPI, DBG, 3>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
+            default: gemm_item<EPI, DBG, 4>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
         }
-        const uint8_t* qsb[NMAT];
-        const uint16_t* qhb[NMAT];
-        const uint16_t* db[NMAT];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-            qsb[m] = p.qs[m] + e * qs_e + 8 * lg;
-            qhb[m] = p.qh[m] + e * qh_e + 2 * lg;
-            db[m] = p.d[m] + e * d_e;
-        }
-
-        auto issue_a = [&](int kb, uint4 (*dst)[kKs][64]) {
-            for (int f = wave; f < MS * kKs; f += kWaves) {
-                const int ms = f / kKs, ks = f % kKs;
-                const int row = s_row[ms * 16 + lc];
-                const uint16_t* src = p.xb + static_cast<int64_t>(row) * K + kb * 256 + (8 * lg + ks) * 8;
-                copy16_to_lds(src, &dst[ms][ks][0]);
-            }
-        };
-        uint2 bq[NMAT][NW];
-        uint32_t bh[NMAT][NW];
-        float bd[NMAT][NW];
-        auto load_b = [&](int kb) {
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    bq[m][w] = *reinterpret_cast<const uint2*>(qsb[m] + nrow[w] * static_cast<int>(qs_row) + kb * 32);
-                    bh[m][w] = *reinterpret_cast<const uint32_t*>(qhb[m] + nrow[w] * static_cast<int>(qh_row) + kb * 8);
-                    bd[m][w] = half_bits_to_float(db[m][nrow[w] * static_cast<int>(d_row) + kb]);
-                }
-        };
-
-        f32x4 tot[kMsMax][NMAT][NW];
-        f32x4 blk[kMsMax][NMAT][NW];
-#pragma unroll
-        for (int ms = 0; ms < kMsMax; ++ms)
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int w = 0; w < NW; ++w) tot[ms][m][w] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        issue_a(0, s_a[0]);
-        load_b(0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-
-        for (int kb = 0; kb < KB; ++kb) {
-            uint2 cq[NMAT][NW];
-            uint32_t ch[NMAT][NW];
-            float cd[NMAT][NW];
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    cq[m][w] = bq[m][w];
-                    ch[m][w] = bh[m][w];
-                    cd[m][w] = bd[m][w];
-                }
-            if (kb + 1 < KB) {
-                issue_a(kb + 1, s_a[(kb + 1) & 1]);
-                load_b(kb + 1);
-            }
-            {
-                uint4 (*src)[kKs][64] = s_a[kb & 1];
-#pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) {
-                    bf16x8 bf[NMAT][NW];
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                        for (int w = 0; w < NW; ++w) {
-                            const uint32_t qword = (ks < 4) ? cq[m][w].x : cq[m][w].y;
-                            const uint32_t lo8 = (qword >> (8 * (ks & 3))) & 0xffu;
-                            const uint32_t hi3 = (ch[m][w] >> (16 * (ks >> 2) + 3 * (ks & 3))) & 7u;
-                            bf[m][w] = __builtin_bit_cast(bf16x8, s_cb[lo8 | (hi3 << 8)]);
-                        }
-#pragma unroll
-                    for (int ms = 0; ms < kMsMax; ++ms) {
-                        if (ms < MS) {
-                            const bf16x8 af = __builtin_bit_cast(bf16x8, src[ms][ks][lane]);
-#pragma unroll
-                            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                                for (int w = 0; w < NW; ++w)
-                                    blk[ms][m][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        af, bf[m][w], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : blk[ms][m][w], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int ms = 0; ms < kMsMax; ++ms) {
-                if (ms < MS) {
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                        for (int w = 0; w < NW; ++w)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) tot[ms][m][w][i] += cd[m][w] * blk[ms][m][w][i];
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-
-        // epilogue: lane holds rows 16*ms + 4*lg + i of column ncol[w]
-#pragma unroll
-        for (int ms = 0; ms < kMsMax; ++ms) {
-            if (ms >= MS) continue;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const int n = ncol[w];
-                if (n >= N) continue;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = ms * 16 + lg * 4 + i;
-                    if (r >= mrows) continue;
-                    const int64_t o = static_cast<int64_t>(s_asg[r]) * N + n;
-                    if constexpr (EPI == kEpiF32) {
-                        static_cast<float*>(p.out0)[o] = tot[ms][0][w][i];
-                        if constexpr (DBG) {
-                            if (p.dbg_g) p.dbg_g[o] = tot[ms][0][w][i];
-                        }
-                    } else {
-                        const float g = tot[ms][0][w][i], u = tot[ms][1][w][i];
-                        const float h = g / (1.0f + expf(-g)) * u;
-                        static_cast<uint16_t*>(p.out0)[o] = float_to_bf16_bits(h);
-                        if constexpr (DBG) {
-                            if (p.dbg_g) p.dbg_g[o] = g;
-                            if (p.dbg_u) p.dbg_u[o] = u;
-                            if (p.dbg_h) p.dbg_h[o] = h;
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();   // s_row / s_asg / A buffers are reused by the next item
+        __syncthreads();   // s_row / s_asg / rings are reused by the next item
     }
 }
 
