@@ -6,7 +6,8 @@
 // out[a][n] = sum_b d[e][n][b] * sum_{k in block b} x[r(a)][k] * w[e][n][k]
 //
 // Work item: (chunk of up to 64 rows of one expert's group, tile of output
-// columns).  Four waves; each wave owns NW 16-column subtiles of every matrix
+// columns: 256 of gate and of up, or 512 of down).  Eight waves; each wave
+// owns NW 16-column subtiles of every matrix
 // (gate and up for the SwiGLU epilogue, so h = silu(g) * u is formed in
 // registers) and all M subtiles of the chunk, i.e. MS x NMAT x NW
 // v_mfma_f32_16x16x32_bf16 tiles.
@@ -14,9 +15,9 @@
 // K loop, one 256-wide scale block at a time:
 //  - A (activations, gathered by assignment) is copied global -> LDS with
 //    global_load_lds_dwordx4, two whole 512-byte row segments per
-//    instruction, into a 3-deep ring so the copies of blocks kb+1 and kb+2
-//    overlap block kb's MFMAs; 16-byte slots are XOR-swizzled by row so
-//    every fragment read (16 rows x one 16-byte column) is conflict-free.
+//    instruction, one block ahead of the MFMAs; 16-byte slots are
+//    XOR-swizzled by row so every fragment read (16 rows x one 16-byte
+//    column) is conflict-free.
 //  - B (weights) is decoded on chip only: lane l of a wave takes column
 //    l % 16 and, in K step ks, the grid group 8*(l/16) + ks of the block; its
 //    11-bit index selects a 16-byte bf16 row of the codebook in LDS, which is
@@ -41,8 +42,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
 constexpr int kMsMax = 4;                 // 16-row M subtiles per chunk
 constexpr int kChunkRows = 16 * kMsMax;   // 64
 constexpr int kKs = 8;                    // 32-wide K steps per 256 block
@@ -54,12 +55,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int waitcnt_vm(int n) {
     return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
+// The same, also waiting for every outstanding LDS operation of the wave.
+constexpr int waitcnt_vm_lgkm0(int n) {
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4);
+}
 
 __device__ __forceinline__ void copy16_to_lds(const void* g, uint4* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_wave_base), 16, 0, 0);
 }
 
-__device__ __forceinline__ int block_exclusive_scan256(int v, int* tmp) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int incl = v;
 #pragma unroll
@@ -75,21 +80,19 @@ __device__ __forceinline__ int block_exclusive_scan256(int v, int* tmp) {
     return base + incl - v;
 }
 
-// LDS rings: A (activations) 2 slots, prefetched one K block ahead (the rows
-// are L2-resident: every row chunk is reused by all column tiles); the weight
-// group indices 3 slots, prefetched two blocks ahead (streamed once from
-// HBM).  The block scales are plain loads issued at the start of the block.  All slots are separate LDS arrays used in a fixed 6-step
-// rotation, so the compiler can tell the slots being copied into from the
-// slots being read and never waits for copies it does not need.
+// LDS rings, one K block ahead of the MFMAs: A (activations) 2 slots and the
+// weight group indices 2 slots, both copied global -> LDS (16-byte form
+// only: the narrow forms write one dword per lane).  The slots are separate
+// LDS arrays used alternately by an unrolled pair of steps, so the compiler
+// can tell the slots being copied into from the slots being read.  Block
+// scales are plain loads issued at the start of the block that uses them.
+// Eight waves (two per SIMD) each cover 64 rows x 32 columns of each matrix,
+// so one block is 256 MFMAs per SIMD (about 1.7 us at the MFMA rate) of
+// latency cover, and the two waves of a SIMD hide each other's LDS latency.
 constexpr int kASlotUnits = kMsMax * kKs * 64;   // 16-byte units per A slot (32 KB)
-constexpr int kPairs = 256;                        // (matrix, column) pairs per tile
+constexpr int kPairs = 512;                        // (matrix, column) pairs per tile
 constexpr int kBQsUnits = kPairs * 2;              // 32 qs bytes per pair and block
 constexpr int kBQhUnits = kPairs;                  // 16 qh bytes per pair and block
-
-struct BSlot {
-    uint4* qs;      // [kPairs][32 B]
-    uint4* qh;      // [kPairs][16 B]
-};
 
 template <int NMAT, int NW>
 struct BCur {
@@ -100,10 +103,12 @@ struct BCur {
 // One row chunk x one column tile, all K blocks, MS = 16-row subtiles in the
 // chunk (compile-time, so the inner loops have no branches).
 template <int EPI, bool DBG, int MS>
-__device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4* a1,
-                                          const BSlot& b0, const BSlot& b1, const BSlot& b2,
-                                          const uint4* s_cb, const int* s_row, const int* s_asg,
-                                          int e, int mrows, int nt) {
+__device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict__ a0,
+                                          uint4* __restrict__ a1, uint4* __restrict__ q0,
+                                          uint4* __restrict__ q1, uint4* __restrict__ h0,
+                                          uint4* __restrict__ h1, const uint4* __restrict__ s_cb,
+                                          const int* __restrict__ s_row,
+                                          const int* __restrict__ s_asg, int e, int mrows, int nt) {
     constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
     constexpr int NW = (NMAT == 2) ? 2 : 4;
     constexpr int TILE_N = kWaves * NW * 16;
@@ -115,9 +120,10 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4*
     const int qs_row = K / 8, qh_row = K / 32, d_row = K / 256;
 
     // activation row of each A copy this lane issues (fixed for the item)
-    int arow[2 * MS];
+    constexpr int ACOPIES = MS * 8 / kWaves;   // A copies per wave per block
+    int arow[ACOPIES];
 #pragma unroll
-    for (int ii = 0; ii < 2 * MS; ++ii) arow[ii] = s_row[2 * (wave + kWaves * ii) + (lane >> 5)];
+    for (int ii = 0; ii < ACOPIES; ++ii) arow[ii] = s_row[2 * (wave + kWaves * ii) + (lane >> 5)];
 
     int ncol[NW];
     const uint16_t* dp[NMAT][NW];   // scale row of each of this lane's columns
@@ -136,7 +142,7 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4*
     // 64*(row/2) + 32*(row%2) + (c ^ (row%16)).
     auto issue_a = [&](int kb, uint4* dst) {
 #pragma unroll
-        for (int ii = 0; ii < 2 * MS; ++ii) {   // MS*8 copies over 4 waves
+        for (int ii = 0; ii < ACOPIES; ++ii) {   // MS*8 copies over the waves
             const int i = wave + kWaves * ii;
             const int row = 2 * i + (lane >> 5);
             const int c = (lane & 31) ^ (row & 15);
@@ -146,29 +152,27 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4*
     };
     // Weight group indices of block kb for the tile's kPairs (matrix, column)
     // pairs: pair pi = m * TILE_N + column offset; qs 2 x 16 bytes and qh 16
-    // bytes per pair, three 16-byte copies per wave (only the 16-byte form of
-    // the global -> LDS copy writes 16 bytes per lane; the narrow forms write
-    // one dword per lane).
-    auto issue_b = [&](int kb, const BSlot& dst) {
+    // bytes per pair: 3 copies per wave.
+    auto issue_b = [&](int kb, uint4* dq, uint4* dh) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {   // qs: 512 units, 128 per wave
-            const int u0 = (wave * 2 + r) * 64;            // uniform
-            const int m = (u0 >> 1) / TILE_N;               // uniform: 32 pairs per copy
+        for (int r = 0; r < kBQsUnits / 64 / kWaves; ++r) {
+            const int u0 = (wave * (kBQsUnits / 64 / kWaves) + r) * 64;   // uniform
+            const int m = (u0 >> 1) / TILE_N;                             // 32 pairs per copy
             const int pi = (u0 + lane) >> 1, half = lane & 1;
             int n = nt * TILE_N + (pi % TILE_N);
             n = n < N ? n : N - 1;
             const uint8_t* base = (NMAT == 1 || m == 0) ? p.qs[0] : p.qs[1];
-            const uint8_t* src = base + (static_cast<int64_t>(e) * N + n) * qs_row + kb * 32 + half * 16;
-            copy16_to_lds(src, dst.qs + u0);
+            copy16_to_lds(base + (static_cast<int64_t>(e) * N + n) * qs_row + kb * 32 + half * 16, dq + u0);
         }
-        {
-            const int m = (wave * 64) / TILE_N;            // uniform
-            const int pi = wave * 64 + lane;                // qh: 256 units, 64 per wave
+#pragma unroll
+        for (int r = 0; r < kBQhUnits / 64 / kWaves; ++r) {
+            const int u0 = (wave * (kBQhUnits / 64 / kWaves) + r) * 64;   // uniform
+            const int m = u0 / TILE_N;                                    // 64 pairs per copy
+            const int pi = u0 + lane;
             int n = nt * TILE_N + (pi % TILE_N);
             n = n < N ? n : N - 1;
-            const uint16_t* hbase = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
-            const int64_t rowi = static_cast<int64_t>(e) * N + n;
-            copy16_to_lds(hbase + rowi * qh_row + kb * 8, dst.qh + wave * 64);
+            const uint16_t* base = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
+            copy16_to_lds(base + (static_cast<int64_t>(e) * N + n) * qh_row + kb * 8, dh + u0);
         }
     };
 
@@ -181,24 +185,24 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4*
             for (int w = 0; w < NW; ++w) tot[ms][m][w] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     issue_a(0, a0);
-    issue_b(0, b0);
-    issue_b(KB > 1 ? 1 : 0, b1);
+    issue_b(0, q0, h0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // One K block: copy A of block kb+1 into `an` and indices of block kb+2
-    // into `bn` (both clamped to the last block, so the instruction stream and
-    // the wait counts are the same every block), then compute block kb from
-    // `ac` / `bc`.
-    auto step = [&](int kb, const uint4* ac, uint4* an, const BSlot& bc, const BSlot& bn) {
-        // block scales of this lane's columns: plain loads, consumed after the MFMAs
+    // One K block: scales of block kb (plain loads), copies of block kb+1 into
+    // the other slots (clamped to the last block, so the instruction stream
+    // is the same every block), then block kb's MFMAs from `ac`, `qc`, `hc`.
+    auto step = [&](int kb, const uint4* __restrict__ ac, uint4* __restrict__ an,
+                    const uint4* __restrict__ qc, uint4* __restrict__ qn,
+                    const uint4* __restrict__ hc, uint4* __restrict__ hn) {
         uint16_t dbits[NMAT][NW];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int w = 0; w < NW; ++w) dbits[m][w] = dp[m][w][kb];
-        issue_a(kb + 1 < KB ? kb + 1 : KB - 1, an);
-        issue_b(kb + 2 < KB ? kb + 2 : KB - 1, bn);
+        const int kp = kb + 1 < KB ? kb + 1 : KB - 1;
+        issue_a(kp, an);
+        issue_b(kp, qn, hn);
 
         BCur<NMAT, NW> cur;
 #pragma unroll
@@ -206,8 +210,8 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4*
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 const int pi = m * TILE_N + (wave * NW + w) * 16 + lc;
-                cur.q[m][w] = reinterpret_cast<const uint2*>(bc.qs)[pi * 4 + lg];
-                cur.h[m][w] = reinterpret_cast<const uint32_t*>(bc.qh)[pi * 4 + lg];
+                cur.q[m][w] = reinterpret_cast<const uint2*>(qc)[pi * 4 + lg];
+                cur.h[m][w] = reinterpret_cast<const uint32_t*>(hc)[pi * 4 + lg];
             }
 
         auto frag_b = [&](int ks, bf16x8 (&bf)[NMAT][NW]) {
@@ -231,19 +235,15 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4*
             }
         };
 
+        // (two waves per SIMD hide each other's LDS latency, so fragments
+        // are not double-buffered in registers)
         f32x4 blk[MS][NMAT][NW];
-        bf16x8 a_cur[MS], a_nxt[MS];
-        bf16x8 b_cur[NMAT][NW], b_nxt[NMAT][NW];
-        frag_a(0, a_cur);
-        frag_b(0, b_cur);
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
-            if (ks + 1 < kKs) {
-                frag_a(ks + 1, a_nxt);
-                frag_b(ks + 1, b_nxt);
-            }
-            // keep the next step's LDS reads ahead of this step's MFMAs
-            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 a_cur[MS];
+            bf16x8 b_cur[NMAT][NW];
+            frag_a(ks, a_cur);
+            frag_b(ks, b_cur);
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -252,41 +252,32 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* a0, uint4*
                     for (int w = 0; w < NW; ++w)
                         blk[ms][m][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             a_cur[ms], b_cur[m][w], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : blk[ms][m][w], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (ks + 1 < kKs) {
-#pragma unroll
-                for (int ms = 0; ms < MS; ++ms) a_cur[ms] = a_nxt[ms];
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) b_cur[m][w] = b_nxt[m][w];
-            }
         }
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
+            for (int w = 0; w < NW; ++w) {
+                const float dsc = half_bits_to_float(dbits[m][w]);
 #pragma unroll
-                for (int w = 0; w < NW; ++w)
+                for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) tot[ms][m][w][i] += half_bits_to_float(dbits[m][w]) * blk[ms][m][w][i];
-        // A of block kb+1 and the indices of block kb+1 (issued one block
-        // earlier) must have landed for every wave; only the 3 index copies
-        // of block kb+2, issued last, may stay outstanding (vector-memory
-        // operations retire in order).  The barrier also frees ac and bc.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
-        __syncthreads();
+                    for (int i = 0; i < 4; ++i) tot[ms][m][w][i] += dsc * blk[ms][m][w][i];
+            }
+        // Block kb+1's copies must have landed for every wave, and this
+        // wave's LDS reads of the current slots must be complete before the
+        // barrier lets the next block's copies overwrite them.  (The scales
+        // were consumed above.)  A __syncthreads() would add a release fence;
+        // the acquire fence after the raw barrier keeps the next block's LDS
+        // reads from moving above it.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
-    for (int kb0 = 0; kb0 < KB; kb0 += 6) {
-        step(kb0, a0, a1, b0, b2);
-        if (kb0 + 1 < KB) step(kb0 + 1, a1, a0, b1, b0);
-        if (kb0 + 2 < KB) step(kb0 + 2, a0, a1, b2, b1);
-        if (kb0 + 3 < KB) step(kb0 + 3, a1, a0, b0, b2);
-        if (kb0 + 4 < KB) step(kb0 + 4, a0, a1, b1, b0);
-        if (kb0 + 5 < KB) step(kb0 + 5, a1, a0, b2, b1);
+    for (int kb0 = 0; kb0 < KB; kb0 += 2) {
+        step(kb0, a0, a1, q0, q1, h0, h1);
+        if (kb0 + 1 < KB) step(kb0 + 1, a1, a0, q1, q0, h1, h0);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // clamped prefetches of the last blocks
 
     // epilogue: lane holds rows 16*ms + 4*lg + i of column ncol[w]
 #pragma unroll
@@ -324,20 +315,19 @@ template <int EPI, bool DBG>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
     constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
     constexpr int NW = (NMAT == 2) ? 2 : 4;       // 16-col subtiles per wave per matrix
-    constexpr int TILE_N = kWaves * NW * 16;      // 128 (gate/up) or 256 (down)
+    constexpr int TILE_N = kWaves * NW * 16;      // 256 (gate/up) or 512 (down)
 
     __shared__ uint4 s_a0[kASlotUnits];
     __shared__ uint4 s_a1[kASlotUnits];
-    __shared__ uint4 s_q0[kBQsUnits], s_q1[kBQsUnits], s_q2[kBQsUnits];
-    __shared__ uint4 s_h0[kBQhUnits], s_h1[kBQhUnits], s_h2[kBQhUnits];
+    __shared__ uint4 s_q0[kBQsUnits], s_q1[kBQsUnits];
+    __shared__ uint4 s_h0[kBQhUnits], s_h1[kBQhUnits];
     __shared__ uint4 s_cb[kGridEntries];
     __shared__ int s_row[kChunkRows];
     __shared__ int s_asg[kChunkRows];
-    __shared__ int s_info[4];
+    __shared__ int s_info[kWaves];   // scan scratch (one per wave), then item info
 
     const int tid = threadIdx.x;
     const int E = p.n_experts, N = p.rows;
-    const BSlot b0{s_q0, s_h0}, b1{s_q1, s_h1}, b2{s_q2, s_h2};
 
     // bf16 codebook: entry i = 8 values in {-1,0,1} -> 8 bf16 (exact).
     for (int i = tid; i < kGridEntries; i += kThreads) {
@@ -361,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
             const int m = p.offsets[e + 1] - p.offsets[e];
             sum += (m + kChunkRows - 1) / kChunkRows;
         }
-        const int tot = block_exclusive_scan256(sum, s_info) + sum;
+        const int tot = block_exclusive_scan(sum, s_info) + sum;
         if (tid == kThreads - 1) s_info[0] = tot;
     }
     __syncthreads();
@@ -405,10 +395,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
         }
         __syncthreads();
         switch ((mrows + 15) >> 4) {
-            case 1: gemm_item<EPI, DBG, 1>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
-            case 2: gemm_item<EPI, DBG, 2>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
-            case 3: gemm_item<EPI, DBG, 3>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
-            default: gemm_item<EPI, DBG, 4>(p, s_a0, s_a1, b0, b1, b2, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 1: gemm_item<EPI, DBG, 1>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 2: gemm_item<EPI, DBG, 2>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 3: gemm_item<EPI, DBG, 3>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
+            default: gemm_item<EPI, DBG, 4>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
         }
         __syncthreads();   // s_row / s_asg / rings are reused by the next item
     }
