@@ -203,6 +203,9 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
         const int kp = kb + 1 < KB ? kb + 1 : KB - 1;
         issue_a(kp, an);
         issue_b(kp, qn, hn);
+        // keep the copies (and the scale loads) at the top of the block, so
+        // they have the whole block's MFMAs to land
+        __builtin_amdgcn_sched_barrier(0);
 
         BCur<NMAT, NW> cur;
 #pragma unroll
@@ -324,7 +327,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
     __shared__ uint4 s_cb[kGridEntries];
     __shared__ int s_row[kChunkRows];
     __shared__ int s_asg[kChunkRows];
-    __shared__ int s_info[kWaves];   // scan scratch (one per wave), then item info
+    __shared__ int s_info[kWaves];            // scan scratch (one per wave)
+    __shared__ int s_misc[2];                 // scan carry, then the item's expert
+    __shared__ int s_off[kMaxExperts + 1];    // expert_offsets
+    __shared__ int s_cpre[kMaxExperts + 1];   // first chunk number of each expert
+    static_assert(kMaxExperts == 2 * kThreads, "expert scan covers two experts per thread");
 
     const int tid = threadIdx.x;
     const int E = p.n_experts, N = p.rows;
@@ -344,49 +351,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
         }
         s_cb[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    // Total number of 64-row chunks over the experts.
+    // Chunks of up to 64 rows are numbered in expert order; s_cpre[e] is the
+    // number of expert e's first chunk (exclusive scan of the chunk counts),
+    // s_cpre[E] the total.
     {
-        int sum = 0;
-        for (int e = tid; e < E; e += kThreads) {
-            const int m = p.offsets[e + 1] - p.offsets[e];
-            sum += (m + kChunkRows - 1) / kChunkRows;
+        int run = 0;
+        for (int half = 0; half < 2; ++half) {
+            const int e = tid + half * kThreads;
+            int nch = 0;
+            if (e < E) {
+                const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
+                s_off[e] = o0;
+                nch = (o1 - o0 + kChunkRows - 1) / kChunkRows;
+            }
+            const int ex = block_exclusive_scan(nch, s_info);
+            if (e < E) s_cpre[e] = run + ex;
+            if (tid == kThreads - 1) s_misc[0] = run + ex + nch;
+            __syncthreads();
+            run = s_misc[0];
+            __syncthreads();
         }
-        const int tot = block_exclusive_scan(sum, s_info) + sum;
-        if (tid == kThreads - 1) s_info[0] = tot;
+        if (tid == 0) {
+            s_cpre[E] = run;
+            s_off[E] = p.offsets[E];
+        }
     }
     __syncthreads();
 
-    const int C = s_info[0];
+    const int C = s_cpre[E];
     const int NT = (N + TILE_N - 1) / TILE_N;
     const int per_xcd = ((C + 7) / 8) * NT;
     const int n_items = 8 * per_xcd;
 
-    // Chunks are numbered in expert order; the first thread locates chunk c
-    // by walking the experts (the walk resumes from the previous item's
-    // expert, since a workgroup's chunks increase).
-    int walk_e = 0, walk_c0 = 0;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int xcd = item & 7, j = item >> 3;
         const int c = xcd + 8 * (j / NT), nt = j % NT;
         if (c >= C) continue;   // uniform over the workgroup
-        if (tid == 0) {
-            int e = walk_e, c0 = walk_c0;
-            for (;;) {
-                const int m = p.offsets[e + 1] - p.offsets[e];
-                const int n = (m + kChunkRows - 1) / kChunkRows;
-                if (c < c0 + n) break;
-                c0 += n;
-                ++e;
-            }
-            walk_e = e;
-            walk_c0 = c0;
-            s_info[1] = e;
-            s_info[2] = p.offsets[e] + (c - c0) * kChunkRows;
-        }
+        // Exactly one expert has s_cpre[e] <= c < s_cpre[e + 1] (experts
+        // without rows have an empty range).
+        for (int e = tid; e < E; e += kThreads)
+            if (s_cpre[e] <= c && c < s_cpre[e + 1]) s_misc[1] = e;
         __syncthreads();
-        const int e = s_info[1];
-        const int cbeg = s_info[2];
-        const int mrows = min(kChunkRows, p.offsets[e + 1] - cbeg);
+        const int e = s_misc[1];
+        const int cbeg = s_off[e] + (c - s_cpre[e]) * kChunkRows;
+        const int mrows = min(kChunkRows, s_off[e + 1] - cbeg);
         if (tid < kChunkRows) {
             const int r = tid < mrows ? tid : 0;
             const int a = p.sorted[cbeg + r];

@@ -33,7 +33,7 @@ int cu_count() {
 
 namespace {
 
-constexpr int kMaxExperts = 1024;
+using pqk::kMaxExperts;
 constexpr int kMaxTopK = 16;
 constexpr int64_t kMaxAssign = int64_t(1) << 20;
 

@@ -8,6 +8,7 @@
 namespace pqk {
 
 constexpr int kGridEntries = 2048;  // grid1 codebook entries of 8 int8 values
+constexpr int kMaxExperts = 1024;   // experts per layer accepted by every entry point
 
 // Number of compute units of the current device (cached per device).
 int cu_count();
