@@ -4,13 +4,15 @@
 // against int8 activations with a 4-way int8 dot product; nothing is ever
 // dequantized to memory).
 //
-// Work decomposition.  A work item is (active expert, tile of 32 output rows);
-// items are numbered slot-major, so the first n_active*tiles items are real
-// and the launch (persistent, grid-stride over items) never needs the
-// routing on the host.  With the SwiGLU epilogue a tile holds the 32 gate rows
-// and the 32 up rows of the same outputs (gate/up fusion: pxq_llama README,
-// "Updates - 2026-07-28"), so h = silu(g)*u and its q8 block of 32 are formed
-// in the same workgroup.
+// Work decomposition.  A work item is (active expert, tile of 32 output rows)
+// and, for skewed routing, also a group of up to MT of the expert's
+// assignments (so a heavily loaded expert is spread over many workgroups
+// instead of serialising in one).  Items are numbered from the routing on the
+// device; the launch is persistent (grid-stride over items) and never needs
+// the routing on the host.  With the SwiGLU epilogue a tile holds the 32 gate
+// rows and the 32 up rows of the same outputs (gate/up fusion: pxq_llama
+// README, "Updates - 2026-07-28"), so h = silu(g)*u and its q8 block of 32
+// are formed in the same workgroup.
 //
 // Lane mapping.  A row is split into LPR chunks of 16 packed bytes (ternary:
 // 64 weights = 2 int8 blocks of 32; grid1: 16 groups = 128 weights = 4 blocks
@@ -18,11 +20,15 @@
 // row it touches, so its slice of the activation row is loaded once into
 // registers and reused for all rows (the pages stage the activation vector
 // on chip for the same reason: pxq_llama README, "Updates - 2026-07-28",
-// 2D decode driver).  Each lane issues all of its 16-byte weight loads for
-// the tile before consuming any, so a wave keeps ITERS x 16 B per lane in
-// flight.  Row slots are LPR rounded up to a power of two lanes wide (a 12-chunk
-// row uses 12 of 16 lanes), so the partial row sums reduce with DPP lane moves
-// (quad_perm, row mirrors, row_bcast) instead of LDS permutes.
+// 2D decode driver).  Row slots are LPR rounded up to a power of two lanes
+// wide, so the partial row sums reduce with DPP lane moves (quad_perm, row
+// mirrors, row_bcast) instead of LDS permutes.
+//
+// Streaming.  The rows of a tile are visited in ITERS row iterations per
+// wave; the weight loads run kDepth iterations ahead of the arithmetic (a
+// register ring), so every wave keeps several 16-byte loads per lane in
+// flight while it computes, and the grid1 codebook reads of a row are all
+// issued before their dot products.
 //
 // Ternary arithmetic.  A dword P of 16 two-bit codes gives, for s = 0..3, the
 // selector (P >> 2s) & 0x03030303 whose byte b is the code of weight 4b+s;
@@ -47,6 +53,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTileRows = 32;
+constexpr int kDepth = 4;   // row iterations of weight loads in flight per wave
 
 template <int FMT>
 struct FmtInfo;
@@ -61,11 +68,34 @@ struct FmtInfo<kGrid1> {
     static constexpr int kSubs = 4;
 };
 
-template <int FMT, int LPR, int MT, int EPI, bool DBG>
+// One lane's packed weights of one row iteration.
+struct WRow {
+    uint4 q;      // 16 bytes of qs
+    uint2 h;      // grid1: the 4 qh words of the chunk
+    uint32_t d;   // fp16 scale bits
+};
+
+// Exclusive scan of one int per thread over the workgroup; `tmp` holds one
+// int per wave.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += tmp[i];
+    __syncthreads();
+    return base + incl - v;
+}
+
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT, bool DBG>
 __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
     using FI = FmtInfo<FMT>;
-    // Row slots are LS lanes wide (LPR rounded up to a power of two, so that
-    // the row sums are DPP segment reductions); lanes chunk >= LPR idle.
     constexpr int LS = (LPR <= 2) ? 2 : (LPR <= 4) ? 4 : (LPR <= 8) ? 8 : (LPR <= 16) ? 16
                      : (LPR <= 32) ? 32 : 64;
     constexpr int RPW = kWave / LS;               // row slots per wave
@@ -73,11 +103,14 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
     constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
     constexpr int P = kTileRows * NMAT;           // physical rows per tile
     constexpr int ITERS = (P + ROWS_IT - 1) / ROWS_IT;
+    constexpr int D = ITERS < kDepth ? ITERS : kDepth;
     constexpr int SUBS = FI::kSubs;
     constexpr int ACT_DW = FI::kChunkWeights / 4;  // activation dwords per chunk
 
     __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : 1];
     __shared__ float s_gu[NMAT][MT][kTileRows];
+    __shared__ int s_apre[SPLIT ? kMaxExperts + 1 : 1];   // first group number per slot
+    __shared__ int s_scan[kWaves + 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -86,15 +119,38 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
 
     const int rows = p.rows, cols = p.cols;
     const int tiles = (rows + kTileRows - 1) / kTileRows;
-    const int n_items = *p.n_active * tiles;
-    if (static_cast<int>(blockIdx.x) >= n_items) return;
+    const int n_active = *p.n_active;
 
     if constexpr (FMT == kGrid1) {
         const uint4* src = reinterpret_cast<const uint4*>(p.grid);
         uint4* dst = reinterpret_cast<uint4*>(s_grid);
         for (int i = tid; i < kGridEntries / 2; i += kThreads) dst[i] = src[i];
-        __syncthreads();
     }
+
+    // Item count.  SPLIT: slot s owns ceil(m_s / MT) assignment groups,
+    // numbered from s_apre[s]; items are (group, tile), tile fastest.
+    int n_groups = n_active;
+    if constexpr (SPLIT) {
+        int run = 0;
+        for (int s0 = 0; s0 < n_active; s0 += kThreads) {
+            const int s = s0 + tid;
+            int na = 0;
+            if (s < n_active) {
+                const int e = p.active[s];
+                na = (p.offsets[e + 1] - p.offsets[e] + MT - 1) / MT;
+            }
+            const int ex = block_exclusive_scan(na, s_scan);
+            if (s < n_active) s_apre[s] = run + ex;
+            if (tid == kThreads - 1) s_scan[kWaves] = run + ex + na;
+            __syncthreads();
+            run = s_scan[kWaves];
+            __syncthreads();
+        }
+        if (tid == 0) s_apre[n_active] = run;
+        n_groups = run;
+    }
+    __syncthreads();   // codebook and group prefix visible
+    const int n_items = n_groups * tiles;
 
     const int64_t qs_row_bytes = (FMT == kTernary) ? cols / 4 : cols / 8;
     const int64_t qh_row = cols / 32;
@@ -104,45 +160,66 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
     const int64_t d_e = static_cast<int64_t>(rows) * d_row;
     const int n_sub_row = cols / 32;
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int slot = item / tiles, tile = item % tiles;
-        const int e = p.active[slot];
-        const int beg = p.offsets[e];
-        const int m = p.offsets[e + 1] - beg;
-        const int n0 = tile * kTileRows;
-
-        // ---- issue every weight load of this lane for the tile
-        uint4 wq[ITERS];
-        uint2 wh[ITERS];
-        float dw[ITERS];
-        bool rv[ITERS], rok[ITERS];  // lane loads for this row / row exists
-        int rn[ITERS], rm[ITERS];
-#pragma unroll
-        for (int it = 0; it < ITERS; ++it) {
-            const int pr = it * ROWS_IT + wave * RPW + slot_row;
-            const int mat = (NMAT == 2) ? (pr / kTileRows) : 0;
-            const int n = n0 + pr % kTileRows;
-            rok[it] = pr < P && n < rows;
-            rv[it] = lane_on && rok[it];
-            rn[it] = n;
-            rm[it] = mat;
-            wq[it] = make_uint4(0, 0, 0, 0);
-            wh[it] = make_uint2(0, 0);
-            dw[it] = 0.0f;
-            if (rv[it]) {
-                const uint8_t* qs = p.qs[mat] + e * qs_e + n * qs_row_bytes + chunk * 16;
-                wq[it] = *reinterpret_cast<const uint4*>(qs);
-                if constexpr (FMT == kGrid1) {
-                    const uint16_t* qh = p.qh[mat] + e * qh_e + n * qh_row + chunk * 4;
-                    wh[it] = *reinterpret_cast<const uint2*>(qh);
-                    dw[it] = half_bits_to_float(p.d[mat][e * d_e + n * d_row + chunk / 2]);
-                } else {
-                    dw[it] = half_bits_to_float(p.d[mat][e * d_e + n * d_row + chunk / 4]);
-                }
+    // Rows of iteration it: the wave's RPW row slots never straddle the
+    // gate/up boundary (RPW divides 32), so the matrix index is wave-uniform
+    // and the weight base pointers stay scalar.
+    const int wrow0 = __builtin_amdgcn_readfirstlane(wave) * RPW;
+    auto row_of = [&](int it, int n0, int& mat, int& n, bool& rok) {
+        const int pr0 = it * ROWS_IT + wrow0;   // uniform
+        mat = (NMAT == 2) ? (pr0 / kTileRows) : 0;
+        n = n0 + pr0 % kTileRows + slot_row;
+        rok = pr0 + slot_row < P && n < rows;
+    };
+    auto load_row = [&](int e, int n0, int it) -> WRow {
+        int mat, n;
+        bool rok;
+        row_of(it, n0, mat, n, rok);
+        WRow w;
+        w.q = make_uint4(0, 0, 0, 0);
+        w.h = make_uint2(0, 0);
+        w.d = 0;
+        if (lane_on && rok) {
+            // per-expert bases are uniform; lane offsets fit in 32 bits
+            const uint8_t* qsb = ((NMAT == 2 && mat == 1) ? p.qs[1] : p.qs[0]) + e * qs_e;
+            const uint16_t* db = ((NMAT == 2 && mat == 1) ? p.d[1] : p.d[0]) + e * d_e;
+            w.q = *reinterpret_cast<const uint4*>(
+                qsb + static_cast<uint32_t>(n * static_cast<int>(qs_row_bytes) + chunk * 16));
+            if constexpr (FMT == kGrid1) {
+                const uint16_t* qhb = ((NMAT == 2 && mat == 1) ? p.qh[1] : p.qh[0]) + e * qh_e;
+                w.h = *reinterpret_cast<const uint2*>(
+                    qhb + static_cast<uint32_t>(n * static_cast<int>(qh_row) + chunk * 4));
+                w.d = db[static_cast<uint32_t>(n * static_cast<int>(d_row) + chunk / 2)];
+            } else {
+                w.d = db[static_cast<uint32_t>(n * static_cast<int>(d_row) + chunk / 4)];
             }
         }
+        return w;
+    };
 
-        for (int base = 0; base < m; base += MT) {
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int grp = item / tiles, tile = item % tiles;
+        int slot = grp, g = 0;
+        if constexpr (SPLIT) {
+            // last slot whose first group is <= grp (uniform binary search)
+            int lo = 0, hi = n_active - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_apre[mid] <= grp) lo = mid; else hi = mid - 1;
+            }
+            slot = lo;
+            g = grp - s_apre[lo];
+        }
+        const int e = p.active[slot];
+        const int n0 = tile * kTileRows;
+
+        WRow buf[D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) buf[i] = load_row(e, n0, i);
+
+        const int beg = p.offsets[e];
+        const int m = p.offsets[e + 1] - beg;
+        int base = SPLIT ? g * MT : 0;
+        for (;;) {
             const int mcount = min(MT, m - base);
             // ---- activation slices of up to MT assignments
             uint32_t act[MT][ACT_DW];
@@ -159,12 +236,12 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
                     const int a = p.sorted[beg + base + j];
                     asg[j] = a;
                     const int r = p.act_by_token ? a / p.top_k : a;
-                    const uint4* xa = reinterpret_cast<const uint4*>(
-                        p.xq + static_cast<int64_t>(r) * cols + chunk * FI::kChunkWeights);
                     if (lane_on) {
+                        const uint4* xa = reinterpret_cast<const uint4*>(
+                            p.xq + static_cast<int64_t>(r) * cols + chunk * FI::kChunkWeights);
 #pragma unroll
                         for (int v = 0; v < ACT_DW / 4; ++v) {
-                            uint4 q = xa[v];
+                            const uint4 q = xa[v];
                             uint32_t qq[4] = {q.x, q.y, q.z, q.w};
                             if constexpr (FMT == kTernary) {
                                 uint32_t t[4];
@@ -183,16 +260,21 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
                 }
             }
 
-            // ---- integer block sums, fp32 scale application
-            float part[ITERS][MT];
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
+                const WRow cur = buf[it % D];
+                if (it + D < ITERS) buf[it % D] = load_row(e, n0, it + D);
+                int mat, n;
+                bool rok;
+                row_of(it, n0, mat, n, rok);
+
+                // ---- integer block sums of the MT activation rows
                 int isum[MT][SUBS];
 #pragma unroll
                 for (int j = 0; j < MT; ++j)
 #pragma unroll
                     for (int s = 0; s < SUBS; ++s) isum[j][s] = 0;
-                const uint32_t wv[4] = {wq[it].x, wq[it].y, wq[it].z, wq[it].w};
+                const uint32_t wv[4] = {cur.q.x, cur.q.y, cur.q.z, cur.q.w};
                 if constexpr (FMT == kTernary) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -206,127 +288,146 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
                         }
                     }
                 } else {
-                    const uint32_t hv[2] = {wh[it].x, wh[it].y};
+                    const uint32_t hv[2] = {cur.h.x, cur.h.y};
+                    // two halves of 8 groups: all codebook reads of a half,
+                    // then its dot products
 #pragma unroll
-                    for (int g = 0; g < 16; ++g) {
-                        const uint32_t lo = (wv[g >> 2] >> (8 * (g & 3))) & 0xffu;
-                        const uint32_t hw = hv[g >> 3] >> (16 * ((g >> 2) & 1));
-                        const uint32_t hi = (hw >> (3 * (g & 3))) & 7u;
-                        const uint2 cb = s_grid[lo | (hi << 8)];
+                    for (int hf = 0; hf < 2; ++hf) {
+                        uint2 cb[8];
 #pragma unroll
-                        for (int j = 0; j < MT; ++j) {
-                            int acc = isum[j][g >> 2];
-                            acc = dot4(static_cast<int>(cb.x), static_cast<int>(act[j][2 * g]), acc);
-                            acc = dot4(static_cast<int>(cb.y), static_cast<int>(act[j][2 * g + 1]), acc);
-                            isum[j][g >> 2] = acc;
+                        for (int q = 0; q < 8; ++q) {
+                            const int gi = 8 * hf + q;
+                            const uint32_t lo = (wv[gi >> 2] >> (8 * (gi & 3))) & 0xffu;
+                            const uint32_t hw = hv[gi >> 3] >> (16 * ((gi >> 2) & 1));
+                            const uint32_t hi = (hw >> (3 * (gi & 3))) & 7u;
+                            cb[q] = s_grid[lo | (hi << 8)];
+                        }
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int gi = 8 * hf + q;
+#pragma unroll
+                            for (int j = 0; j < MT; ++j) {
+                                int acc = isum[j][gi >> 2];
+                                acc = dot4(static_cast<int>(cb[q].x), static_cast<int>(act[j][2 * gi]), acc);
+                                acc = dot4(static_cast<int>(cb[q].y), static_cast<int>(act[j][2 * gi + 1]), acc);
+                                isum[j][gi >> 2] = acc;
+                            }
                         }
                     }
                 }
+
+                // ---- fp32 scale application and the sum over the row slot
+                const float dw = half_bits_to_float(static_cast<uint16_t>(cur.d));
+                float part[MT];
 #pragma unroll
                 for (int j = 0; j < MT; ++j) {
                     float f = 0.0f;
 #pragma unroll
                     for (int s = 0; s < SUBS; ++s) f += xs[j][s] * static_cast<float>(isum[j][s]);
-                    part[it][j] = dw[it] * f;
+                    part[j] = seg_sum<LS>(lane_on ? dw * f : 0.0f);
                     if constexpr (DBG) {
-                        int32_t* dst = p.dbg_isums[rm[it]];
-                        if (dst && rv[it] && j < mcount) {
-                            const int64_t o = (static_cast<int64_t>(asg[j]) * rows + rn[it]) * n_sub_row +
+                        int32_t* dst = p.dbg_isums[mat];
+                        if (dst && lane_on && rok && j < mcount) {
+                            const int64_t o = (static_cast<int64_t>(asg[j]) * rows + n) * n_sub_row +
                                               chunk * SUBS;
 #pragma unroll
                             for (int s = 0; s < SUBS; ++s) dst[o + s] = isum[j][s];
                         }
                     }
                 }
-            }
-
-            // ---- sum over the lanes of each row slot (result in its last lane)
-#pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-#pragma unroll
-                for (int j = 0; j < MT; ++j) part[it][j] = seg_sum<LS>(lane_on ? part[it][j] : 0.0f);
-            }
-            const bool out_lane = chunk == LS - 1;
-
-            // ---- epilogue
-            if constexpr (EPI == kEpiF32) {
-                float* out = static_cast<float*>(p.out0);
-#pragma unroll
-                for (int it = 0; it < ITERS; ++it) {
-                    if (rok[it] && out_lane) {
+                // the segment sum sits in the last lane of each row slot
+                if (rok && chunk == LS - 1) {
+                    if constexpr (EPI == kEpiF32) {
+                        float* out = static_cast<float*>(p.out0);
 #pragma unroll
                         for (int j = 0; j < MT; ++j)
-                            if (j < mcount)
-                                out[static_cast<int64_t>(asg[j]) * rows + rn[it]] = part[it][j];
+                            if (j < mcount) out[static_cast<int64_t>(asg[j]) * rows + n] = part[j];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < MT; ++j) s_gu[mat][j][n - n0] = part[j];
                     }
                 }
-            } else {
-#pragma unroll
-                for (int it = 0; it < ITERS; ++it) {
-                    if (rok[it] && out_lane) {
-#pragma unroll
-                        for (int j = 0; j < MT; ++j) s_gu[rm[it]][j][rn[it] - n0] = part[it][j];
-                    }
-                }
+            }
+
+            // ---- SwiGLU + q8 epilogue over the tile's 32 outputs
+            if constexpr (EPI == kEpiSwigluQ8) {
                 __syncthreads();
                 if (wave < (MT * kTileRows + kWave - 1) / kWave) {
                     const int j = tid / kTileRows, i = tid % kTileRows;
                     const bool jv = j < MT;
-                    const float g = jv ? s_gu[0][j][i] : 0.0f, u = jv ? s_gu[1][j][i] : 0.0f;
-                    const float h = g / (1.0f + expf(-g)) * u;
+                    const float gg = jv ? s_gu[0][j][i] : 0.0f, uu = jv ? s_gu[1][j][i] : 0.0f;
+                    const float h = gg / (1.0f + expf(-gg)) * uu;
                     const float amax = half_wave_max(fabsf(h));
-                    const float d = amax / 127.0f;
+                    const float dq = amax / 127.0f;
                     if (jv && j < mcount) {
                         const int a = p.sorted[beg + base + j];
                         const int64_t o = static_cast<int64_t>(a) * rows + n0 + i;
-                        static_cast<int8_t*>(p.out0)[o] = static_cast<int8_t>(q8_value(h, d));
+                        static_cast<int8_t*>(p.out0)[o] = static_cast<int8_t>(q8_value(h, dq));
                         if (i == 0)
                             static_cast<float*>(p.out1)[static_cast<int64_t>(a) * (rows / kTileRows) +
-                                                        tile] = d;
+                                                        tile] = dq;
                         if constexpr (DBG) {
-                            if (p.dbg_g) p.dbg_g[o] = g;
-                            if (p.dbg_u) p.dbg_u[o] = u;
+                            if (p.dbg_g) p.dbg_g[o] = gg;
+                            if (p.dbg_u) p.dbg_u[o] = uu;
                             if (p.dbg_h) p.dbg_h[o] = h;
                         }
                     }
                 }
                 __syncthreads();
             }
+
+            base += MT;
+            if (SPLIT || base >= m) break;
+            // another pass over the same tile (weights come back from cache)
+#pragma unroll
+            for (int i = 0; i < D; ++i) buf[i] = load_row(e, n0, i);
         }
     }
 }
 
-template <int FMT, int LPR, int MT, int EPI, bool DBG>
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT, bool DBG>
 hipError_t launch_one(const ExpertArgs& a, hipStream_t s) {
     const int tiles = (a.rows + kTileRows - 1) / kTileRows;
-    const int64_t max_items = static_cast<int64_t>(a.n_experts) * tiles;
+    // upper bound of the item count: every expert active, or the assignment
+    // groups (sum over slots of ceil(m / MT) <= A / MT + slots)
+    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    const int64_t slots = A < a.n_experts ? A : a.n_experts;
+    const int64_t groups = SPLIT ? (A + MT - 1) / MT + slots : slots;
+    const int64_t max_items = groups * tiles;
     const int64_t cap = static_cast<int64_t>(cu_count()) * 8;
-    const unsigned grid = static_cast<unsigned>(max_items < cap ? max_items : cap);
-    hipLaunchKernelGGL((k_matvec<FMT, LPR, MT, EPI, DBG>), dim3(grid), dim3(kThreads), 0, s, a);
+    int64_t grid = max_items < cap ? max_items : cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((k_matvec<FMT, LPR, MT, EPI, SPLIT, DBG>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <int FMT, int LPR, int MT, int EPI>
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT>
 hipError_t launch_dbg(const ExpertArgs& a, hipStream_t s) {
-    return a.debug ? launch_one<FMT, LPR, MT, EPI, true>(a, s)
-                   : launch_one<FMT, LPR, MT, EPI, false>(a, s);
+    return a.debug ? launch_one<FMT, LPR, MT, EPI, SPLIT, true>(a, s)
+                   : launch_one<FMT, LPR, MT, EPI, SPLIT, false>(a, s);
 }
 
-template <int FMT, int LPR, int MT>
+template <int FMT, int LPR, int MT, bool SPLIT>
 hipError_t launch_epi(Epi epi, const ExpertArgs& a, hipStream_t s) {
-    if (epi == kEpiF32) return launch_dbg<FMT, LPR, MT, kEpiF32>(a, s);
-    if (epi == kEpiSwigluQ8) return launch_dbg<FMT, LPR, MT, kEpiSwigluQ8>(a, s);
+    if (epi == kEpiF32) return launch_dbg<FMT, LPR, MT, kEpiF32, SPLIT>(a, s);
+    if (epi == kEpiSwigluQ8) return launch_dbg<FMT, LPR, MT, kEpiSwigluQ8, SPLIT>(a, s);
     return hipErrorInvalidValue;
 }
 
 template <int FMT, int LPR>
 hipError_t launch_mt(Epi epi, const ExpertArgs& a, hipStream_t s) {
-    // Tokens held per pass: one when every expert sees at most one activation
-    // row, otherwise a few (the assignment-per-expert mean decides).
+    // One token: every expert sees one activation row.  Up to one assignment
+    // per expert on average: pairs (single rows for grid1, whose codebook
+    // decode already holds more registers), passes repeated for the rare
+    // heavier expert.  Otherwise groups of four assignments, spread over workgroups.
     const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
-    if (a.n_tokens <= 1) return launch_epi<FMT, LPR, 1>(epi, a, s);
-    if (A <= a.n_experts) return launch_epi<FMT, LPR, 2>(epi, a, s);
-    return launch_epi<FMT, LPR, 4>(epi, a, s);
+    if (a.n_tokens <= 1) return launch_epi<FMT, LPR, 1, false>(epi, a, s);
+#ifndef PQ_MT_PAIR
+#define PQ_MT_PAIR (FMT == kGrid1 ? 1 : 2)
+#endif
+    if (A <= a.n_experts) return launch_epi<FMT, LPR, PQ_MT_PAIR, false>(epi, a, s);
+    return launch_epi<FMT, LPR, 4, true>(epi, a, s);
 }
 
 template <int FMT>
