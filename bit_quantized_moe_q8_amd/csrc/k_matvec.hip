@@ -24,11 +24,15 @@
 // wide, so the partial row sums reduce with DPP lane moves (quad_perm, row
 // mirrors, row_bcast) instead of LDS permutes.
 //
-// Streaming.  The rows of a tile are visited in ITERS row iterations per
-// wave; the weight loads run kDepth iterations ahead of the arithmetic (a
-// register ring), so every wave keeps several 16-byte loads per lane in
-// flight while it computes, and the grid1 codebook reads of a row are all
-// issued before their dot products.
+// Streaming.  The rows of a tile are visited in row iterations (one row slot
+// per wave each); the weight loads run kDepth iterations ahead of the
+// arithmetic (a register ring), so every wave keeps several 16-byte loads per
+// lane in flight while it computes, and the grid1 codebook reads of a row are
+// all issued before their dot products.  A tile is 32, 64 or 128 output rows,
+// chosen at launch so that short rows still give a long stream per item while
+// leaving enough items to fill the chip; each workgroup of the persistent
+// grid fetches the next item's routing metadata while the current item
+// streams.
 //
 // Ternary arithmetic.  A dword P of 16 two-bit codes gives, for s = 0..3, the
 // selector (P >> 2s) & 0x03030303 whose byte b is the code of weight 4b+s;
@@ -52,8 +56,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTileRows = 32;
-constexpr int kDepth = 4;   // row iterations of weight loads in flight per wave
+constexpr int kTileRows = 32;      // q8 block of the SwiGLU epilogue; tiles are 1, 2 or 4 of these
+constexpr int kMaxTileShift = 2;
+constexpr int kDepth = 4;          // row iterations of weight loads in flight per wave
 
 template <int FMT>
 struct FmtInfo;
@@ -93,22 +98,40 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp) {
     return base + incl - v;
 }
 
-template <int FMT, int LPR, int MT, int EPI, bool SPLIT, bool DBG>
+// Rows per workgroup row iteration for LPR chunks per row.
+template <int LPR>
+struct RowGeom {
+    static constexpr int LS = (LPR <= 2) ? 2 : (LPR <= 4) ? 4 : (LPR <= 8) ? 8 : (LPR <= 16) ? 16
+                            : (LPR <= 32) ? 32 : 64;
+    static constexpr int ROWS_IT = kWaves * (kWave / LS);
+};
+// Tall-tile shift: the largest TS <= kMaxTileShift with at most 2*kDepth row
+// iterations per tile (0 when a 32-row tile already has more).
+template <int LPR, int NMAT>
+constexpr int tall_shift() {
+    int ts = 0;
+    while (ts < kMaxTileShift &&
+           ((kTileRows << (ts + 1)) * NMAT + RowGeom<LPR>::ROWS_IT - 1) / RowGeom<LPR>::ROWS_IT <= 2 * kDepth)
+        ++ts;
+    return ts;
+}
+
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG>
 __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
     using FI = FmtInfo<FMT>;
-    constexpr int LS = (LPR <= 2) ? 2 : (LPR <= 4) ? 4 : (LPR <= 8) ? 8 : (LPR <= 16) ? 16
-                     : (LPR <= 32) ? 32 : 64;
+    constexpr int LS = RowGeom<LPR>::LS;
     constexpr int RPW = kWave / LS;               // row slots per wave
     constexpr int ROWS_IT = kWaves * RPW;         // rows per workgroup iteration
     constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
-    constexpr int P = kTileRows * NMAT;           // physical rows per tile
-    constexpr int ITERS = (P + ROWS_IT - 1) / ROWS_IT;
+    constexpr int TR = kTileRows << TS;                 // output rows per tile
+    constexpr int P = TR * NMAT;                        // physical rows per tile
+    constexpr int ITERS = (P + ROWS_IT - 1) / ROWS_IT;  // row iterations per tile
     constexpr int D = ITERS < kDepth ? ITERS : kDepth;
     constexpr int SUBS = FI::kSubs;
     constexpr int ACT_DW = FI::kChunkWeights / 4;  // activation dwords per chunk
 
     __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : 1];
-    __shared__ float s_gu[NMAT][MT][kTileRows];
+    __shared__ float s_gu[NMAT][MT][TR];
     __shared__ int s_apre[SPLIT ? kMaxExperts + 1 : 1];   // first group number per slot
     __shared__ int s_scan[kWaves + 1];
 
@@ -118,8 +141,8 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
     const bool lane_on = chunk < LPR;
 
     const int rows = p.rows, cols = p.cols;
-    const int tiles = (rows + kTileRows - 1) / kTileRows;
-    const int n_active = *p.n_active;
+    const int tiles = (rows + TR - 1) / TR;
+    const int n_active = load_uniform(p.n_active);
 
     if constexpr (FMT == kGrid1) {
         const uint4* src = reinterpret_cast<const uint4*>(p.grid);
@@ -162,100 +185,128 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
 
     // Rows of iteration it: the wave's RPW row slots never straddle the
     // gate/up boundary (RPW divides 32), so the matrix index is wave-uniform
-    // and the weight base pointers stay scalar.
+    // and the weight base pointers stay scalar.  Iterations past the tile
+    // (it >= NIT, only in the prefetch of short tiles) land on rows of the
+    // tile again, or on clamped rows, and are never consumed.
     const int wrow0 = __builtin_amdgcn_readfirstlane(wave) * RPW;
     auto row_of = [&](int it, int n0, int& mat, int& n, bool& rok) {
         const int pr0 = it * ROWS_IT + wrow0;   // uniform
-        mat = (NMAT == 2) ? (pr0 / kTileRows) : 0;
-        n = n0 + pr0 % kTileRows + slot_row;
+        mat = (NMAT == 2) ? (pr0 / TR) : 0;
+        n = n0 + (pr0 & (TR - 1)) + slot_row;
         rok = pr0 + slot_row < P && n < rows;
     };
     auto load_row = [&](int e, int n0, int it) -> WRow {
         int mat, n;
         bool rok;
         row_of(it, n0, mat, n, rok);
+        // Branch-free: idle lanes and rows past the end load a valid
+        // (clamped) location whose result is never used, so the loads of
+        // all iterations can be in flight together.
+        (void)rok;
+        const int nc = n < rows ? n : rows - 1;
+        const int cc = lane_on ? chunk : LPR - 1;
         WRow w;
-        w.q = make_uint4(0, 0, 0, 0);
-        w.h = make_uint2(0, 0);
-        w.d = 0;
-        if (lane_on && rok) {
-            // per-expert bases are uniform; lane offsets fit in 32 bits
-            const uint8_t* qsb = ((NMAT == 2 && mat == 1) ? p.qs[1] : p.qs[0]) + e * qs_e;
-            const uint16_t* db = ((NMAT == 2 && mat == 1) ? p.d[1] : p.d[0]) + e * d_e;
-            w.q = *reinterpret_cast<const uint4*>(
-                qsb + static_cast<uint32_t>(n * static_cast<int>(qs_row_bytes) + chunk * 16));
-            if constexpr (FMT == kGrid1) {
-                const uint16_t* qhb = ((NMAT == 2 && mat == 1) ? p.qh[1] : p.qh[0]) + e * qh_e;
-                w.h = *reinterpret_cast<const uint2*>(
-                    qhb + static_cast<uint32_t>(n * static_cast<int>(qh_row) + chunk * 4));
-                w.d = db[static_cast<uint32_t>(n * static_cast<int>(d_row) + chunk / 2)];
-            } else {
-                w.d = db[static_cast<uint32_t>(n * static_cast<int>(d_row) + chunk / 4)];
-            }
+        // per-expert bases are uniform; lane offsets fit in 32 bits
+        const uint8_t* qsb = ((NMAT == 2 && mat == 1) ? p.qs[1] : p.qs[0]) + e * qs_e;
+        const uint16_t* db = ((NMAT == 2 && mat == 1) ? p.d[1] : p.d[0]) + e * d_e;
+        w.q = *reinterpret_cast<const uint4*>(
+            qsb + static_cast<uint32_t>(nc * static_cast<int>(qs_row_bytes) + cc * 16));
+        if constexpr (FMT == kGrid1) {
+            const uint16_t* qhb = ((NMAT == 2 && mat == 1) ? p.qh[1] : p.qh[0]) + e * qh_e;
+            w.h = *reinterpret_cast<const uint2*>(
+                qhb + static_cast<uint32_t>(nc * static_cast<int>(qh_row) + cc * 4));
+            w.d = db[static_cast<uint32_t>(nc * static_cast<int>(d_row) + cc / 2)];
+        } else {
+            w.h = make_uint2(0, 0);
+            w.d = db[static_cast<uint32_t>(nc * static_cast<int>(d_row) + cc / 4)];
         }
         return w;
     };
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int grp = item / tiles, tile = item % tiles;
+    // Uniform metadata of an item, read with scalar loads (the routing arrays
+    // are read-only here); the next item's is fetched while the current
+    // item's weight loads are in flight.
+    struct Meta {
+        int e, tile, beg, m, base;
+        int asg[MT];
+    };
+    auto fetch_meta = [&](int item, Meta& mt) {
+        const int grp = item / tiles;
+        mt.tile = item % tiles;
         int slot = grp, g = 0;
         if constexpr (SPLIT) {
-            // last slot whose first group is <= grp (uniform binary search)
+            // last slot whose first group is <= grp
             int lo = 0, hi = n_active - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
                 if (s_apre[mid] <= grp) lo = mid; else hi = mid - 1;
             }
-            slot = lo;
-            g = grp - s_apre[lo];
+            slot = __builtin_amdgcn_readfirstlane(lo);
+            g = __builtin_amdgcn_readfirstlane(grp - s_apre[lo]);
         }
-        const int e = p.active[slot];
-        const int n0 = tile * kTileRows;
+        mt.e = load_uniform(p.active + slot);
+        mt.beg = load_uniform(p.offsets + mt.e);
+        mt.m = load_uniform(p.offsets + mt.e + 1) - mt.beg;
+        mt.base = SPLIT ? g * MT : 0;
+        const int mc = min(MT, mt.m - mt.base);
+#pragma unroll
+        for (int j = 0; j < MT; ++j) mt.asg[j] = load_uniform(p.sorted + mt.beg + mt.base + (j < mc ? j : mc - 1));
+    };
+
+    Meta cur;
+    if (static_cast<int>(blockIdx.x) < n_items) fetch_meta(blockIdx.x, cur);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int e = cur.e, tile = cur.tile, beg = cur.beg, m = cur.m;
+        const int n0 = tile * TR;
+        int base = cur.base;
+        int asg[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) asg[j] = cur.asg[j];
 
         WRow buf[D];
 #pragma unroll
         for (int i = 0; i < D; ++i) buf[i] = load_row(e, n0, i);
 
-        const int beg = p.offsets[e];
-        const int m = p.offsets[e + 1] - beg;
-        int base = SPLIT ? g * MT : 0;
+        const int next_item = item + gridDim.x;
+        Meta nxt = cur;
+        bool first_pass = true;
         for (;;) {
             const int mcount = min(MT, m - base);
-            // ---- activation slices of up to MT assignments
-            uint32_t act[MT][ACT_DW];
+            // ---- activation slices of up to MT assignments.  Rows past
+            // mcount repeat the last assignment (never stored) and idle lanes
+            // read chunk LPR-1, so all loads are issued before any is used.
+            const int cc = lane_on ? chunk : LPR - 1;
+            uint4 raw[MT][ACT_DW / 4];
             float xs[MT][SUBS];
-            int asg[MT];
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
-                asg[j] = 0;
+                const int r = p.act_by_token ? asg[j] / p.top_k : asg[j];
+                const uint4* xa = reinterpret_cast<const uint4*>(
+                    p.xq + static_cast<int64_t>(r) * cols + cc * FI::kChunkWeights);
 #pragma unroll
-                for (int i = 0; i < ACT_DW; ++i) act[j][i] = 0;
+                for (int v = 0; v < ACT_DW / 4; ++v) raw[j][v] = xa[v];
+                const float* xdp = p.xd + static_cast<int64_t>(r) * n_sub_row + cc * SUBS;
 #pragma unroll
-                for (int s = 0; s < SUBS; ++s) xs[j][s] = 0.0f;
-                if (j < mcount) {
-                    const int a = p.sorted[beg + base + j];
-                    asg[j] = a;
-                    const int r = p.act_by_token ? a / p.top_k : a;
-                    if (lane_on) {
-                        const uint4* xa = reinterpret_cast<const uint4*>(
-                            p.xq + static_cast<int64_t>(r) * cols + chunk * FI::kChunkWeights);
+                for (int s = 0; s < SUBS; ++s) xs[j][s] = xdp[s];
+            }
+            if (first_pass) {
+                if (next_item < n_items) fetch_meta(next_item, nxt);
+                first_pass = false;
+            }
+            uint32_t act[MT][ACT_DW];
 #pragma unroll
-                        for (int v = 0; v < ACT_DW / 4; ++v) {
-                            const uint4 q = xa[v];
-                            uint32_t qq[4] = {q.x, q.y, q.z, q.w};
-                            if constexpr (FMT == kTernary) {
-                                uint32_t t[4];
-                                transpose_bytes4(qq, t);
+            for (int j = 0; j < MT; ++j) {
 #pragma unroll
-                                for (int s = 0; s < 4; ++s) act[j][4 * v + s] = t[s];
-                            } else {
+                for (int v = 0; v < ACT_DW / 4; ++v) {
+                    uint32_t qq[4] = {raw[j][v].x, raw[j][v].y, raw[j][v].z, raw[j][v].w};
+                    if constexpr (FMT == kTernary) {
+                        uint32_t t[4];
+                        transpose_bytes4(qq, t);
 #pragma unroll
-                                for (int s = 0; s < 4; ++s) act[j][4 * v + s] = qq[s];
-                            }
-                        }
-                        const float* xdp = p.xd + static_cast<int64_t>(r) * n_sub_row + chunk * SUBS;
+                        for (int s = 0; s < 4; ++s) act[j][4 * v + s] = t[s];
+                    } else {
 #pragma unroll
-                        for (int s = 0; s < SUBS; ++s) xs[j][s] = xdp[s];
+                        for (int s = 0; s < 4; ++s) act[j][4 * v + s] = qq[s];
                     }
                 }
             }
@@ -349,23 +400,29 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
                 }
             }
 
-            // ---- SwiGLU + q8 epilogue over the tile's 32 outputs
+            // ---- SwiGLU + q8 epilogue: one 32-lane half per (assignment,
+            // block of 32 outputs); every lane takes part in each round so the
+            // half-wave max sees whole halves
             if constexpr (EPI == kEpiSwigluQ8) {
                 __syncthreads();
-                if (wave < (MT * kTileRows + kWave - 1) / kWave) {
-                    const int j = tid / kTileRows, i = tid % kTileRows;
-                    const bool jv = j < MT;
-                    const float gg = jv ? s_gu[0][j][i] : 0.0f, uu = jv ? s_gu[1][j][i] : 0.0f;
+                constexpr int npairs = MT << TS;
+                for (int r0 = 0; r0 < npairs; r0 += kThreads / 32) {
+                    const int pi = r0 + (tid >> 5), i = tid & 31;
+                    const bool pv = pi < npairs;
+                    const int j = pv ? (pi >> TS) : 0, blk = pv ? (pi & ((1 << TS) - 1)) : 0;
+                    const float gg = pv ? s_gu[0][j][blk * 32 + i] : 0.0f;
+                    const float uu = pv ? s_gu[1][j][blk * 32 + i] : 0.0f;
                     const float h = gg / (1.0f + expf(-gg)) * uu;
                     const float amax = half_wave_max(fabsf(h));
                     const float dq = amax / 127.0f;
-                    if (jv && j < mcount) {
-                        const int a = p.sorted[beg + base + j];
-                        const int64_t o = static_cast<int64_t>(a) * rows + n0 + i;
+                    const int nb = n0 + blk * 32;
+                    if (pv && j < mcount && nb < rows) {
+                        const int a = p.sorted[beg + base + j];   // j varies by lane here
+                        const int64_t o = static_cast<int64_t>(a) * rows + nb + i;
                         static_cast<int8_t*>(p.out0)[o] = static_cast<int8_t>(q8_value(h, dq));
                         if (i == 0)
                             static_cast<float*>(p.out1)[static_cast<int64_t>(a) * (rows / kTileRows) +
-                                                        tile] = dq;
+                                                        nb / kTileRows] = dq;
                         if constexpr (DBG) {
                             if (p.dbg_g) p.dbg_g[o] = gg;
                             if (p.dbg_u) p.dbg_u[o] = uu;
@@ -379,33 +436,54 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
             base += MT;
             if (SPLIT || base >= m) break;
             // another pass over the same tile (weights come back from cache)
+            const int mc = min(MT, m - base);
+#pragma unroll
+            for (int j = 0; j < MT; ++j) asg[j] = load_uniform(p.sorted + beg + base + (j < mc ? j : mc - 1));
 #pragma unroll
             for (int i = 0; i < D; ++i) buf[i] = load_row(e, n0, i);
         }
+        cur = nxt;
     }
 }
 
-template <int FMT, int LPR, int MT, int EPI, bool SPLIT, bool DBG>
-hipError_t launch_one(const ExpertArgs& a, hipStream_t s) {
-    const int tiles = (a.rows + kTileRows - 1) / kTileRows;
-    // upper bound of the item count: every expert active, or the assignment
-    // groups (sum over slots of ceil(m / MT) <= A / MT + slots)
-    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
-    const int64_t slots = A < a.n_experts ? A : a.n_experts;
-    const int64_t groups = SPLIT ? (A + MT - 1) / MT + slots : slots;
-    const int64_t max_items = groups * tiles;
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG>
+hipError_t launch_one(const ExpertArgs& a, int64_t groups, hipStream_t s) {
+    auto kernel = k_matvec<FMT, LPR, MT, EPI, SPLIT, TS, DBG>;
+    // Persistent grid of up to 8 workgroups per CU (more than are resident:
+    // a finishing workgroup's slot is refilled by the dispatcher, which
+    // measured faster than exactly the resident count or one item each).
+    const int tr = kTileRows << TS;
+    const int64_t max_items = groups * ((a.rows + tr - 1) / tr);
     const int64_t cap = static_cast<int64_t>(cu_count()) * 8;
     int64_t grid = max_items < cap ? max_items : cap;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_matvec<FMT, LPR, MT, EPI, SPLIT, DBG>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
+}
+
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT, bool DBG>
+hipError_t launch_ts(const ExpertArgs& a, hipStream_t s) {
+    constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
+    constexpr int TALL = tall_shift<LPR, NMAT>();
+    // Upper bound of the work-item groups: every slot active, or the
+    // assignment groups (sum over slots of ceil(m / MT) <= A / MT + slots).
+    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    const int64_t slots = A < a.n_experts ? A : a.n_experts;
+    const int64_t groups = SPLIT ? (A + MT - 1) / MT + slots : slots;
+    // Tall tiles (longer streams per item) only when they still leave a few
+    // items per CU.
+    if constexpr (TALL > 0) {
+        const int tr = kTileRows << TALL;
+        if (groups * ((a.rows + tr - 1) / tr) >= 4 * static_cast<int64_t>(cu_count()))
+            return launch_one<FMT, LPR, MT, EPI, SPLIT, TALL, DBG>(a, groups, s);
+    }
+    return launch_one<FMT, LPR, MT, EPI, SPLIT, 0, DBG>(a, groups, s);
 }
 
 template <int FMT, int LPR, int MT, int EPI, bool SPLIT>
 hipError_t launch_dbg(const ExpertArgs& a, hipStream_t s) {
-    return a.debug ? launch_one<FMT, LPR, MT, EPI, SPLIT, true>(a, s)
-                   : launch_one<FMT, LPR, MT, EPI, SPLIT, false>(a, s);
+    return a.debug ? launch_ts<FMT, LPR, MT, EPI, SPLIT, true>(a, s)
+                   : launch_ts<FMT, LPR, MT, EPI, SPLIT, false>(a, s);
 }
 
 template <int FMT, int LPR, int MT, bool SPLIT>

@@ -23,6 +23,14 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Load through the scalar data cache (s_load).  Only for addresses that are
+// uniform over the wave and data that nothing writes while the kernel runs
+// (routing arrays, counts).
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* ptr) {
+    return *(const __attribute__((address_space(4))) T*)(ptr);
+}
+
 // v_dot4_i32_i8: acc + sum of the four signed byte products of a and b.
 __device__ __forceinline__ int dot4(int a, int b, int acc) {
     return __builtin_amdgcn_sdot4(a, b, acc, false);
