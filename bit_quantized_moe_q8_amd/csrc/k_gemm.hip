@@ -94,6 +94,18 @@ constexpr int kPairs = 512;                        // (matrix, column) pairs per
 constexpr int kBQsUnits = kPairs * 2;              // 32 qs bytes per pair and block
 constexpr int kBQhUnits = kPairs;                  // 16 qh bytes per pair and block
 
+// Scheduling groups of one K block, K step KS onwards: vector-memory reads
+// (the NV scale loads with the first step, one copy per step while NC
+// copies last), then the step's NM MFMAs.
+template <int KS, int NC, int NV, int NM>
+__device__ __forceinline__ void order_block() {
+    if constexpr (KS < kKs) {
+        __builtin_amdgcn_sched_group_barrier(0x0020, (KS == 0 ? NV : 0) + (KS < NC ? 1 : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x0008, NM, 0);
+        order_block<KS + 1, NC, NV, NM>();
+    }
+}
+
 template <int NMAT, int NW>
 struct BCur {
     uint2 q[NMAT][NW];
@@ -126,14 +138,12 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
     for (int ii = 0; ii < ACOPIES; ++ii) arow[ii] = s_row[2 * (wave + kWaves * ii) + (lane >> 5)];
 
     int ncol[NW];
-    const uint16_t* dp[NMAT][NW];   // scale row of each of this lane's columns
+    uint32_t doff[NW];   // scale row of each of this lane's columns (element offset)
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         ncol[w] = nt * TILE_N + (wave * NW + w) * 16 + lc;
         const int nn = ncol[w] < N ? ncol[w] : N - 1;
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-            dp[m][w] = p.d[m] + (static_cast<int64_t>(e) * N + nn) * d_row;
+        doff[w] = static_cast<uint32_t>((e * N + nn) * d_row);
     }
 
     // A block -> slot: copy instruction i moves chunk rows 2i, 2i+1 whole
@@ -152,27 +162,51 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
     };
     // Weight group indices of block kb for the tile's kPairs (matrix, column)
     // pairs: pair pi = m * TILE_N + column offset; qs 2 x 16 bytes and qh 16
-    // bytes per pair: 3 copies per wave.
+    // bytes per pair: kQsCopies + kQhCopies copies per wave.
+    constexpr int kQsCopies = kBQsUnits / 64 / kWaves;
+    constexpr int kQhCopies = kBQhUnits / 64 / kWaves;
+    auto issue_qs = [&](int r, int kb, uint4* dq, int ee, int ntt) {
+        const int u0 = (wave * kQsCopies + r) * 64;   // uniform
+        const int m = (u0 >> 1) / TILE_N;              // 32 pairs per copy
+        const int pi = (u0 + lane) >> 1, half = lane & 1;
+        int n = ntt * TILE_N + (pi % TILE_N);
+        n = n < N ? n : N - 1;
+        const uint8_t* base = (NMAT == 1 || m == 0) ? p.qs[0] : p.qs[1];
+        copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qs_row + kb * 32 + half * 16, dq + u0);
+    };
+    auto issue_qh = [&](int r, int kb, uint4* dh, int ee, int ntt) {
+        const int u0 = (wave * kQhCopies + r) * 64;   // uniform
+        const int m = u0 / TILE_N;                     // 64 pairs per copy
+        const int pi = u0 + lane;
+        int n = ntt * TILE_N + (pi % TILE_N);
+        n = n < N ? n : N - 1;
+        const uint16_t* base = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
+        copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qh_row + kb * 8, dh + u0);
+    };
     auto issue_b = [&](int kb, uint4* dq, uint4* dh) {
 #pragma unroll
-        for (int r = 0; r < kBQsUnits / 64 / kWaves; ++r) {
-            const int u0 = (wave * (kBQsUnits / 64 / kWaves) + r) * 64;   // uniform
-            const int m = (u0 >> 1) / TILE_N;                             // 32 pairs per copy
-            const int pi = (u0 + lane) >> 1, half = lane & 1;
-            int n = nt * TILE_N + (pi % TILE_N);
-            n = n < N ? n : N - 1;
-            const uint8_t* base = (NMAT == 1 || m == 0) ? p.qs[0] : p.qs[1];
-            copy16_to_lds(base + (static_cast<int64_t>(e) * N + n) * qs_row + kb * 32 + half * 16, dq + u0);
-        }
+        for (int r = 0; r < kQsCopies; ++r) issue_qs(r, kb, dq, e, nt);
 #pragma unroll
-        for (int r = 0; r < kBQhUnits / 64 / kWaves; ++r) {
-            const int u0 = (wave * (kBQhUnits / 64 / kWaves) + r) * 64;   // uniform
-            const int m = u0 / TILE_N;                                    // 64 pairs per copy
-            const int pi = u0 + lane;
-            int n = nt * TILE_N + (pi % TILE_N);
-            n = n < N ? n : N - 1;
-            const uint16_t* base = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
-            copy16_to_lds(base + (static_cast<int64_t>(e) * N + n) * qh_row + kb * 8, dh + u0);
+        for (int r = 0; r < kQhCopies; ++r) issue_qh(r, kb, dh, e, nt);
+    };
+    auto issue_a_row = [&](int ii, int kb, uint4* an, int row_src) {
+        const int i = wave + kWaves * ii;
+        const int row = 2 * i + (lane >> 5);
+        const int cc = (lane & 31) ^ (row & 15);
+        copy16_to_lds(p.xb + static_cast<int64_t>(row_src) * K + kb * 256 + cc * 8, an + 64 * i);
+    };
+    // Copy c of the next block (weights first: they come from HBM, the
+    // activations mostly from L2).
+    constexpr int NCOPIES = kQsCopies + kQhCopies + ACOPIES;
+    static_assert(NCOPIES <= kKs, "one copy per K step");
+    auto issue_copy = [&](int c, int kb, uint4* an, uint4* dq, uint4* dh) {
+        if (c < kQsCopies) {
+            issue_qs(c, kb, dq, e, nt);
+        } else if (c < kQsCopies + kQhCopies) {
+            issue_qh(c - kQsCopies, kb, dh, e, nt);
+        } else {
+            const int ii = c - kQsCopies - kQhCopies;
+            issue_a_row(ii, kb, an, arow[ii]);
         }
     };
 
@@ -189,9 +223,12 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // One K block: scales of block kb (plain loads), copies of block kb+1 into
-    // the other slots (clamped to the last block, so the instruction stream
-    // is the same every block), then block kb's MFMAs from `ac`, `qc`, `hc`.
+    // One K block: scales of block kb (plain loads), then block kb's MFMAs
+    // from `ac`, `qc`, `hc` with the copies of block kb+1 into the other
+    // slots spread one per K step (clamped to the last block, so the
+    // instruction stream is the same every block): issued all at once after
+    // the barrier, the eight waves' copies queue up in the address unit while
+    // no MFMA runs.
     auto step = [&](int kb, const uint4* __restrict__ ac, uint4* __restrict__ an,
                     const uint4* __restrict__ qc, uint4* __restrict__ qn,
                     const uint4* __restrict__ hc, uint4* __restrict__ hn) {
@@ -199,13 +236,8 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int w = 0; w < NW; ++w) dbits[m][w] = dp[m][w][kb];
+            for (int w = 0; w < NW; ++w) dbits[m][w] = p.d[m][doff[w] + kb];
         const int kp = kb + 1 < KB ? kb + 1 : KB - 1;
-        issue_a(kp, an);
-        issue_b(kp, qn, hn);
-        // keep the copies (and the scale loads) at the top of the block, so
-        // they have the whole block's MFMAs to land
-        __builtin_amdgcn_sched_barrier(0);
 
         BCur<NMAT, NW> cur;
 #pragma unroll
@@ -243,6 +275,7 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
         f32x4 blk[MS][NMAT][NW];
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
+            if (ks < NCOPIES) issue_copy(ks, kp, an, qn, hn);
             bf16x8 a_cur[MS];
             bf16x8 b_cur[NMAT][NW];
             frag_a(ks, a_cur);
@@ -256,6 +289,10 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
                         blk[ms][m][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             a_cur[ms], b_cur[m][w], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : blk[ms][m][w], 0, 0, 0);
         }
+        // Instruction order of the block: the scale loads and the first copy,
+        // then one K step of MFMAs, one more copy, and so on (the scheduler
+        // would otherwise sink all copies to the end of the block).
+        order_block<0, NCOPIES, NMAT * NW, MS * NMAT * NW>();
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
