@@ -18,10 +18,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpq.so")
 
 PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE, PQ_ERR_ALIGN, PQ_ERR_UNSUPPORTED, PQ_ERR_HIP = range(6)
-PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16 = 0, 1, 2
+PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 3
 
 EXPORTS = (
-    "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert",
+    "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
     "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_gemm_dequant_tile",
     "pq_moe_combine", "pq_status_str", "pq_abi_version",
 )
@@ -65,6 +65,7 @@ def _load():
         "pq_quantize_act_q8": [p, i32, i32, p, p, p],
         "pq_moe_route_topk": [p, i32, i32, i32, p, p, p],
         "pq_group_tokens_by_expert": [p, i32, i32, i32, p, p, p, p, p],
+        "pq_moe_decode_prep": [p, p, i32, i32, i32, i32, p, p, p, p, p, p, p, p, p, p],
         "pq_moe_matvec_ternary": [ctypes.POINTER(TernaryW), ctypes.POINTER(TernaryW),
                                   ctypes.POINTER(Groups), p, p, i32, i32, p, p,
                                   ctypes.POINTER(Debug), p],
@@ -243,6 +244,26 @@ def group_tokens_by_expert(ids: torch.Tensor, n_experts: int, groups: GroupBuffe
         _ptr(ids), T, k, n_experts, _ptr(g.expert_offsets), _ptr(g.sorted_assign),
         _ptr(g.active_experts), _ptr(g.n_active), _stream()))
     return groups
+
+
+def decode_prep(x: torch.Tensor, logits: torch.Tensor, top_k: int, xq, xd, ids, w,
+                groups: GroupBuffers, y_zero: torch.Tensor = None):
+    """pq_moe_decode_prep: q8(x), top-k routing and grouping for a few tokens in
+    one launch, into the given buffers (and y_zero cleared if given)."""
+    _dt(x, torch.float32)
+    _dt(logits, torch.float32)
+    T, H = x.shape
+    E = logits.shape[1]
+    g = groups
+    _check("pq_moe_decode_prep", _lib.pq_moe_decode_prep(
+        _ptr(x), _ptr(logits), T, H, E, top_k, _ptr(xq), _ptr(xd), _ptr(ids), _ptr(w),
+        _ptr(g.expert_offsets), _ptr(g.sorted_assign), _ptr(g.active_experts), _ptr(g.n_active),
+        _ptr(y_zero), _stream()))
+
+
+def decode_prep_supported(n_tokens: int, n_experts: int, top_k: int) -> bool:
+    """The limits of pq_moe_decode_prep (include/pq.h)."""
+    return 1 <= n_tokens <= 16 and n_experts <= 1024 and n_tokens * top_k <= 256 and top_k <= 16
 
 
 def _matvec(fn_name, w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg):

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
     constexpr int LS = RowGeom<LPR>::LS;
     constexpr int RPW = kWave / LS;               // row slots per wave
     constexpr int ROWS_IT = kWaves * RPW;         // rows per workgroup iteration
-    constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
+    constexpr int NMAT = (EPI == kEpiSwigluQ8) ? 2 : 1;
     constexpr int TR = kTileRows << TS;                 // output rows per tile
     constexpr int P = TR * NMAT;                        // physical rows per tile
     constexpr int ITERS = (P + ROWS_IT - 1) / ROWS_IT;  // row iterations per tile
@@ -293,6 +293,11 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
                 if (next_item < n_items) fetch_meta(next_item, nxt);
                 first_pass = false;
             }
+            // combine weights of the pass's assignments
+            float wsel[MT];
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
+                wsel[j] = (EPI == kEpiF32Combine) ? load_uniform(static_cast<const float*>(p.out1) + asg[j]) : 0.0f;
             uint32_t act[MT][ACT_DW];
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
@@ -393,6 +398,12 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
 #pragma unroll
                         for (int j = 0; j < MT; ++j)
                             if (j < mcount) out[static_cast<int64_t>(asg[j]) * rows + n] = part[j];
+                    } else if constexpr (EPI == kEpiF32Combine) {
+                        float* y = static_cast<float*>(p.out0);
+#pragma unroll
+                        for (int j = 0; j < MT; ++j)
+                            if (j < mcount)
+                                atomicAdd(y + static_cast<int64_t>(asg[j] / p.top_k) * rows + n, wsel[j] * part[j]);
                     } else {
 #pragma unroll
                         for (int j = 0; j < MT; ++j) s_gu[mat][j][n - n0] = part[j];
@@ -463,7 +474,7 @@ hipError_t launch_one(const ExpertArgs& a, int64_t groups, hipStream_t s) {
 
 template <int FMT, int LPR, int MT, int EPI, bool SPLIT, bool DBG>
 hipError_t launch_ts(const ExpertArgs& a, hipStream_t s) {
-    constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
+    constexpr int NMAT = (EPI == kEpiSwigluQ8) ? 2 : 1;
     constexpr int TALL = tall_shift<LPR, NMAT>();
     // Upper bound of the work-item groups: every slot active, or the
     // assignment groups (sum over slots of ceil(m / MT) <= A / MT + slots).
@@ -489,6 +500,7 @@ hipError_t launch_dbg(const ExpertArgs& a, hipStream_t s) {
 template <int FMT, int LPR, int MT, bool SPLIT>
 hipError_t launch_epi(Epi epi, const ExpertArgs& a, hipStream_t s) {
     if (epi == kEpiF32) return launch_dbg<FMT, LPR, MT, kEpiF32, SPLIT>(a, s);
+    if (epi == kEpiF32Combine) return launch_dbg<FMT, LPR, MT, kEpiF32Combine, SPLIT>(a, s);
     if (epi == kEpiSwigluQ8) return launch_dbg<FMT, LPR, MT, kEpiSwigluQ8, SPLIT>(a, s);
     return hipErrorInvalidValue;
 }

@@ -10,14 +10,13 @@ namespace pqk {
 // Eight lanes per 32-value block, four floats per lane (one 16-byte load):
 // block max via three xor shuffles, d = max/127, q = round_half_away(x/d).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_quantize_q8(const float* __restrict__ x,
-                                                     int64_t n_blocks,
-                                                     int8_t* __restrict__ xq,
-                                                     float* __restrict__ xd) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+// Thread t of a pass quantizes the 4 values 4t..4t+3 (block t/8), already
+// loaded in v (zeros past the end); every lane of the 8-lane group takes
+// part in the shuffles, in range or not.
+__device__ __forceinline__ void q8_lane_v(float4 v, int64_t t, int64_t n_blocks,
+                                          int8_t* __restrict__ xq, float* __restrict__ xd) {
     const int64_t blk = t >> 3;
     const bool ok = blk < n_blocks;
-    float4 v = ok ? reinterpret_cast<const float4*>(x)[t] : make_float4(0.f, 0.f, 0.f, 0.f);
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     a = fmaxf(a, __shfl_xor(a, 1));
     a = fmaxf(a, __shfl_xor(a, 2));
@@ -30,6 +29,19 @@ __global__ __launch_bounds__(256) void k_quantize_q8(const float* __restrict__ x
                        ((static_cast<uint32_t>(q8_value(v.w, d)) & 0xffu) << 24);
     reinterpret_cast<uint32_t*>(xq)[t] = q;
     if ((t & 7) == 0) xd[blk] = d;
+}
+
+__device__ __forceinline__ void q8_lane(const float* __restrict__ x, int64_t t, int64_t n_blocks,
+                                        int8_t* __restrict__ xq, float* __restrict__ xd) {
+    const float4 v = (t >> 3) < n_blocks ? reinterpret_cast<const float4*>(x)[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    q8_lane_v(v, t, n_blocks, xq, xd);
+}
+
+__global__ __launch_bounds__(256) void k_quantize_q8(const float* __restrict__ x,
+                                                     int64_t n_blocks,
+                                                     int8_t* __restrict__ xq,
+                                                     float* __restrict__ xd) {
+    q8_lane(x, static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x, n_blocks, xq, xd);
 }
 
 hipError_t launch_quantize_q8(const float* x, int64_t n_blocks, int8_t* xq, float* xd,
@@ -58,6 +70,23 @@ __device__ __forceinline__ uint64_t route_key(float v, int e) {
     return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
 }
 
+// Softmax over the k selected logits (s_val in rank order), by the lanes of
+// one wave (lane < k holds selection `lane`); writes ids and weights.
+__device__ __forceinline__ void route_softmax_store(const float* s_val, const int* s_idx, int k,
+                                                    int lane, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w) {
+    const bool on = lane < k;
+    const float v = on ? s_val[lane] : 0.0f;
+    const float ex = on ? expf(v - s_val[0]) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (on) {
+        ids[lane] = s_idx[lane];
+        w[lane] = ex / sum;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
@@ -84,18 +113,8 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
             }
         }
         __syncthreads();
-        if (tid < 64) {
-            const bool on = tid < k;
-            const float v = on ? s_val[tid] : 0.0f;
-            const float ex = on ? expf(v - s_val[0]) : 0.0f;
-            float sum = ex;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-            if (on) {
-                ids[static_cast<int64_t>(t) * k + tid] = s_idx[tid];
-                w[static_cast<int64_t>(t) * k + tid] = ex / sum;
-            }
-        }
+        if (tid < 64) route_softmax_store(s_val, s_idx, k, tid, ids + static_cast<int64_t>(t) * k,
+                                          w + static_cast<int64_t>(t) * k);
         __syncthreads();
     }
 }
@@ -223,6 +242,179 @@ hipError_t launch_group(const int32_t* ids, int n_assign, int n_experts, int32_t
     hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), 0, s, ids, n_assign, n_experts,
                        offsets, sorted, active, n_active);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode prep for a few tokens: q8 of the activations, top-k routing
+// and the stable grouping in one workgroup (one launch instead of three; at
+// a handful of tokens each of those is a few microseconds of launch and
+// ramp for almost no work).  Results are identical to the three kernels
+// above: the same q8 lanes, the same rank-by-key selection and softmax, and
+// a grouping that is unique by definition.  Optionally zeroes y (for the
+// accumulating combine epilogue of the down mat-vec).
+// ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepWaves = kPrepThreads / kWave;
+constexpr int kPrepMaxAssign = 256;     // n_tokens * top_k
+static_assert(kMaxExperts == kPrepThreads, "one expert per thread in the grouping scans");
+
+__device__ __forceinline__ int prep_block_exclusive_scan(int v, int* wave_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += wave_tot[i];
+    __syncthreads();
+    return base + incl - v;
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_decode_prep(
+    const float* __restrict__ x, const float* __restrict__ logits, int T, int H, int E, int k,
+    int8_t* __restrict__ xq, float* __restrict__ xd, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, float* __restrict__ y_zero) {
+    __shared__ uint64_t s_key[kPrepThreads];
+    __shared__ float s_val[16][16];
+    __shared__ int s_idx[16][16];
+    __shared__ int s_ids[kPrepMaxAssign];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_tot[kPrepWaves];
+    __shared__ int s_carry[2];
+    const int tid = threadIdx.x;
+
+    // q8 of x [T][H]
+    // (eight loads in flight per thread before any is used: one workgroup
+    // cannot hide a load round trip per pass otherwise)
+    const int64_t n_blocks = static_cast<int64_t>(T) * H / 32;
+    constexpr int kQ8Batch = 8;
+    for (int64_t base = 0; base < n_blocks * 8; base += kQ8Batch * kPrepThreads) {
+        float4 v[kQ8Batch];
+#pragma unroll
+        for (int u = 0; u < kQ8Batch; ++u) {
+            const int64_t t = base + u * kPrepThreads + tid;
+            v[u] = (t >> 3) < n_blocks ? reinterpret_cast<const float4*>(x)[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kQ8Batch; ++u) q8_lane_v(v[u], base + u * kPrepThreads + tid, n_blocks, xq, xd);
+    }
+
+    // top-k per token over the same 64-bit keys as the separate router (value
+    // bits, then the complemented expert id), so the selection and its order
+    // are identical.  Up to kPrepThreads keys in all: one thread per key
+    // counts the larger keys of its token (its rank).  More: one wave per
+    // token, k rounds of a wave-wide maximum.
+    for (int i = tid; i < E; i += kPrepThreads) s_cnt[i] = 0;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int TE = T * E;
+    if (TE <= kPrepThreads) {
+        if (tid < TE) {
+            float v = logits[tid];
+            if (v == 0.0f) v = 0.0f;
+            s_key[tid] = route_key(v, tid % E);
+        }
+        __syncthreads();
+        if (tid < TE) {
+            const int t = tid / E;
+            const uint64_t me = s_key[tid];
+            const uint64_t* row = s_key + t * E;
+            int rank = 0;
+#pragma unroll 8
+            for (int j = 0; j < E; ++j) rank += (row[j] > me) ? 1 : 0;
+            if (rank < k) {
+                s_val[t][rank] = logits[tid];
+                s_idx[t][rank] = tid % E;
+            }
+        }
+    } else for (int t = wave; t < T; t += kPrepWaves) {
+        const float* l = logits + static_cast<int64_t>(t) * E;
+        uint64_t kk[kMaxExperts / kWave];
+#pragma unroll
+        for (int i = 0; i < kMaxExperts / kWave; ++i) {
+            const int e = lane + kWave * i;
+            float v = e < E ? l[e] : 0.0f;
+            if (v == 0.0f) v = 0.0f;
+            kk[i] = e < E ? route_key(v, e) : 0ull;   // real keys are never 0
+        }
+        for (int r = 0; r < k; ++r) {
+            uint64_t mx = 0;
+#pragma unroll
+            for (int i = 0; i < kMaxExperts / kWave; ++i) mx = kk[i] > mx ? kk[i] : mx;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx >> 32), off))) << 32) |
+                                   static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx & 0xffffffffu), off));
+                mx = o > mx ? o : mx;
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxExperts / kWave; ++i)
+                if (kk[i] == mx) kk[i] = 0ull;
+            if (lane == 0) {
+                const int e = static_cast<int>(~static_cast<uint32_t>(mx));
+                s_idx[t][r] = e;
+                s_val[t][r] = l[e];
+            }
+        }
+    }
+    __syncthreads();
+    for (int t = wave; t < T; t += kPrepWaves) {
+        route_softmax_store(s_val[t], s_idx[t], k, lane, ids + t * k, w + t * k);
+        if (lane < k) s_ids[t * k + lane] = s_idx[t][lane];
+    }
+    __syncthreads();
+
+    // grouping: counts, exclusive scans over the experts, stable positions
+    const int A = T * k;
+    for (int a = tid; a < A; a += kPrepThreads) atomicAdd(&s_cnt[s_ids[a]], 1);
+    __syncthreads();
+    const int cnt = tid < E ? s_cnt[tid] : 0;   // E <= kMaxExperts == kPrepThreads
+    const int off = prep_block_exclusive_scan(cnt, s_tot);
+    const int act = prep_block_exclusive_scan(cnt > 0 ? 1 : 0, s_tot);
+    if (tid < E) {
+        offsets[tid] = off;
+        if (cnt > 0) active[act] = tid;
+        s_cnt[tid] = off;
+    }
+    if (tid == kPrepThreads - 1) {
+        s_carry[0] = off + cnt;
+        s_carry[1] = act + (cnt > 0 ? 1 : 0);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        offsets[E] = s_carry[0];
+        *n_active = s_carry[1];
+    }
+    for (int a = tid; a < A; a += kPrepThreads) {
+        const int e = s_ids[a];
+        int before = 0;
+        for (int b = 0; b < a; ++b) before += (s_ids[b] == e) ? 1 : 0;
+        sorted[s_cnt[e] + before] = a;
+    }
+
+    if (y_zero) {
+        const int64_t n = static_cast<int64_t>(T) * H;
+        for (int64_t i = tid; i < n; i += kPrepThreads) y_zero[i] = 0.0f;
+    }
+}
+
+hipError_t launch_decode_prep(const float* x, const float* logits, int n_tokens, int hidden,
+                              int n_experts, int top_k, int8_t* xq, float* xd, int32_t* ids,
+                              float* w, int32_t* offsets, int32_t* sorted, int32_t* active,
+                              int32_t* n_active, float* y_zero, hipStream_t s) {
+    hipLaunchKernelGGL(k_decode_prep, dim3(1), dim3(kPrepThreads), 0, s, x, logits, n_tokens,
+                       hidden, n_experts, top_k, xq, xd, ids, w, offsets, sorted, active, n_active,
+                       y_zero);
+    return hipGetLastError();
+}
+
+bool decode_prep_supported(int n_tokens, int n_experts, int top_k) {
+    return n_tokens >= 1 && n_tokens <= kPrepWaves && n_experts <= kMaxExperts &&
+           n_tokens * top_k <= kPrepMaxAssign && top_k <= 16;
 }
 
 // ---------------------------------------------------------------------------

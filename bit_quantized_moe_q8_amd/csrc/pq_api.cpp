@@ -85,6 +85,12 @@ pq_status check_epilogue_outputs(int epilogue, const void* up, int rows, void* o
         if (!aligned(out0, 4)) return PQ_ERR_ALIGN;
         return PQ_OK;
     }
+    if (epilogue == PQ_EPI_F32_COMBINE) {
+        if (!decode) return PQ_ERR_UNSUPPORTED;
+        if (!out1) return PQ_ERR_NULL;
+        if (!aligned(out0, 4) || !aligned(out1, 4)) return PQ_ERR_ALIGN;
+        return PQ_OK;
+    }
     if ((decode && epilogue != PQ_EPI_SWIGLU_Q8) || (!decode && epilogue != PQ_EPI_SWIGLU_BF16))
         return PQ_ERR_UNSUPPORTED;
     if (!up) return PQ_ERR_NULL;
@@ -170,6 +176,32 @@ pq_status pq_group_tokens_by_expert(const int32_t* topk_ids, int32_t n_tokens, i
     });
 }
 
+pq_status pq_moe_decode_prep(const float* x, const float* logits, int32_t n_tokens,
+                             int32_t hidden, int32_t n_experts, int32_t top_k, int8_t* xq,
+                             float* xd, int32_t* topk_ids, float* topk_w,
+                             int32_t* expert_offsets, int32_t* sorted_assign,
+                             int32_t* active_experts, int32_t* n_active, float* y_zero,
+                             pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (n_tokens < 0 || hidden < 0 || hidden % 32 != 0) return PQ_ERR_SHAPE;
+        if (n_experts < 1 || n_experts > kMaxExperts) return PQ_ERR_SHAPE;
+        if (top_k < 1 || top_k > kMaxTopK || top_k > n_experts) return PQ_ERR_SHAPE;
+        if (!pqk::decode_prep_supported(n_tokens, n_experts, top_k)) return PQ_ERR_UNSUPPORTED;
+        if (!x || !logits || !xq || !xd || !topk_ids || !topk_w || !expert_offsets ||
+            !sorted_assign || !active_experts || !n_active)
+            return PQ_ERR_NULL;
+        if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(logits, 4) ||
+            !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
+            !aligned(sorted_assign, 4) || !aligned(active_experts, 4) || !aligned(n_active, 4) ||
+            !aligned(y_zero, 4))
+            return PQ_ERR_ALIGN;
+        return from_hip(pqk::launch_decode_prep(x, logits, n_tokens, hidden, n_experts, top_k, xq,
+                                                xd, topk_ids, topk_w, expert_offsets,
+                                                sorted_assign, active_experts, n_active, y_zero,
+                                                as_stream(stream)));
+    });
+}
+
 pq_status pq_moe_matvec_ternary(const pq_ternary_w* w, const pq_ternary_w* w_up,
                                 const pq_groups* g, const int8_t* xq, const float* xd,
                                 int32_t act_by_token, int32_t epilogue, void* out0, void* out1,
@@ -181,6 +213,7 @@ pq_status pq_moe_matvec_ternary(const pq_ternary_w* w, const pq_ternary_w* w_up,
         if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
         if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
             return st;
+        if (epilogue == PQ_EPI_F32_COMBINE && act_by_token) return PQ_ERR_UNSUPPORTED;
         if (epilogue == PQ_EPI_SWIGLU_Q8) {
             if (!w_up->qs || !w_up->d) return PQ_ERR_NULL;
             if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
@@ -222,6 +255,7 @@ pq_status pq_moe_matvec_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, const
         if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
         if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
             return st;
+        if (epilogue == PQ_EPI_F32_COMBINE && act_by_token) return PQ_ERR_UNSUPPORTED;
         if (epilogue == PQ_EPI_SWIGLU_Q8) {
             if (!w_up->qs || !w_up->qh || !w_up->d) return PQ_ERR_NULL;
             if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)

@@ -22,11 +22,18 @@ hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, i
 hipError_t launch_group(const int32_t* ids, int n_assign, int n_experts, int32_t* offsets,
                         int32_t* sorted, int32_t* active, int32_t* n_active, hipStream_t s);
 
+// Fused q8 + route + group for up to 16 tokens in one workgroup.
+hipError_t launch_decode_prep(const float* x, const float* logits, int n_tokens, int hidden,
+                              int n_experts, int top_k, int8_t* xq, float* xd, int32_t* ids,
+                              float* w, int32_t* offsets, int32_t* sorted, int32_t* active,
+                              int32_t* n_active, float* y_zero, hipStream_t s);
+bool decode_prep_supported(int n_tokens, int n_experts, int top_k);
+
 hipError_t launch_combine(const float* out, const float* w, int n_tokens, int top_k, int rows,
                           float* y, hipStream_t s);
 
 enum Fmt { kTernary = 0, kGrid1 = 1 };
-enum Epi { kEpiF32 = 0, kEpiSwigluQ8 = 1, kEpiSwigluBf16 = 2 };
+enum Epi { kEpiF32 = 0, kEpiSwigluQ8 = 1, kEpiSwigluBf16 = 2, kEpiF32Combine = 3 };
 
 // Everything an expert kernel needs; index 0 is `w`, index 1 is `w_up`.
 struct ExpertArgs {

@@ -7,6 +7,10 @@ nothing).
 Decode (Parakon Runtime README, "How it works"):
     q8(x) -> top-k route -> group by expert -> fused gate/up mat-vec with
     SwiGLU + q8 epilogue -> down mat-vec -> weighted combine.
+    For a few tokens the first three are one launch (pq_moe_decode_prep), and
+    for a single token the combine is fused into the down mat-vec
+    (PQ_EPI_F32_COMBINE; fp32 atomic adds, so the summation order of the
+    top-k terms is not fixed).
 Prefill (same section; dequant-per-tile GEMM for large batches):
     route -> group -> fused gate/up GEMM with SwiGLU epilogue (bf16 h)
     -> down GEMM -> weighted combine.
@@ -15,19 +19,34 @@ from __future__ import annotations
 
 import torch
 
-from . import (PQ_EPI_F32, PQ_EPI_SWIGLU_BF16, PQ_EPI_SWIGLU_Q8, GroupBuffers,
-               Grid1Weights, TernaryWeights, group_tokens_by_expert, moe_combine,
-               moe_gemm_dequant_tile, moe_matvec_grid1, moe_matvec_ternary, moe_route_topk,
-               quantize_act_q8)
+from . import (PQ_EPI_F32, PQ_EPI_F32_COMBINE, PQ_EPI_SWIGLU_BF16, PQ_EPI_SWIGLU_Q8,
+               GroupBuffers, Grid1Weights, TernaryWeights, decode_prep, decode_prep_supported,
+               group_tokens_by_expert, moe_combine, moe_gemm_dequant_tile, moe_matvec_grid1,
+               moe_matvec_ternary, moe_route_topk, quantize_act_q8)
+
+# When the decode layer fuses the prep kernels (tokens x experts up to one
+# key per thread of the fused kernel), and the combine into the down mat-vec
+# (one token).  Launch latency dominates there; above, the separate kernels
+# spread the work over more of the chip (measured: the fused prep breaks even
+# at 8 tokens x 256 experts), and the fp32 atomic adds of the fused combine
+# start to contend.
+FUSED_PREP_MAX_KEYS = 1024
+FUSED_COMBINE_MAX_TOKENS = 1
 
 
 class DecodeLayer:
     """Buffers and call sequence of one decode MoE FFN layer of fixed shape."""
 
     def __init__(self, fmt: str, n_tokens: int, hidden: int, inter: int, n_experts: int,
-                 top_k: int, device="cuda"):
+                 top_k: int, device="cuda", fused: bool = None, fused_combine: bool = None):
         self.fmt, self.T, self.H, self.I, self.E, self.k = fmt, n_tokens, hidden, inter, n_experts, top_k
         self.device = device
+        if fused is None:
+            fused = n_tokens * n_experts <= FUSED_PREP_MAX_KEYS
+        self.fused = bool(fused) and decode_prep_supported(n_tokens, n_experts, top_k)
+        if fused_combine is None:
+            fused_combine = n_tokens <= FUSED_COMBINE_MAX_TOKENS
+        self.fused_combine = self.fused and bool(fused_combine)
         A = n_tokens * top_k
         f32, i8 = torch.float32, torch.int8
         self.use_state(self.new_route_state())
@@ -51,6 +70,10 @@ class DecodeLayer:
         self.xq, self.xd, self.ids, self.w, self.groups = st["xq"], st["xd"], st["ids"], st["w"], st["groups"]
 
     def route(self, x: torch.Tensor, logits: torch.Tensor):
+        if self.fused:
+            decode_prep(x, logits, self.k, self.xq, self.xd, self.ids, self.w, self.groups,
+                        self.y if self.fused_combine else None)
+            return
         quantize_act_q8(x, self.xq, self.xd)
         moe_route_topk(logits, self.k, self.ids, self.w)
         group_tokens_by_expert(self.ids, self.E, self.groups)
@@ -59,10 +82,14 @@ class DecodeLayer:
         self._mv(gate, up, self.groups, self.xq, self.xd, True, PQ_EPI_SWIGLU_Q8, self.hq, self.hd, dbg)
 
     def down(self, down, dbg=None):
-        self._mv(down, None, self.groups, self.hq, self.hd, False, PQ_EPI_F32, self.out, None, dbg)
+        if self.fused_combine:
+            self._mv(down, None, self.groups, self.hq, self.hd, False, PQ_EPI_F32_COMBINE, self.y, self.w, dbg)
+        else:
+            self._mv(down, None, self.groups, self.hq, self.hd, False, PQ_EPI_F32, self.out, None, dbg)
 
     def combine(self):
-        moe_combine(self.out, self.w, self.k, self.y)
+        if not self.fused_combine:   # else the down mat-vec already accumulated y
+            moe_combine(self.out, self.w, self.k, self.y)
 
     def __call__(self, x, logits, gate, up, down):
         self.route(x, logits)

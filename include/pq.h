@@ -73,9 +73,10 @@ typedef enum pq_status {
 } pq_status;
 
 enum {
-    PQ_EPI_F32 = 0,        /* out0 = float [A][rows] */
-    PQ_EPI_SWIGLU_Q8 = 1,  /* out0 = int8 hq [A][rows], out1 = float hd [A][rows/32] */
-    PQ_EPI_SWIGLU_BF16 = 2 /* out0 = bf16 bits h [A][rows] */
+    PQ_EPI_F32 = 0,         /* out0 = float [A][rows] */
+    PQ_EPI_SWIGLU_Q8 = 1,   /* out0 = int8 hq [A][rows], out1 = float hd [A][rows/32] */
+    PQ_EPI_SWIGLU_BF16 = 2, /* out0 = bf16 bits h [A][rows] */
+    PQ_EPI_F32_COMBINE = 3  /* out0 = float y [n_tokens][rows] (+=), out1 = float topk_w */
 };
 
 /* hipStream_t, passed as an opaque pointer; NULL = null stream. */
@@ -161,6 +162,26 @@ pq_status pq_group_tokens_by_expert(const int32_t *topk_ids, int32_t n_tokens, i
                                     int32_t *n_active, pq_stream stream);
 
 /*
+ * Decode prep for a few tokens in one launch: pq_quantize_act_q8 of x
+ * [n_tokens][hidden], pq_moe_route_topk of logits [n_tokens][n_experts] and
+ * pq_group_tokens_by_expert of the result, with outputs identical to those
+ * three calls (same layouts as there); if y_zero != NULL it is also set to
+ * zero, float [n_tokens][hidden] (for PQ_EPI_F32_COMBINE).  One workgroup
+ * (one wave per token for the selection): 1 <= n_tokens <= 16,
+ * n_tokens*top_k <= 256, n_experts <= 1024, top_k <= 16, hidden % 32 == 0;
+ * otherwise
+ * PQ_ERR_UNSUPPORTED (use the three calls).  (Parakon Runtime README, "How it
+ * works": int8 activations; llama-modchip summary, "Key highlights": top-k
+ * with no dropping; pxq_llama README, "What's PXQ?": grouped experts.)
+ */
+pq_status pq_moe_decode_prep(const float *x, const float *logits, int32_t n_tokens,
+                             int32_t hidden, int32_t n_experts, int32_t top_k, int8_t *xq,
+                             float *xd, int32_t *topk_ids, float *topk_w,
+                             int32_t *expert_offsets, int32_t *sorted_assign,
+                             int32_t *active_experts, int32_t *n_active, float *y_zero,
+                             pq_stream stream);
+
+/*
  * Grouped expert mat-vec over packed ternary weights against q8 activations
  * (Parakon Runtime README, "How it works": fused decode mat-vec reading the
  * packed blocks directly with int8 dot products; gate/up fusion with SiLU:
@@ -172,6 +193,15 @@ pq_status pq_group_tokens_by_expert(const int32_t *topk_ids, int32_t n_tokens, i
  *   PQ_EPI_SWIGLU_Q8: needs w_up (same shape); g = W_e . act_r, u = Wup_e . act_r,
  *                     h = silu(g) * u in fp32, then q8 of h per 32 rows:
  *                     out0 int8 [A][rows], out1 float [A][rows/32]; rows % 32 == 0.
+ *   PQ_EPI_F32_COMBINE: the weighted combine fused into the mat-vec (for the
+ *                     down projection, act_by_token == 0): out0 float y
+ *                     [n_tokens][rows] receives y[a/top_k][n] += topk_w[a] *
+ *                     (W_e . act_a) by fp32 atomic adds, so y must hold zeros
+ *                     (pq_moe_decode_prep can clear it) and the order of the
+ *                     top_k additions is unspecified (the result can differ in
+ *                     the last bits between runs); out1 = topk_w float
+ *                     [n_tokens][top_k] (read only).  Saves the separate
+ *                     pq_moe_combine launch at a few tokens.
  * cols % 256 == 0 and cols/64 in {2,4,8,12,16,32,64} (cols 256..4096 for
  * those divisors); rows >= 1.  w->n_experts == g->n_experts.  dbg may be NULL.
  */

@@ -192,12 +192,13 @@ def test_matvec_one_expert_many_tokens():
 
 # ----------------------------------------------------------- decode layers
 
-def _run_layer(name, **override):
+def _run_layer(name, fused=False, **override):
     inp = decode_inputs(name, **override)
     cfg = inp["cfg"]
     fmt, T, H, I, E, k = cfg["fmt"], cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
     A = T * k
-    layer = DecodeLayer(fmt, T, H, I, E, k, dev())
+    layer = DecodeLayer(fmt, T, H, I, E, k, dev(), fused=fused, fused_combine=fused)
+    assert layer.fused == fused and layer.fused_combine == fused
     grid = inp.get("grid")
     W = {n: weights_to_device(fmt, inp[n], grid) for n in ("gate", "up", "down")}
     x, logits = to_dev(inp["x"]), to_dev(inp["logits"])
@@ -221,6 +222,7 @@ def _run_layer(name, **override):
     layer(x, logits, W["gate"], W["up"], W["down"])
     torch.cuda.synchronize()
     gpu["hq2"], gpu["y2"] = to_host(layer.hq), to_host(layer.y)
+    gpu["fused"] = fused
     return inp, gpu
 
 
@@ -256,13 +258,22 @@ def _check_layer(inp, gpu):
     # stage 4: down on the GPU's own hq/hd
     o_ref, to, io = moe.grouped_matvec_q8(fmt, inp["down"], grid, ids, gpu["hq"], gpu["hd"], np.arange(A), I)
     assert_equal(gpu["dbg_isum_d"], io, "down isums")
-    assert_tol(gpu["out"], o_ref, to, "out")
-    # stage 5: combine on the GPU's own out and w
-    y_ref, ty = oracle.combine(gpu["out"], gpu["w"], k)
-    assert_tol(gpu["y"], y_ref, ty, "y (staged)")
-    # repeat run is bitwise identical
-    assert_equal(gpu["hq2"], gpu["hq"], "hq repeat")
-    assert_equal(gpu["y2"], gpu["y"], "y repeat")
+    ty_down = np.einsum("tj,tjn->tn", np.abs(gpu["w"].astype(np.float64)), to.reshape(T, k, H))
+    if gpu["fused"]:
+        # stage 5 fused into the down mat-vec: y against the oracle's combine
+        # of the oracle's down outputs (the bound adds the weighted term sums)
+        y_ref, ty = oracle.combine(o_ref.astype(np.float32), gpu["w"], k)
+        assert_tol(gpu["y"], y_ref, ty + ty_down, "y (fused combine)")
+        assert_equal(gpu["hq2"], gpu["hq"], "hq repeat")
+        assert_tol(gpu["y2"], y_ref, ty + ty_down, "y repeat (fused combine)")
+    else:
+        assert_tol(gpu["out"], o_ref, to, "out")
+        # stage 5: combine on the GPU's own out and w
+        y_ref, ty = oracle.combine(gpu["out"], gpu["w"], k)
+        assert_tol(gpu["y"], y_ref, ty, "y (staged)")
+        # repeat run is bitwise identical
+        assert_equal(gpu["hq2"], gpu["hq"], "hq repeat")
+        assert_equal(gpu["y2"], gpu["y"], "y repeat")
     # free-running oracle chain: tokens whose q8 h rows all agree must match y
     ref = moe.decode_ffn(inp, want_isums=False)
     same = (ref["hq"] == gpu["hq"]).reshape(T, k, I).all(axis=(1, 2))
@@ -273,17 +284,79 @@ def _check_layer(inp, gpu):
     assert_tol(gpu["y"][same], ref["y"][same], ty_free[same], "y (free-running)")
 
 
-@pytest.mark.parametrize("name,override", [
-    ("ternary_moe_decode_t1", {}),
-    ("grid1_moe_decode_t8", {}),
-    ("ternary_moe_decode_t64_zipf", {}),
-    ("ternary_moe_decode_t1", dict(T=4, E=16, H=768, I=256, top_k=4)),
-    ("grid1_moe_decode_t8", dict(T=3, E=8, H=1024, I=512, top_k=2)),
+@pytest.mark.parametrize("name,override,fused", [
+    ("ternary_moe_decode_t1", {}, False),
+    ("ternary_moe_decode_t1", {}, True),
+    ("grid1_moe_decode_t8", {}, False),
+    ("grid1_moe_decode_t8", {}, True),
+    ("ternary_moe_decode_t64_zipf", {}, False),
+    ("ternary_moe_decode_t1", dict(T=4, E=16, H=768, I=256, top_k=4), False),
+    ("ternary_moe_decode_t1", dict(T=4, E=16, H=768, I=256, top_k=4), True),
+    ("grid1_moe_decode_t8", dict(T=3, E=8, H=1024, I=512, top_k=2), False),
+    ("grid1_moe_decode_t8", dict(T=16, E=256, H=1024, I=256, top_k=16), True),
 ])
-def test_decode_layer(name, override):
-    say("decode layer", name, override)
-    inp, gpu = _run_layer(name, **override)
+def test_decode_layer(name, override, fused):
+    say("decode layer", name, override, "fused" if fused else "separate")
+    inp, gpu = _run_layer(name, fused, **override)
     _check_layer(inp, gpu)
+
+
+def _prep_case(T, E, H, k, logits=None, seed=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, :32] = 0.0                              # an all-zero q8 block
+    if logits is None:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+    xd_, ld = to_dev(x), to_dev(logits)
+    sep = {}
+    sep["xq"], sep["xd"] = pq.quantize_act_q8(xd_)
+    sep["ids"], sep["w"] = pq.moe_route_topk(ld, k)
+    g = pq.group_tokens_by_expert(sep["ids"], E)
+    fz = pq.GroupBuffers.empty(T, k, E, dev())
+    f = {"xq": torch.empty((T, H), dtype=torch.int8, device=dev()),
+         "xd": torch.empty((T, H // 32), dtype=torch.float32, device=dev()),
+         "ids": torch.empty((T, k), dtype=torch.int32, device=dev()),
+         "w": torch.empty((T, k), dtype=torch.float32, device=dev())}
+    y = torch.full((T, H), 7.0, device=dev())
+    pq.decode_prep(xd_, ld, k, f["xq"], f["xd"], f["ids"], f["w"], fz, y)
+    torch.cuda.synchronize()
+    for key in ("xq", "xd", "ids", "w"):
+        assert_equal(to_host(f[key]), to_host(sep[key]), "prep " + key)
+    n = int(to_host(g.n_active)[0])
+    assert int(to_host(fz.n_active)[0]) == n
+    assert_equal(to_host(fz.expert_offsets), to_host(g.expert_offsets), "prep offsets")
+    assert_equal(to_host(fz.sorted_assign)[:T * k], to_host(g.sorted_assign)[:T * k], "prep sorted")
+    assert_equal(to_host(fz.active_experts)[:n], to_host(g.active_experts)[:n], "prep active")
+    assert not to_host(y).any(), "y not cleared"
+    # and against the oracle
+    xq, xdq = oracle.quantize_q8(x)
+    assert_equal(to_host(f["xq"]), xq, "prep xq vs oracle")
+    ids, w = oracle.route_topk(logits, k)
+    assert_equal(to_host(f["ids"]), ids, "prep ids vs oracle")
+    assert_tol(to_host(f["w"]), w, w, "prep w vs oracle")
+
+
+@pytest.mark.parametrize("T,E,H,k", [(1, 128, 2048, 8), (8, 256, 4096, 8), (16, 256, 256, 16),
+                                     (4, 1024, 512, 8), (16, 1024, 64, 16), (3, 5, 64, 5),
+                                     (1, 1, 32, 1)])
+def test_decode_prep_matches_separate_calls(T, E, H, k):
+    say("decode prep", T, E, H, k)
+    _prep_case(T, E, H, k, seed=T * 131 + E)
+
+
+def test_decode_prep_ties():
+    say("decode prep ties")
+    logits = np.zeros((6, 64), np.float32)
+    logits[1, 10:20] = 1.0
+    logits[2] = -0.0
+    logits[3, ::2] = 2.5
+    logits[4] = np.arange(64, dtype=np.float32)[::-1]
+    _prep_case(6, 64, 128, 8, logits=logits, seed=3)
+
+
+def test_decode_prep_rejects_large():
+    st = pq.lib().pq_moe_decode_prep(None, None, 17, 64, 8, 2, *([None] * 9), None)
+    assert st == pq.PQ_ERR_UNSUPPORTED
 
 
 def test_combine():
