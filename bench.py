@@ -214,9 +214,11 @@ def main():
     log("step: %.4f ms, %.1f GB/s packed, %.0f tokens/s" % (ms_step, value, tokens_s))
 
     # ---- dominant kernel: fused gate/up.  Every layer input gets its own
-    # routing buffers; the R launches (one per layer, cycling) are captured in
-    # one HIP graph like the steps, replayed once to warm up, then timed
-    # between two HIP events on the launch stream.
+    # routing buffers; R launches (one per layer, cycling) are captured in one
+    # HIP graph like the steps, replayed once to warm up, then timed between
+    # two HIP events on the launch stream.  Back to back, a long MFMA-bound
+    # launch runs at a lower sustained clock than between the lighter kernels
+    # of a step (see the profile summaries).
     R = min(args.kernel_launches, 4 * L) if args.kernel_launches > 0 else 0
     states = []
     for l in range(L):
