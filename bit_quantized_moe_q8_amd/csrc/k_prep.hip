@@ -283,22 +283,34 @@ __global__ __launch_bounds__(kPrepThreads) void k_decode_prep(
     __shared__ float s_val[16][16];
     __shared__ int s_idx[16][16];
     __shared__ int s_ids[kPrepMaxAssign];
-    __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_tot[kPrepWaves];
-    __shared__ int s_carry[2];
+    __shared__ int s_carry;
     const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int TE = T * E;
+    const bool rank_path = TE <= kPrepThreads;
 
-    // q8 of x [T][H]
-    // (eight loads in flight per thread before any is used: one workgroup
-    // cannot hide a load round trip per pass otherwise)
+    // Every load first: this thread's logit (rank path) and its first batch
+    // of activations, so the two round trips overlap.
+    const float lv = (rank_path && tid < TE) ? logits[tid] : 0.0f;
     const int64_t n_blocks = static_cast<int64_t>(T) * H / 32;
     constexpr int kQ8Batch = 8;
-    for (int64_t base = 0; base < n_blocks * 8; base += kQ8Batch * kPrepThreads) {
-        float4 v[kQ8Batch];
+    float4 v[kQ8Batch];
 #pragma unroll
-        for (int u = 0; u < kQ8Batch; ++u) {
-            const int64_t t = base + u * kPrepThreads + tid;
-            v[u] = (t >> 3) < n_blocks ? reinterpret_cast<const float4*>(x)[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < kQ8Batch; ++u) {
+        const int64_t t = u * kPrepThreads + tid;
+        v[u] = (t >> 3) < n_blocks ? reinterpret_cast<const float4*>(x)[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (rank_path && tid < TE) s_key[tid] = route_key(lv == 0.0f ? 0.0f : lv, tid % E);
+
+    // q8 of x [T][H], eight loads in flight per thread per batch
+    for (int64_t base = 0; base < n_blocks * 8; base += kQ8Batch * kPrepThreads) {
+        if (base > 0) {
+#pragma unroll
+            for (int u = 0; u < kQ8Batch; ++u) {
+                const int64_t t = base + u * kPrepThreads + tid;
+                v[u] = (t >> 3) < n_blocks ? reinterpret_cast<const float4*>(x)[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kQ8Batch; ++u) q8_lane_v(v[u], base + u * kPrepThreads + tid, n_blocks, xq, xd);
@@ -306,18 +318,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_decode_prep(
 
     // top-k per token over the same 64-bit keys as the separate router (value
     // bits, then the complemented expert id), so the selection and its order
-    // are identical.  Up to kPrepThreads keys in all: one thread per key
-    // counts the larger keys of its token (its rank).  More: one wave per
-    // token, k rounds of a wave-wide maximum.
-    for (int i = tid; i < E; i += kPrepThreads) s_cnt[i] = 0;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int TE = T * E;
-    if (TE <= kPrepThreads) {
-        if (tid < TE) {
-            float v = logits[tid];
-            if (v == 0.0f) v = 0.0f;
-            s_key[tid] = route_key(v, tid % E);
-        }
+    // are identical.  Up to one key per thread: each thread counts the larger
+    // keys of its token (its rank).  More: one wave per token, k rounds of a
+    // wave-wide maximum.
+    if (rank_path) {
         __syncthreads();
         if (tid < TE) {
             const int t = tid / E;
@@ -327,37 +331,39 @@ __global__ __launch_bounds__(kPrepThreads) void k_decode_prep(
 #pragma unroll 8
             for (int j = 0; j < E; ++j) rank += (row[j] > me) ? 1 : 0;
             if (rank < k) {
-                s_val[t][rank] = logits[tid];
+                s_val[t][rank] = lv;
                 s_idx[t][rank] = tid % E;
             }
         }
-    } else for (int t = wave; t < T; t += kPrepWaves) {
-        const float* l = logits + static_cast<int64_t>(t) * E;
-        uint64_t kk[kMaxExperts / kWave];
+    } else {
+        for (int t = wave; t < T; t += kPrepWaves) {
+            const float* l = logits + static_cast<int64_t>(t) * E;
+            uint64_t kk[kMaxExperts / kWave];
 #pragma unroll
-        for (int i = 0; i < kMaxExperts / kWave; ++i) {
-            const int e = lane + kWave * i;
-            float v = e < E ? l[e] : 0.0f;
-            if (v == 0.0f) v = 0.0f;
-            kk[i] = e < E ? route_key(v, e) : 0ull;   // real keys are never 0
-        }
-        for (int r = 0; r < k; ++r) {
-            uint64_t mx = 0;
-#pragma unroll
-            for (int i = 0; i < kMaxExperts / kWave; ++i) mx = kk[i] > mx ? kk[i] : mx;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx >> 32), off))) << 32) |
-                                   static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx & 0xffffffffu), off));
-                mx = o > mx ? o : mx;
+            for (int i = 0; i < kMaxExperts / kWave; ++i) {
+                const int e = lane + kWave * i;
+                float lvv = e < E ? l[e] : 0.0f;
+                if (lvv == 0.0f) lvv = 0.0f;
+                kk[i] = e < E ? route_key(lvv, e) : 0ull;   // real keys are never 0
             }
+            for (int r = 0; r < k; ++r) {
+                uint64_t mx = 0;
 #pragma unroll
-            for (int i = 0; i < kMaxExperts / kWave; ++i)
-                if (kk[i] == mx) kk[i] = 0ull;
-            if (lane == 0) {
-                const int e = static_cast<int>(~static_cast<uint32_t>(mx));
-                s_idx[t][r] = e;
-                s_val[t][r] = l[e];
+                for (int i = 0; i < kMaxExperts / kWave; ++i) mx = kk[i] > mx ? kk[i] : mx;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx >> 32), off))) << 32) |
+                                       static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx & 0xffffffffu), off));
+                    mx = o > mx ? o : mx;
+                }
+#pragma unroll
+                for (int i = 0; i < kMaxExperts / kWave; ++i)
+                    if (kk[i] == mx) kk[i] = 0ull;
+                if (lane == 0) {
+                    const int e = static_cast<int>(~static_cast<uint32_t>(mx));
+                    s_idx[t][r] = e;
+                    s_val[t][r] = l[e];
+                }
             }
         }
     }
@@ -368,32 +374,31 @@ __global__ __launch_bounds__(kPrepThreads) void k_decode_prep(
     }
     __syncthreads();
 
-    // grouping: counts, exclusive scans over the experts, stable positions
+    // grouping: thread e counts its expert's assignments (A <= 256), one
+    // scan gives the row offset (low 16 bits) and the active-list slot (high
+    // 16 bits) together, then thread e lists its assignments in id order
+    // (stable)
     const int A = T * k;
-    for (int a = tid; a < A; a += kPrepThreads) atomicAdd(&s_cnt[s_ids[a]], 1);
-    __syncthreads();
-    const int cnt = tid < E ? s_cnt[tid] : 0;   // E <= kMaxExperts == kPrepThreads
-    const int off = prep_block_exclusive_scan(cnt, s_tot);
-    const int act = prep_block_exclusive_scan(cnt > 0 ? 1 : 0, s_tot);
+    int cnt = 0;
+    if (tid < E)
+        for (int a = 0; a < A; ++a) cnt += (s_ids[a] == tid) ? 1 : 0;
+    const int packed = cnt | ((cnt > 0 ? 1 : 0) << 16);
+    const int ex = prep_block_exclusive_scan(packed, s_tot);   // E <= kPrepThreads
+    const int off = ex & 0xffff, act = ex >> 16;
     if (tid < E) {
         offsets[tid] = off;
-        if (cnt > 0) active[act] = tid;
-        s_cnt[tid] = off;
+        if (cnt > 0) {
+            active[act] = tid;
+            int j = off;
+            for (int a = 0; a < A; ++a)
+                if (s_ids[a] == tid) sorted[j++] = a;
+        }
     }
-    if (tid == kPrepThreads - 1) {
-        s_carry[0] = off + cnt;
-        s_carry[1] = act + (cnt > 0 ? 1 : 0);
-    }
+    if (tid == kPrepThreads - 1) s_carry = ex + packed;
     __syncthreads();
     if (tid == 0) {
-        offsets[E] = s_carry[0];
-        *n_active = s_carry[1];
-    }
-    for (int a = tid; a < A; a += kPrepThreads) {
-        const int e = s_ids[a];
-        int before = 0;
-        for (int b = 0; b < a; ++b) before += (s_ids[b] == e) ? 1 : 0;
-        sorted[s_cnt[e] + before] = a;
+        offsets[E] = s_carry & 0xffff;
+        *n_active = s_carry >> 16;
     }
 
     if (y_zero) {
