@@ -17,13 +17,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpq.so")
 
-PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE, PQ_ERR_ALIGN, PQ_ERR_UNSUPPORTED, PQ_ERR_HIP = range(6)
+PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE, PQ_ERR_ALIGN, PQ_ERR_UNSUPPORTED, PQ_ERR_HIP, PQ_ERR_SELFTEST = range(7)
 PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 3
 
 EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
     "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_gemm_dequant_tile",
-    "pq_moe_combine", "pq_status_str", "pq_abi_version",
+    "pq_moe_combine", "pq_validate_ternary", "pq_selftest", "pq_status_str", "pq_abi_version",
 )
 
 
@@ -76,6 +76,8 @@ def _load():
                                      ctypes.POINTER(Groups), p, i32, i32, p,
                                      ctypes.POINTER(Debug), p],
         "pq_moe_combine": [p, p, i32, i32, i32, p, p],
+        "pq_validate_ternary": [ctypes.POINTER(TernaryW), p, p],
+        "pq_selftest": [p],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -330,3 +332,18 @@ def moe_combine(out_assign: torch.Tensor, topk_w: torch.Tensor, top_k: int, y: t
         y = torch.empty((T, rows), dtype=torch.float32, device=out_assign.device)
     _check("pq_moe_combine", _lib.pq_moe_combine(_ptr(out_assign), _ptr(topk_w), T, top_k, rows, _ptr(y), _stream()))
     return y
+
+
+def validate_ternary(w: "TernaryWeights", n_bad: torch.Tensor = None) -> torch.Tensor:
+    """pq_validate_ternary: device int32 [1] holding the number of code-3 fields in w.qs."""
+    if n_bad is None:
+        n_bad = torch.empty(1, dtype=torch.int32, device=w.qs.device)
+    _dt(n_bad, torch.int32)
+    cw = w.cstruct()
+    _check("pq_validate_ternary", _lib.pq_validate_ternary(ctypes.byref(cw), _ptr(n_bad), _stream()))
+    return n_bad
+
+
+def selftest() -> int:
+    """pq_selftest on the current stream; returns the status code (PQ_OK on success)."""
+    return int(_lib.pq_selftest(_stream()))

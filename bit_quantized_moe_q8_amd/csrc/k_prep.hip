@@ -423,6 +423,43 @@ bool decode_prep_supported(int n_tokens, int n_experts, int top_k) {
 }
 
 // ---------------------------------------------------------------------------
+// Load-time validation of a ternary plane: codes equal to 3 (a 2-bit field
+// with both bits set) counted over the whole plane by one workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_validate_ternary(const uint8_t* __restrict__ qs,
+                                                           int64_t n_bytes, int32_t* __restrict__ n_bad) {
+    __shared__ long long s_part[16];
+    const int tid = threadIdx.x;
+    long long cnt = 0;
+    const int64_t n16 = n_bytes / 16;
+    const uint4* q4 = reinterpret_cast<const uint4*>(qs);
+    for (int64_t i = tid; i < n16; i += 1024) {
+        const uint4 v = q4[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt += __popc(w[j] & (w[j] >> 1) & 0x55555555u);
+    }
+    for (int64_t i = n16 * 16 + tid; i < n_bytes; i += 1024) {
+        const uint32_t b = qs[i];
+        cnt += __popc(b & (b >> 1) & 0x55u);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if ((tid & 63) == 0) s_part[tid >> 6] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        long long tot = 0;
+        for (int i = 0; i < 16; ++i) tot += s_part[i];
+        *n_bad = tot > 0x7fffffffLL ? 0x7fffffff : static_cast<int32_t>(tot);
+    }
+}
+
+hipError_t launch_validate_ternary(const uint8_t* qs, int64_t n_bytes, int32_t* n_bad, hipStream_t s) {
+    hipLaunchKernelGGL(k_validate_ternary, dim3(1), dim3(1024), 0, s, qs, n_bytes, n_bad);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Weighted combine in slot order: y[t][n] = sum_j w[t][j] * out[t*k+j][n].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ out,

@@ -127,6 +127,7 @@ const char* pq_status_str(pq_status s) {
         case PQ_ERR_ALIGN: return "misaligned pointer";
         case PQ_ERR_UNSUPPORTED: return "no kernel for these (valid) arguments";
         case PQ_ERR_HIP: return "HIP runtime or launch failure";
+        case PQ_ERR_SELFTEST: return "self test: a known answer did not come out";
     }
     return "unknown status";
 }
@@ -346,6 +347,17 @@ pq_status pq_moe_combine(const float* out_assign, const float* topk_w, int32_t n
         if (!aligned(out_assign, 4) || !aligned(topk_w, 4) || !aligned(y, 4)) return PQ_ERR_ALIGN;
         return from_hip(
             pqk::launch_combine(out_assign, topk_w, n_tokens, top_k, rows, y, as_stream(stream)));
+    });
+}
+
+pq_status pq_validate_ternary(const pq_ternary_w* w, int32_t* n_bad, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->qs || !n_bad) return PQ_ERR_NULL;
+        if (w->n_experts < 1 || w->rows < 1 || w->cols < 256 || w->cols % 256 != 0)
+            return PQ_ERR_SHAPE;
+        if (!aligned(w->qs, 16) || !aligned(n_bad, 4)) return PQ_ERR_ALIGN;
+        const int64_t n_bytes = int64_t(w->n_experts) * w->rows * (w->cols / 4);
+        return from_hip(pqk::launch_validate_ternary(w->qs, n_bytes, n_bad, as_stream(stream)));
     });
 }
 

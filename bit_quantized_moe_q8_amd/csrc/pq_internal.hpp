@@ -29,6 +29,9 @@ hipError_t launch_decode_prep(const float* x, const float* logits, int n_tokens,
                               int32_t* n_active, float* y_zero, hipStream_t s);
 bool decode_prep_supported(int n_tokens, int n_experts, int top_k);
 
+// Count of 2-bit codes equal to 3 in n_bytes of ternary qs (one workgroup).
+hipError_t launch_validate_ternary(const uint8_t* qs, int64_t n_bytes, int32_t* n_bad, hipStream_t s);
+
 hipError_t launch_combine(const float* out, const float* w, int n_tokens, int top_k, int rows,
                           float* y, hipStream_t s);
 

@@ -69,7 +69,8 @@ typedef enum pq_status {
     PQ_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
     PQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
     PQ_ERR_UNSUPPORTED = 4, /* valid arguments this build has no kernel for */
-    PQ_ERR_HIP = 5          /* a HIP call or kernel launch failed */
+    PQ_ERR_HIP = 5,         /* a HIP call or kernel launch failed */
+    PQ_ERR_SELFTEST = 6     /* pq_selftest: a known answer did not come out */
 } pq_status;
 
 enum {
@@ -245,6 +246,27 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w *w, const pq_grid1_w *w_up,
  */
 pq_status pq_moe_combine(const float *out_assign, const float *topk_w, int32_t n_tokens,
                          int32_t top_k, int32_t rows, float *y, pq_stream stream);
+
+/*
+ * Load-time check of a ternary tensor: *n_bad (a device int32) receives the
+ * number of 2-bit codes equal to 3 in w->qs (an invalid code: the format has
+ * 0 -> 0, 1 -> +1, 2 -> -1 only, and the kernels' output on code 3 is
+ * unspecified).  One workgroup streams the whole plane (meant for load time,
+ * not the hot path); qs 16-byte aligned.
+ */
+pq_status pq_validate_ternary(const pq_ternary_w *w, int32_t *n_bad, pq_stream stream);
+
+/*
+ * Known-answer self test of every kernel on tiny inputs whose results follow
+ * in closed form: q8 blocks with max|x| = 127 (scale exactly 1), routing of
+ * increasing logits, grouping of a fixed id list, ternary and grid1 mat-vecs
+ * and the prefill GEMM with all-(+1) weights and unit scales (each output is
+ * the exact sum of its activations), the fused prep and combine.  Unlike
+ * every other entry point it allocates device memory and synchronizes
+ * `stream`; not for the hot path.  PQ_OK, PQ_ERR_SELFTEST on a wrong answer,
+ * PQ_ERR_HIP on a runtime failure.
+ */
+pq_status pq_selftest(pq_stream stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *pq_status_str(pq_status status);

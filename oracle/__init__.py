@@ -142,6 +142,19 @@ def unpack_ternary(qs: np.ndarray, k: int) -> np.ndarray:
     return w
 
 
+def count_invalid_ternary(qs: np.ndarray, k: int) -> int:
+    """Number of code-3 fields in ternary planes (rows of k weights; k/4 bytes
+    per row).  The format defines codes 0, 1, 2 only (ternary format of the
+    Parakon Runtime README, "How it works")."""
+    qs = _c(qs, np.uint8)
+    n = qs.size // (k // 4)
+    w = np.empty((n, k), np.int8)
+    bad = lib().or_unpack_ternary(_p(qs), n, k, _p(w))
+    if bad < 0:
+        raise OracleError("or_unpack_ternary failed (%d)" % bad)
+    return int(bad)
+
+
 def unpack_grid1(qs: np.ndarray, qh: np.ndarray, grid: np.ndarray, k: int) -> np.ndarray:
     qs = _c(qs, np.uint8)
     qh = _c(qh, np.uint16)

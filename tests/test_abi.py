@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 def test_abi_version_and_status_strings(L):
     import bit_quantized_moe_q8_amd as pq
     assert pq.abi_version() == 1
-    for s in range(6):
+    for s in range(7):
         assert pq.status_str(s)
     assert pq.status_str(0) == "ok"
 
@@ -122,3 +122,16 @@ def test_combine_validation(L):
     assert f(A16, A16, 2, 0, 64, A16, S) == pq.PQ_ERR_SHAPE
     assert f(None, A16, 2, 2, 64, A16, S) == pq.PQ_ERR_NULL
     assert f(A16, A16, 2, 2, 64, A1, S) == pq.PQ_ERR_ALIGN
+
+
+def test_validate_ternary_validation(L):
+    import bit_quantized_moe_q8_amd as pq
+    f = L.pq_validate_ternary
+    b = ctypes.byref
+    assert f(None, A16, S) == pq.PQ_ERR_NULL
+    assert f(b(pq.TernaryW(A16, A16, 8, 64, 1024)), None, S) == pq.PQ_ERR_NULL
+    assert f(b(pq.TernaryW(None, A16, 8, 64, 1024)), A16, S) == pq.PQ_ERR_NULL
+    assert f(b(pq.TernaryW(A16, A16, 8, 64, 1000)), A16, S) == pq.PQ_ERR_SHAPE
+    assert f(b(pq.TernaryW(A16, A16, 0, 64, 1024)), A16, S) == pq.PQ_ERR_SHAPE
+    assert f(b(pq.TernaryW(A1, A16, 8, 64, 1024)), A16, S) == pq.PQ_ERR_ALIGN
+    assert f(b(pq.TernaryW(A16, A16, 8, 64, 1024)), A1, S) == pq.PQ_ERR_ALIGN

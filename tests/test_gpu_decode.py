@@ -367,3 +367,30 @@ def test_combine():
     y = pq.moe_combine(to_dev(out), to_dev(w), 3)
     y_ref, ty = oracle.combine(out, w, 3)
     assert_tol(to_host(y), y_ref, ty, "y")
+
+
+# ------------------------------------------------------- load-time helpers
+
+@pytest.mark.parametrize("E,N,K,n_plant,seed", [(4, 96, 512, 0, 1), (4, 96, 512, 37, 2),
+                                                (1, 1, 256, 5, 3), (3, 65, 1280, 1000, 4)])
+def test_validate_ternary_counts(E, N, K, n_plant, seed):
+    say("validate ternary", E, N, K, n_plant, seed)
+    planes = wl.stack_experts("ternary", seed, "w", E, N, K)
+    qs = planes["qs"].copy()
+    rng = np.random.default_rng(seed)
+    flat = qs.reshape(-1)
+    pos = rng.integers(0, flat.size, size=n_plant)
+    field = rng.integers(0, 4, size=n_plant)
+    for p_, f_ in zip(pos, field):   # set one 2-bit field of the byte to 3
+        flat[p_] |= np.uint8(3 << (2 * int(f_)))
+    want = oracle.count_invalid_ternary(qs.reshape(E * N, K // 4), K)
+    assert (want > 0) == (n_plant > 0)
+    w = pq.TernaryWeights(to_dev(qs), to_dev(planes["d"]))
+    n_bad = pq.validate_ternary(w)
+    assert int(to_host(n_bad)[0]) == want
+
+
+def test_selftest_known_answers():
+    say("selftest")
+    st = pq.selftest()
+    assert st == pq.PQ_OK, pq.status_str(st)

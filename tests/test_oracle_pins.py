@@ -141,6 +141,17 @@ def test_ternary_all_81_valid_bytes_exhaustive():
         assert list(w[0, :4]) == [{0: 0, 1: 1, 2: -1}[f] for f in fields]
 
 
+def test_ternary_invalid_count_brute_force():
+    # per byte: the number of its four 2-bit fields that equal 3, summed
+    rng = np.random.default_rng(17)
+    qs = rng.integers(0, 256, size=(3, 64), dtype=np.uint8)
+    want = sum(((int(b) >> (2 * j)) & 3) == 3 for b in qs.ravel() for j in range(4))
+    assert oracle.count_invalid_ternary(qs, 256) == want
+    assert oracle.count_invalid_ternary(np.full((2, 64), 0xFF, np.uint8), 256) == 512
+    assert oracle.count_invalid_ternary(np.full((2, 64), 0x0F, np.uint8), 256) == 256
+    assert oracle.count_invalid_ternary(wl.ternary_expert(3, "w", 0, 8, 256)[0], 256) == 0
+
+
 def test_ternary_unpack_vs_numpy_codes():
     qs, _ = wl.ternary_expert(3, "w", 0, 64, 1024)
     w = oracle.unpack_ternary(qs, 1024)
