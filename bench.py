@@ -231,11 +231,18 @@ def main():
         states.append(st)
     torch.cuda.synchronize()
 
+    decode1 = (not prefill) and layer.decode1
+
     def dominant(i):
         l = i % L
         layer.use_state(states[l])
         if prefill:
             layer.gate_up(xs[l], layers[l]["gate"], layers[l]["up"])
+        elif decode1:
+            # one token: the gate/up launch that routes and quantizes itself
+            st = states[l]
+            pq.moe_decode1_gate_up(layers[l]["gate"], layers[l]["up"], xs[l], lg[l], k, st["ids"],
+                                   st["w"], st["groups"], layer.hq, layer.hd, layer.y)
         else:
             layer.gate_up(layers[l]["gate"], layers[l]["up"])
 
@@ -261,7 +268,8 @@ def main():
         torch.cuda.synchronize()
         kms = [k0.elapsed_time(k1) / R] * R
     roofline = None
-    srcs = ["k_gemm.hip" if prefill else "k_matvec.hip", "pq_device.hpp", "pq_internal.hpp"]
+    kfile = "k_gemm.hip" if prefill else ("k_matvec1.hip" if decode1 else "k_matvec.hip")
+    srcs = [kfile, "pq_device.hpp", "pq_internal.hpp"]
     traffic = measured_traffic(args.workload, srcs)
     if R:
         avg_ms = sum(kms) / R
@@ -276,7 +284,9 @@ def main():
                         "avg_launch_us": round(avg_ms * 1e3, 3), "flop_per_launch": flops}
         else:
             ach = avg_bytes / (avg_ms * 1e-3) / 1e9
-            roofline = {"bound": "hbm", "kernel": "k_matvec (gate/up, SwiGLU+q8 epilogue)",
+            kname = ("k_matvec_tok1 (one token: routing, q8, gate/up, SwiGLU+q8 epilogue)" if decode1
+                     else "k_matvec (gate/up, SwiGLU+q8 epilogue)")
+            roofline = {"bound": "hbm", "kernel": kname,
                         "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                         "avg_launch_us": round(avg_ms * 1e3, 3),

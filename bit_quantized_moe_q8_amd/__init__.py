@@ -23,7 +23,8 @@ PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 
 EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
     "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_gemm_dequant_tile",
-    "pq_moe_combine", "pq_validate_ternary", "pq_selftest", "pq_status_str", "pq_abi_version",
+    "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1", "pq_validate_ternary",
+    "pq_selftest", "pq_status_str", "pq_abi_version",
 )
 
 
@@ -76,6 +77,10 @@ def _load():
                                      ctypes.POINTER(Groups), p, i32, i32, p,
                                      ctypes.POINTER(Debug), p],
         "pq_moe_combine": [p, p, i32, i32, i32, p, p],
+        "pq_moe_decode1_gate_up_ternary": [p, p, i32, i32, ctypes.POINTER(TernaryW),
+                                           ctypes.POINTER(TernaryW)] + [p] * 10,
+        "pq_moe_decode1_gate_up_grid1": [p, p, i32, i32, ctypes.POINTER(Grid1W),
+                                         ctypes.POINTER(Grid1W)] + [p] * 10,
         "pq_validate_ternary": [ctypes.POINTER(TernaryW), p, p],
         "pq_selftest": [p],
     }
@@ -347,3 +352,21 @@ def validate_ternary(w: "TernaryWeights", n_bad: torch.Tensor = None) -> torch.T
 def selftest() -> int:
     """pq_selftest on the current stream; returns the status code (PQ_OK on success)."""
     return int(_lib.pq_selftest(_stream()))
+
+
+def moe_decode1_gate_up(gate, up, x: torch.Tensor, logits: torch.Tensor, top_k: int, ids, w, groups,
+                        hq, hd, y_zero=None):
+    """pq_moe_decode1_gate_up_{ternary,grid1}: one token's routing, q8 and gate/up
+    (SwiGLU + q8) in one launch.  x float32 [1][H], logits float32 [1][E];
+    writes ids int32 [1][k], w float32 [1][k], groups (GroupBuffers), hq int8
+    [k][I], hd float32 [k][I/32], and zeros y_zero float32 [1][H] if given."""
+    _dt(x, torch.float32)
+    _dt(logits, torch.float32)
+    E = logits.shape[-1]
+    fn = "pq_moe_decode1_gate_up_ternary" if isinstance(gate, TernaryWeights) else "pq_moe_decode1_gate_up_grid1"
+    cg, cu = gate.cstruct(), up.cstruct()
+    rc = getattr(_lib, fn)(_ptr(x), _ptr(logits), E, top_k, ctypes.byref(cg), ctypes.byref(cu),
+                           _ptr(ids), _ptr(w), _ptr(groups.expert_offsets), _ptr(groups.sorted_assign),
+                           _ptr(groups.active_experts), _ptr(groups.n_active), _ptr(hq), _ptr(hd),
+                           _ptr(y_zero), _stream())
+    _check(fn, rc)

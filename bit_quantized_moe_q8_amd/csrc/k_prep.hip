@@ -16,17 +16,9 @@ namespace pqk {
 __device__ __forceinline__ void q8_lane_v(float4 v, int64_t t, int64_t n_blocks,
                                           int8_t* __restrict__ xq, float* __restrict__ xd) {
     const int64_t blk = t >> 3;
-    const bool ok = blk < n_blocks;
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = fmaxf(a, __shfl_xor(a, 1));
-    a = fmaxf(a, __shfl_xor(a, 2));
-    a = fmaxf(a, __shfl_xor(a, 4));
-    const float d = a / 127.0f;
-    if (!ok) return;
-    const uint32_t q = (static_cast<uint32_t>(q8_value(v.x, d)) & 0xffu) |
-                       ((static_cast<uint32_t>(q8_value(v.y, d)) & 0xffu) << 8) |
-                       ((static_cast<uint32_t>(q8_value(v.z, d)) & 0xffu) << 16) |
-                       ((static_cast<uint32_t>(q8_value(v.w, d)) & 0xffu) << 24);
+    float d;
+    const uint32_t q = q8_pack4(v, d);
+    if (blk >= n_blocks) return;
     reinterpret_cast<uint32_t*>(xq)[t] = q;
     if ((t & 7) == 0) xd[blk] = d;
 }
@@ -63,29 +55,6 @@ hipError_t launch_quantize_q8(const float* x, int64_t n_blocks, int8_t* xq, floa
 // serial arg-max rounds.  -0.0 is folded to +0.0 first (they compare equal).
 // ---------------------------------------------------------------------------
 constexpr int kRouteMaxExperts = 1024;
-
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
-}
-
-// Softmax over the k selected logits (s_val in rank order), by the lanes of
-// one wave (lane < k holds selection `lane`); writes ids and weights.
-__device__ __forceinline__ void route_softmax_store(const float* s_val, const int* s_idx, int k,
-                                                    int lane, int32_t* __restrict__ ids,
-                                                    float* __restrict__ w) {
-    const bool on = lane < k;
-    const float v = on ? s_val[lane] : 0.0f;
-    const float ex = on ? expf(v - s_val[0]) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if (on) {
-        ids[lane] = s_idx[lane];
-        w[lane] = ex / sum;
-    }
-}
 
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ ids,

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/pq.h"
 #include "pq_internal.hpp"
@@ -111,6 +112,65 @@ pq_status guarded(F&& f) {
     } catch (...) {
         return PQ_ERR_HIP;
     }
+}
+
+// One-token gate/up with its own routing and q8; W is pq_ternary_w or pq_grid1_w.
+template <typename W>
+pq_status decode1_gate_up(pqk::Fmt fmt, const float* x, const float* logits, int32_t n_experts,
+                          int32_t top_k, const W* gate, const W* up, int32_t* topk_ids,
+                          float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                          int32_t* active_experts, int32_t* n_active, int8_t* hq, float* hd,
+                          float* y_zero, pq_stream stream) {
+    if (!x || !logits || !gate || !up || !topk_ids || !topk_w || !expert_offsets || !sorted_assign ||
+        !active_experts || !n_active || !hq || !hd)
+        return PQ_ERR_NULL;
+    const W* ws[2] = {gate, up};
+    for (const W* w : ws) {
+        if (!w->qs || !w->d) return PQ_ERR_NULL;
+        if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+    }
+    const int8_t* grid = nullptr;
+    const uint16_t* qh[2] = {nullptr, nullptr};
+    if constexpr (std::is_same<W, pq_grid1_w>::value) {
+        for (int i = 0; i < 2; ++i) {
+            if (!ws[i]->qh || !ws[i]->grid) return PQ_ERR_NULL;
+            if (!aligned(ws[i]->qh, 8) || !aligned(ws[i]->grid, 16)) return PQ_ERR_ALIGN;
+            qh[i] = ws[i]->qh;
+        }
+        grid = gate->grid;   // used for both, as by the mat-vec
+    }
+    if (n_experts < 1 || n_experts > kMaxExperts) return PQ_ERR_SHAPE;
+    if (top_k < 1 || top_k > kMaxTopK || top_k > n_experts) return PQ_ERR_SHAPE;
+    const int I = gate->rows, H = gate->cols;
+    if (gate->n_experts != n_experts || up->n_experts != n_experts) return PQ_ERR_SHAPE;
+    if (up->rows != I || up->cols != H) return PQ_ERR_SHAPE;
+    if (I < 32 || I % 32 != 0 || H < 256 || H % 256 != 0) return PQ_ERR_SHAPE;
+    if (int64_t(I) * H > (int64_t(1) << 31)) return PQ_ERR_SHAPE;
+    if (!pqk::matvec_supported(fmt, H)) return PQ_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(hd, 4) || !aligned(topk_ids, 4) ||
+        !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_assign, 4) ||
+        !aligned(active_experts, 4) || !aligned(n_active, 4) || (y_zero && !aligned(y_zero, 4)))
+        return PQ_ERR_ALIGN;
+
+    pqk::ExpertArgs a{};
+    a.qs[0] = gate->qs;
+    a.qs[1] = up->qs;
+    a.d[0] = gate->d;
+    a.d[1] = up->d;
+    a.qh[0] = qh[0];
+    a.qh[1] = qh[1];
+    a.grid = grid;
+    a.rows = I;
+    a.cols = H;
+    a.n_experts = n_experts;
+    a.n_tokens = 1;
+    a.top_k = top_k;
+    a.act_by_token = 1;
+    a.out0 = hq;
+    a.out1 = hd;
+    const pqk::RouteArgs ra{x, logits, topk_ids, topk_w, expert_offsets, sorted_assign,
+                            active_experts, n_active, y_zero};
+    return from_hip(pqk::launch_decode1_gate_up(fmt, a, ra, as_stream(stream)));
 }
 
 }  // namespace
@@ -240,6 +300,9 @@ pq_status pq_moe_matvec_ternary(const pq_ternary_w* w, const pq_ternary_w* w_up,
         a.out0 = out0;
         a.out1 = out1;
         fill_debug(a, dbg);
+        if (g->n_tokens == 1 && !dbg)
+            return from_hip(pqk::launch_matvec_tok1(pqk::kTernary, static_cast<pqk::Epi>(epilogue), a,
+                                                    as_stream(stream)));
         return from_hip(pqk::launch_matvec(pqk::kTernary, static_cast<pqk::Epi>(epilogue), a,
                                            as_stream(stream)));
     });
@@ -288,6 +351,9 @@ pq_status pq_moe_matvec_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, const
         a.out0 = out0;
         a.out1 = out1;
         fill_debug(a, dbg);
+        if (g->n_tokens == 1 && !dbg)
+            return from_hip(pqk::launch_matvec_tok1(pqk::kGrid1, static_cast<pqk::Epi>(epilogue), a,
+                                                    as_stream(stream)));
         return from_hip(pqk::launch_matvec(pqk::kGrid1, static_cast<pqk::Epi>(epilogue), a,
                                            as_stream(stream)));
     });
@@ -347,6 +413,32 @@ pq_status pq_moe_combine(const float* out_assign, const float* topk_w, int32_t n
         if (!aligned(out_assign, 4) || !aligned(topk_w, 4) || !aligned(y, 4)) return PQ_ERR_ALIGN;
         return from_hip(
             pqk::launch_combine(out_assign, topk_w, n_tokens, top_k, rows, y, as_stream(stream)));
+    });
+}
+
+pq_status pq_moe_decode1_gate_up_ternary(const float* x, const float* logits, int32_t n_experts,
+                                         int32_t top_k, const pq_ternary_w* gate,
+                                         const pq_ternary_w* up, int32_t* topk_ids, float* topk_w,
+                                         int32_t* expert_offsets, int32_t* sorted_assign,
+                                         int32_t* active_experts, int32_t* n_active, int8_t* hq,
+                                         float* hd, float* y_zero, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        return decode1_gate_up(pqk::kTernary, x, logits, n_experts, top_k, gate, up, topk_ids, topk_w,
+                               expert_offsets, sorted_assign, active_experts, n_active, hq, hd,
+                               y_zero, stream);
+    });
+}
+
+pq_status pq_moe_decode1_gate_up_grid1(const float* x, const float* logits, int32_t n_experts,
+                                       int32_t top_k, const pq_grid1_w* gate, const pq_grid1_w* up,
+                                       int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                       int32_t* sorted_assign, int32_t* active_experts,
+                                       int32_t* n_active, int8_t* hq, float* hd, float* y_zero,
+                                       pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        return decode1_gate_up(pqk::kGrid1, x, logits, n_experts, top_k, gate, up, topk_ids, topk_w,
+                               expert_offsets, sorted_assign, active_experts, n_active, hq, hd,
+                               y_zero, stream);
     });
 }
 

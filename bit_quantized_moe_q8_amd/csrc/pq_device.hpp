@@ -49,6 +49,25 @@ __device__ __forceinline__ int ternary_decode4(uint32_t sel) {
     return static_cast<int>(byte_perm(0u, 0x00FF0100u, sel));
 }
 
+// The same for codes held in bits 2..3 of each byte of `sel` (values 0, 4,
+// 8): selector 0 picks byte 0 of the low word (0x00), 4 byte 0 of the high
+// word (0x01), and 8 replicates bit 7 of byte 1 of the low word (0x80 ->
+// 0xFF), so the field needs no shift.
+__device__ __forceinline__ int ternary_decode4_hi(uint32_t sel) {
+    return static_cast<int>(byte_perm(0x00000001u, 0x00008000u, sel));
+}
+
+// Four ternary int8 weight words from one dword P of 16 two-bit codes: word
+// s holds the codes of fields s of the four bytes (weights 4b+s), as the
+// byte-transposed activations expect.
+__device__ __forceinline__ void ternary_decode16(uint32_t P, int w[4]) {
+    const uint32_t P4 = P >> 4;
+    w[0] = ternary_decode4(P & 0x03030303u);
+    w[1] = ternary_decode4_hi(P & 0x0C0C0C0Cu);
+    w[2] = ternary_decode4(P4 & 0x03030303u);
+    w[3] = ternary_decode4_hi(P4 & 0x0C0C0C0Cu);
+}
+
 // Activation bytes permuted for ternary decoding: given four dwords q[0..3]
 // holding 16 consecutive int8 activations, returns t[s] whose byte b is
 // activation 4b+s, i.e. a 4x4 byte transpose.
@@ -113,6 +132,48 @@ __device__ __forceinline__ int q8_value(float x, float d) {
     float r = roundf(x / d);
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return static_cast<int>(r);
+}
+
+// q8 of a 32-value block held by 8 consecutive lanes, 4 values each (lanes
+// 8g..8g+7 form a group; every lane of the group must call): the block
+// scale d = max|x| / 127 and this lane's four codes round_half_away(x / d),
+// packed little-endian.
+__device__ __forceinline__ uint32_t q8_pack4(float4 v, float& d) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    d = a / 127.0f;
+    return (static_cast<uint32_t>(q8_value(v.x, d)) & 0xffu) |
+           ((static_cast<uint32_t>(q8_value(v.y, d)) & 0xffu) << 8) |
+           ((static_cast<uint32_t>(q8_value(v.z, d)) & 0xffu) << 16) |
+           ((static_cast<uint32_t>(q8_value(v.w, d)) & 0xffu) << 24);
+}
+
+// Routing key of logit v of expert e: the order-preserving bits of v, then
+// the complement of e, so that a larger key is a larger logit or an equal
+// logit with a lower expert id.  -0.0 must be folded to +0.0 by the caller.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
+}
+
+// Softmax over the k selected logits (s_val in rank order), by the lanes of
+// one wave (lane < k holds selection `lane`); writes ids and weights.
+__device__ __forceinline__ void route_softmax_store(const float* s_val, const int* s_idx, int k,
+                                                    int lane, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w) {
+    const bool on = lane < k;
+    const float v = on ? s_val[lane] : 0.0f;
+    const float ex = on ? expf(v - s_val[0]) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (on) {
+        ids[lane] = s_idx[lane];
+        w[lane] = ex / sum;
+    }
 }
 
 }  // namespace pqk

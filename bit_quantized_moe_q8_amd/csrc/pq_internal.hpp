@@ -64,6 +64,27 @@ struct ExpertArgs {
 
 // Decode mat-vec; returns hipErrorInvalidValue when no kernel matches cols.
 hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
+
+// Decode mat-vec at one token (n_tokens == 1): one workgroup per (slot,
+// tile), every weight row of the tile in flight at once.
+hipError_t launch_matvec_tok1(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
+
+// One-token gate/up with its own routing and q8 (see the one-token kernel):
+// reads x [cols] and logits [n_experts]; writes ids, w [top_k], the grouping
+// (offsets [n_experts+1], sorted [top_k], active [top_k], n_active) and
+// zeros y [cols]; hq/hd through a.out0/out1 as the SwiGLU q8 epilogue.
+struct RouteArgs {
+    const float* x;
+    const float* logits;
+    int32_t* ids;
+    float* w;
+    int32_t* offsets;
+    int32_t* sorted;
+    int32_t* active;
+    int32_t* n_active;
+    float* y;
+};
+hipError_t launch_decode1_gate_up(Fmt fmt, const ExpertArgs& a, const RouteArgs& r, hipStream_t s);
 bool matvec_supported(Fmt fmt, int cols);
 
 // Prefill dequant-per-tile GEMM (grid1, bf16 MFMA).

@@ -10,7 +10,9 @@ Decode (Parakon Runtime README, "How it works"):
     For a few tokens the first three are one launch (pq_moe_decode_prep), and
     for a single token the combine is fused into the down mat-vec
     (PQ_EPI_F32_COMBINE; fp32 atomic adds, so the summation order of the
-    top-k terms is not fixed).
+    top-k terms is not fixed).  A single token's whole layer is two launches
+    (pq_moe_decode1_gate_up_*, which routes and quantizes by itself, then
+    the down mat-vec with the fused combine).
 Prefill (same section; dequant-per-tile GEMM for large batches):
     route -> group -> fused gate/up GEMM with SwiGLU epilogue (bf16 h)
     -> down GEMM -> weighted combine.
@@ -21,8 +23,8 @@ import torch
 
 from . import (PQ_EPI_F32, PQ_EPI_F32_COMBINE, PQ_EPI_SWIGLU_BF16, PQ_EPI_SWIGLU_Q8,
                GroupBuffers, Grid1Weights, TernaryWeights, decode_prep, decode_prep_supported,
-               group_tokens_by_expert, moe_combine, moe_gemm_dequant_tile, moe_matvec_grid1,
-               moe_matvec_ternary, moe_route_topk, quantize_act_q8)
+               group_tokens_by_expert, moe_combine, moe_decode1_gate_up, moe_gemm_dequant_tile,
+               moe_matvec_grid1, moe_matvec_ternary, moe_route_topk, quantize_act_q8)
 
 # When the decode layer fuses the prep kernels (tokens x experts up to one
 # key per thread of the fused kernel), and the combine into the down mat-vec
@@ -38,7 +40,8 @@ class DecodeLayer:
     """Buffers and call sequence of one decode MoE FFN layer of fixed shape."""
 
     def __init__(self, fmt: str, n_tokens: int, hidden: int, inter: int, n_experts: int,
-                 top_k: int, device="cuda", fused: bool = None, fused_combine: bool = None):
+                 top_k: int, device="cuda", fused: bool = None, fused_combine: bool = None,
+                 decode1: bool = None):
         self.fmt, self.T, self.H, self.I, self.E, self.k = fmt, n_tokens, hidden, inter, n_experts, top_k
         self.device = device
         if fused is None:
@@ -47,6 +50,9 @@ class DecodeLayer:
         if fused_combine is None:
             fused_combine = n_tokens <= FUSED_COMBINE_MAX_TOKENS
         self.fused_combine = self.fused and bool(fused_combine)
+        if decode1 is None:
+            decode1 = self.fused_combine
+        self.decode1 = bool(decode1) and n_tokens == 1
         A = n_tokens * top_k
         f32, i8 = torch.float32, torch.int8
         self.use_state(self.new_route_state())
@@ -92,6 +98,11 @@ class DecodeLayer:
             moe_combine(self.out, self.w, self.k, self.y)
 
     def __call__(self, x, logits, gate, up, down):
+        if self.decode1:
+            moe_decode1_gate_up(gate, up, x, logits, self.k, self.ids, self.w, self.groups,
+                                self.hq, self.hd, self.y)
+            self.down(down)
+            return self.y
         self.route(x, logits)
         self.gate_up(gate, up)
         self.down(down)

@@ -248,6 +248,40 @@ pq_status pq_moe_combine(const float *out_assign, const float *topk_w, int32_t n
                          int32_t top_k, int32_t rows, float *y, pq_stream stream);
 
 /*
+ * One-token gate/up with its own routing (the fused decode path of the
+ * Parakon Runtime README, "How it works", at batch 1; gate/up fusion with
+ * SiLU: pxq_llama README, "Updates - 2026-07-28").  Every workgroup computes
+ * the top-k routing of `logits` and the q8 of `x` itself, so the launch
+ * waits for no earlier one; then the gate/up mat-vec with the SwiGLU + q8
+ * epilogue.  Outputs equal, bit for bit, those of pq_moe_decode_prep (routing
+ * and grouping; no xq/xd) followed by pq_moe_matvec_*(gate, up,
+ * act_by_token = 1, PQ_EPI_SWIGLU_Q8) on the same inputs:
+ *   topk_ids int32 [top_k], topk_w float [top_k] (rank order);
+ *   expert_offsets [n_experts+1], sorted_assign [top_k], active_experts
+ *   [top_k], n_active [1]: the grouping of those ids, ready for the down
+ *   mat-vec (e.g. pq_moe_matvec_*(down, ..., PQ_EPI_F32_COMBINE));
+ *   hq int8 [top_k][I], hd float [top_k][I/32];
+ *   y_zero (may be NULL): float [H] set to zero for that fused combine.
+ * x float [H] (16-byte aligned), logits float [n_experts], gate and up
+ * [n_experts][I][H] (grid1: gate's codebook serves both, as in the mat-vec
+ * with w_up); H as the mat-vec accepts
+ * for cols, I % 32 == 0; n_experts <= 1024, 1 <= top_k <= min(16,
+ * n_experts).  Inputs finite.
+ */
+pq_status pq_moe_decode1_gate_up_ternary(const float *x, const float *logits, int32_t n_experts,
+                                         int32_t top_k, const pq_ternary_w *gate,
+                                         const pq_ternary_w *up, int32_t *topk_ids, float *topk_w,
+                                         int32_t *expert_offsets, int32_t *sorted_assign,
+                                         int32_t *active_experts, int32_t *n_active, int8_t *hq,
+                                         float *hd, float *y_zero, pq_stream stream);
+pq_status pq_moe_decode1_gate_up_grid1(const float *x, const float *logits, int32_t n_experts,
+                                       int32_t top_k, const pq_grid1_w *gate, const pq_grid1_w *up,
+                                       int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                                       int32_t *sorted_assign, int32_t *active_experts,
+                                       int32_t *n_active, int8_t *hq, float *hd, float *y_zero,
+                                       pq_stream stream);
+
+/*
  * Load-time check of a ternary tensor: *n_bad (a device int32) receives the
  * number of 2-bit codes equal to 3 in w->qs (an invalid code: the format has
  * 0 -> 0, 1 -> +1, 2 -> -1 only, and the kernels' output on code 3 is

@@ -73,6 +73,7 @@ def decode_inputs(name, **override):
 def q8_rows_equal_ignoring_ties(hq_gpu, hq_ref, h_ref, hd_ref):
     """Positions where the free-running chains legitimately differ in q8: where
     the reference value sits within 1e-3 of a rounding boundary of its block."""
-    v = h_ref / np.where(hd_ref == 0, 1, np.repeat(hd_ref, 32, axis=-1))
+    dd = np.repeat(hd_ref, 32, axis=-1)
+    v = h_ref / np.where(dd == 0, 1, dd)
     near = np.abs(np.abs(v) - np.floor(np.abs(v)) - 0.5) < 1e-3
     return (hq_gpu == hq_ref) | near

@@ -135,3 +135,23 @@ def test_validate_ternary_validation(L):
     assert f(b(pq.TernaryW(A16, A16, 0, 64, 1024)), A16, S) == pq.PQ_ERR_SHAPE
     assert f(b(pq.TernaryW(A1, A16, 8, 64, 1024)), A16, S) == pq.PQ_ERR_ALIGN
     assert f(b(pq.TernaryW(A16, A16, 8, 64, 1024)), A1, S) == pq.PQ_ERR_ALIGN
+
+
+def test_decode1_gate_up_validation(L):
+    import bit_quantized_moe_q8_amd as pq
+    b = ctypes.byref
+    tw = pq.TernaryW(A16, A16, 8, 256, 1024)
+    f = L.pq_moe_decode1_gate_up_ternary
+    args = lambda **kw: [kw.get("x", A16), kw.get("lg", A16), kw.get("E", 8), kw.get("k", 2),
+                         b(kw.get("g", tw)), b(kw.get("u", tw))] + [A16] * 8 + [kw.get("y", A16), S]
+    assert f(*args(x=None)) == pq.PQ_ERR_NULL
+    assert f(*args(k=9)) == pq.PQ_ERR_SHAPE                                    # top_k > E
+    assert f(*args(E=7)) == pq.PQ_ERR_SHAPE                                    # E != weights
+    assert f(*args(u=pq.TernaryW(A16, A16, 8, 128, 1024))) == pq.PQ_ERR_SHAPE  # up shape
+    assert f(*args(g=pq.TernaryW(A16, A16, 8, 256, 1024 + 256), u=pq.TernaryW(A16, A16, 8, 256, 1280))) \
+        == pq.PQ_ERR_UNSUPPORTED                                               # cols/64 = 20
+    assert f(*args(x=A1)) == pq.PQ_ERR_ALIGN
+    assert f(*args(y=A1)) == pq.PQ_ERR_ALIGN
+    gw = pq.Grid1W(A16, None, A16, A16, 8, 256, 1024)
+    f2 = L.pq_moe_decode1_gate_up_grid1
+    assert f2(A16, A16, 8, 2, b(gw), b(gw), *([A16] * 8), A16, S) == pq.PQ_ERR_NULL

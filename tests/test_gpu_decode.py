@@ -18,7 +18,8 @@ import oracle
 from oracle import moe
 import workloads as wl
 
-from gpu_util import (assert_equal, assert_tol, dev, decode_inputs, say, to_dev, to_host)
+from gpu_util import (assert_equal, assert_tol, dev, decode_inputs, q8_rows_equal_ignoring_ties, say,
+                      to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,10 +123,13 @@ def test_group_all_to_one_expert_and_twice_identical():
 
 # ------------------------------------------------------- single mat-vecs
 
-def _single(fmt, E, N, K, T, k, act_by_token, seed, want_dbg=True):
-    """Grouped F32 mat-vec on random routing; compare isums exactly and y within tolerance."""
+def _single(fmt, E, N, K, T, k, act_by_token, seed, want_dbg=True, ids=None):
+    """Grouped F32 mat-vec on random routing; compare isums exactly and y within tolerance.
+    Without debug outputs the production kernels run (at one token: the
+    one-token kernel)."""
     rng = np.random.default_rng(seed)
-    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    if ids is None:
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     planes = wl.stack_experts(fmt, seed, "w", E, N, K)
     grid = wl.codebook(seed) if fmt == "grid1" else None
     n_rows = T if act_by_token else T * k
@@ -188,6 +192,62 @@ def test_matvec_one_expert_many_tokens():
     say("matvec one expert")
     for fmt in ("ternary", "grid1"):
         _single(fmt, 1, 64, 1024, 37, 1, True, seed=7)
+
+
+@pytest.mark.parametrize("fmt,K,k,abt", [
+    ("ternary", 256, 8, True),     # 4 lanes per row
+    ("ternary", 768, 8, False),    # 12 lanes per row (down projection shape)
+    ("ternary", 2048, 8, True),    # 32 lanes per row (gate/up shape)
+    ("ternary", 4096, 2, False),   # 64 lanes per row
+    ("ternary", 512, 1, True),
+    ("grid1", 256, 4, True),       # 2 lanes per row
+    ("grid1", 1536, 8, False),
+    ("grid1", 4096, 8, True),
+])
+def test_matvec_one_token(fmt, K, k, abt):
+    """The one-token production kernel (no debug outputs), ragged row tiles."""
+    say("matvec one token", fmt, K, k, abt)
+    _single(fmt, 16, 72, K, 1, k, abt, seed=K + k, want_dbg=False)
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "grid1"])
+def test_matvec_one_token_repeated_ids(fmt):
+    """One token whose top-k list repeats an expert (fewer active experts than
+    assignments): every epilogue of the one-token kernel against the oracle."""
+    say("matvec one token repeated ids", fmt)
+    E, N, K, k = 8, 256, 512, 5
+    ids = np.array([[5, 5, 2, 7, 5]], np.int32)
+    for abt in (True, False):
+        _single(fmt, E, N, K, 1, k, abt, seed=11, want_dbg=False, ids=ids)
+    grid = wl.codebook(3) if fmt == "grid1" else None
+    gate = wl.stack_experts(fmt, 3, "gate", E, N, K)
+    up = wl.stack_experts(fmt, 3, "up", E, N, K)
+    xq, xd = oracle.quantize_q8(wl.activations_f32(3, 1, K))
+    g = pq.group_tokens_by_expert(to_dev(ids), E)
+    mv = pq.moe_matvec_ternary if fmt == "ternary" else pq.moe_matvec_grid1
+    hq, hd = mv(weights_to_device(fmt, gate, grid), weights_to_device(fmt, up, grid), g,
+                to_dev(xq), to_dev(xd), True, pq.PQ_EPI_SWIGLU_Q8)
+    tok = np.zeros(k, np.int64)
+    g_ref, tg, _ = moe.grouped_matvec_q8(fmt, gate, grid, ids, xq, xd, tok, K, False)
+    u_ref, tu, _ = moe.grouped_matvec_q8(fmt, up, grid, ids, xq, xd, tok, K, False)
+    h_ref = oracle.swiglu(g_ref.astype(np.float32), u_ref.astype(np.float32))
+    hq_ref, hd_ref = oracle.quantize_q8(h_ref.astype(np.float32))
+    hq_g, hd_g = to_host(hq), to_host(hd)
+    assert q8_rows_equal_ignoring_ties(hq_g, hq_ref, h_ref, hd_ref).all()
+    assert_tol(hd_g, hd_ref, hd_ref, "hd", rtol=1e-4)
+    # the repeated assignments (slots 0, 1, 4 of expert 5) are identical
+    assert_equal(hq_g[1], hq_g[0], "repeat hq")
+    assert_equal(hq_g[4], hq_g[0], "repeat hq")
+    # down projection with the fused combine, activation row per assignment
+    down = wl.stack_experts(fmt, 3, "down", E, K, N)
+    w = np.array([[0.4, 0.1, 0.2, 0.2, 0.1]], np.float32)
+    y = torch.zeros((1, K), device=dev())
+    mv(weights_to_device(fmt, down, grid), None, g, hq, hd, False, pq.PQ_EPI_F32_COMBINE,
+       out0=y, out1=to_dev(w))
+    o_ref, to, _ = moe.grouped_matvec_q8(fmt, down, grid, ids, hq_g, hd_g, np.arange(k), N, False)
+    y_ref, ty = oracle.combine(o_ref.astype(np.float32), w, k)
+    ty_d = np.abs(w.astype(np.float64)) @ to
+    assert_tol(to_host(y), y_ref, ty + ty_d, "y")
 
 
 # ----------------------------------------------------------- decode layers
@@ -367,6 +427,77 @@ def test_combine():
     y = pq.moe_combine(to_dev(out), to_dev(w), 3)
     y_ref, ty = oracle.combine(out, w, 3)
     assert_tol(to_host(y), y_ref, ty, "y")
+
+
+# ------------------------------------------- one-token gate/up with routing
+
+@pytest.mark.parametrize("fmt,E,H,I,k,kind", [
+    ("ternary", 128, 2048, 768, 8, "normal"),    # the one-token layer shape
+    ("grid1", 256, 4096, 1536, 8, "uniform"),
+    ("ternary", 16, 256, 96, 4, "normal"),        # smallest rows, ragged q8 pass
+    ("grid1", 8, 1536, 64, 8, "ties"),            # k == E, equal logits
+    ("ternary", 1024, 512, 32, 16, "normal"),     # most experts, top-16
+    ("ternary", 5, 4096, 256, 1, "ties"),
+])
+def test_decode1_gate_up(fmt, E, H, I, k, kind):
+    """The routed one-token gate/up against the oracle, and bit for bit
+    against the staged prep + gate/up mat-vec on the same inputs."""
+    say("decode1 gate/up", fmt, E, H, I, k, kind)
+    seed = E + H + k
+    x = wl.activations_f32(seed, 1, H)
+    if kind == "ties":
+        logits = np.zeros((1, E), np.float32)
+        logits[0, ::2] = 1.5
+        logits[0, 1] = -0.0
+    else:
+        logits = wl.router_logits(seed, 1, E, kind)
+    grid = wl.codebook(seed) if fmt == "grid1" else None
+    gate = wl.stack_experts(fmt, seed, "gate", E, I, H)
+    up = wl.stack_experts(fmt, seed, "up", E, I, H)
+    Wg, Wu = weights_to_device(fmt, gate, grid), weights_to_device(fmt, up, grid)
+    xd_, lg_ = to_dev(x), to_dev(logits)
+    i32 = torch.int32
+    ids = torch.empty((1, k), dtype=i32, device=dev())
+    w = torch.empty((1, k), device=dev())
+    g = pq.GroupBuffers.empty(1, k, E, dev())
+    hq = torch.empty((k, I), dtype=torch.int8, device=dev())
+    hd = torch.empty((k, I // 32), device=dev())
+    y = torch.full((1, H), 7.0, device=dev())
+    pq.moe_decode1_gate_up(Wg, Wu, xd_, lg_, k, ids, w, g, hq, hd, y)
+    # staged path
+    ids2 = torch.empty_like(ids)
+    w2 = torch.empty_like(w)
+    g2 = pq.GroupBuffers.empty(1, k, E, dev())
+    xq2 = torch.empty((1, H), dtype=torch.int8, device=dev())
+    xs2 = torch.empty((1, H // 32), device=dev())
+    pq.decode_prep(xd_, lg_, k, xq2, xs2, ids2, w2, g2)
+    mv = pq.moe_matvec_ternary if fmt == "ternary" else pq.moe_matvec_grid1
+    hq2, hd2 = mv(Wg, Wu, g2, xq2, xs2, True, pq.PQ_EPI_SWIGLU_Q8)
+    torch.cuda.synchronize()
+    na = int(to_host(g.n_active)[0])
+    assert na == k
+    for got, ref, what in ((ids, ids2, "ids"), (w, w2, "w"), (g.expert_offsets, g2.expert_offsets, "offsets"),
+                           (g.sorted_assign[:k], g2.sorted_assign[:k], "sorted"),
+                           (g.active_experts[:k], g2.active_experts[:k], "active"), (hq, hq2, "hq"),
+                           (hd, hd2, "hd")):
+        assert_equal(to_host(got), to_host(ref), what + " vs staged")
+    assert_equal(to_host(y), np.zeros((1, H), np.float32), "y zeroed")
+    # the oracle
+    ids_ref, w_ref = oracle.route_topk(logits, k)
+    assert_equal(to_host(ids), ids_ref, "ids")
+    assert_tol(to_host(w), w_ref, w_ref, "w")
+    off, srt, act = oracle.group(ids_ref, E)
+    assert_equal(to_host(g.expert_offsets), off, "offsets")
+    assert_equal(to_host(g.sorted_assign)[:k], srt, "sorted")
+    assert_equal(to_host(g.active_experts)[:k], act, "active")
+    xq, xs = oracle.quantize_q8(x)
+    tok = np.zeros(k, np.int64)
+    g_ref, _, _ = moe.grouped_matvec_q8(fmt, gate, grid, ids_ref, xq, xs, tok, H, False)
+    u_ref, _, _ = moe.grouped_matvec_q8(fmt, up, grid, ids_ref, xq, xs, tok, H, False)
+    h_ref = oracle.swiglu(g_ref.astype(np.float32), u_ref.astype(np.float32))
+    hq_ref, hd_ref = oracle.quantize_q8(h_ref.astype(np.float32))
+    assert q8_rows_equal_ignoring_ties(to_host(hq), hq_ref, h_ref, hd_ref).all()
+    assert_tol(to_host(hd), hd_ref, hd_ref, "hd", rtol=1e-4)
 
 
 # ------------------------------------------------------- load-time helpers
