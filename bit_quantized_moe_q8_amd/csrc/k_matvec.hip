@@ -116,8 +116,15 @@ constexpr int tall_shift() {
     return ts;
 }
 
+// Waves per SIMD asked of the single-assignment grid1 variants: three
+// (<= 168 VGPRs, a few spilled) measured ~8% faster on the grid1 decode
+// shapes than the two their natural 171 VGPRs allow; four spills too much.
+constexpr int kGrid1WavesPerSimd = 3;
+
 template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG>
-__global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu((FMT == kGrid1 && MT == 1 && !DBG) ? kGrid1WavesPerSimd : 1)))
+void k_matvec(ExpertArgs p) {
     using FI = FmtInfo<FMT>;
     constexpr int LS = RowGeom<LPR>::LS;
     constexpr int RPW = kWave / LS;               // row slots per wave
@@ -334,14 +341,14 @@ __global__ __launch_bounds__(kThreads) void k_matvec(ExpertArgs p) {
                 if constexpr (FMT == kTernary) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
+                        int wdec[4];
+                        ternary_decode16(wv[i], wdec);
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const int wdec = ternary_decode4((wv[i] >> (2 * s)) & 0x03030303u);
+                        for (int s = 0; s < 4; ++s)
 #pragma unroll
                             for (int j = 0; j < MT; ++j)
-                                isum[j][i >> 1] = dot4(wdec, static_cast<int>(act[j][4 * i + s]),
+                                isum[j][i >> 1] = dot4(wdec[s], static_cast<int>(act[j][4 * i + s]),
                                                        isum[j][i >> 1]);
-                        }
                     }
                 } else {
                     const uint32_t hv[2] = {cur.h.x, cur.h.y};
@@ -528,7 +535,9 @@ hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
         case 8: return launch_mt<FMT, 8>(epi, a, s);
         case 12: return launch_mt<FMT, 12>(epi, a, s);
         case 16: return launch_mt<FMT, 16>(epi, a, s);
+        case 24: return launch_mt<FMT, 24>(epi, a, s);
         case 32: return launch_mt<FMT, 32>(epi, a, s);
+        case 48: return launch_mt<FMT, 48>(epi, a, s);
         case 64: return launch_mt<FMT, 64>(epi, a, s);
         default: return hipErrorInvalidValue;
     }
@@ -540,7 +549,7 @@ bool matvec_supported(Fmt fmt, int cols) {
     const int cw = (fmt == kTernary) ? 64 : 128;
     if (cols % 256 != 0) return false;
     switch (cols / cw) {
-        case 2: case 4: case 8: case 12: case 16: case 32: case 64: return true;
+        case 2: case 4: case 8: case 12: case 16: case 24: case 32: case 48: case 64: return true;
         default: return false;
     }
 }

@@ -510,7 +510,9 @@ hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
         case 8: return launch_epi<FMT, 8>(epi, a, s);
         case 12: return launch_epi<FMT, 12>(epi, a, s);
         case 16: return launch_epi<FMT, 16>(epi, a, s);
+        case 24: return launch_epi<FMT, 24>(epi, a, s);
         case 32: return launch_epi<FMT, 32>(epi, a, s);
+        case 48: return launch_epi<FMT, 48>(epi, a, s);
         case 64: return launch_epi<FMT, 64>(epi, a, s);
         default: return hipErrorInvalidValue;
     }
@@ -538,7 +540,9 @@ hipError_t launch_route_fmt(const ExpertArgs& a, const RouteArgs& r, hipStream_t
         case 8: return launch_route_one<FMT, 8>(a, r, s);
         case 12: return launch_route_one<FMT, 12>(a, r, s);
         case 16: return launch_route_one<FMT, 16>(a, r, s);
+        case 24: return launch_route_one<FMT, 24>(a, r, s);
         case 32: return launch_route_one<FMT, 32>(a, r, s);
+        case 48: return launch_route_one<FMT, 48>(a, r, s);
         case 64: return launch_route_one<FMT, 64>(a, r, s);
         default: return hipErrorInvalidValue;
     }

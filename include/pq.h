@@ -203,8 +203,8 @@ pq_status pq_moe_decode_prep(const float *x, const float *logits, int32_t n_toke
  *                     the last bits between runs); out1 = topk_w float
  *                     [n_tokens][top_k] (read only).  Saves the separate
  *                     pq_moe_combine launch at a few tokens.
- * cols % 256 == 0 and cols/64 in {2,4,8,12,16,32,64} (cols 256..4096 for
- * those divisors); rows >= 1.  w->n_experts == g->n_experts.  dbg may be NULL.
+ * cols % 256 == 0 and cols/64 in {4,8,12,16,24,32,48,64} (cols 256..4096);
+ * rows >= 1.  w->n_experts == g->n_experts.  dbg may be NULL.
  */
 pq_status pq_moe_matvec_ternary(const pq_ternary_w *w, const pq_ternary_w *w_up,
                                 const pq_groups *g, const int8_t *xq, const float *xd,
@@ -214,7 +214,7 @@ pq_status pq_moe_matvec_ternary(const pq_ternary_w *w, const pq_ternary_w *w_up,
 /*
  * The same over grid1 weights (1-bit codebook format).  The codebook is staged
  * in LDS once per workgroup.  cols % 256 == 0 and cols/128 in
- * {2,4,8,12,16,32,64}.
+ * {2,4,8,12,16,24,32,48,64} (cols 256..8192).
  */
 pq_status pq_moe_matvec_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
                               const pq_groups *g, const int8_t *xq, const float *xd,
