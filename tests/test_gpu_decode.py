@@ -181,6 +181,10 @@ def test_ternary_matvec_1024_single_matrix():
     ("grid1", 8, 40, 1536, 3, 2, False),
     ("grid1", 8, 64, 1024, 6, 3, True),
     ("grid1", 16, 50, 4096, 9, 4, True),
+    ("ternary", 8, 40, 1536, 3, 2, True),     # 24 chunks per row
+    ("ternary", 4, 33, 3072, 2, 2, False),    # 48 chunks per row
+    ("grid1", 8, 40, 3072, 3, 2, True),       # 24 chunks per row
+    ("grid1", 4, 20, 6144, 2, 2, False),      # 48 chunks per row
 ])
 def test_grouped_matvec(fmt, E, N, K, T, k, abt):
     say("matvec", fmt, E, N, K, T, k, abt)
@@ -203,6 +207,9 @@ def test_matvec_one_expert_many_tokens():
     ("grid1", 256, 4, True),       # 2 lanes per row
     ("grid1", 1536, 8, False),
     ("grid1", 4096, 8, True),
+    ("ternary", 1536, 8, True),    # 24 lanes per row
+    ("grid1", 3072, 4, False),
+    ("grid1", 6144, 2, True),      # 48 lanes per row
 ])
 def test_matvec_one_token(fmt, K, k, abt):
     """The one-token production kernel (no debug outputs), ragged row tiles."""
@@ -438,6 +445,7 @@ def test_combine():
     ("grid1", 8, 1536, 64, 8, "ties"),            # k == E, equal logits
     ("ternary", 1024, 512, 32, 16, "normal"),     # most experts, top-16
     ("ternary", 5, 4096, 256, 1, "ties"),
+    ("ternary", 300, 1536, 64, 6, "normal"),     # rank over 300 keys, 24 lanes per row
 ])
 def test_decode1_gate_up(fmt, E, H, I, k, kind):
     """The routed one-token gate/up against the oracle, and bit for bit
