@@ -22,7 +22,8 @@ PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 
 
 EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
-    "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_gemm_dequant_tile",
+    "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_tile_q8_ternary", "pq_moe_tile_q8_grid1",
+    "pq_moe_gemm_dequant_tile",
     "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1", "pq_validate_ternary",
     "pq_selftest", "pq_status_str", "pq_abi_version",
 )
@@ -73,6 +74,12 @@ def _load():
         "pq_moe_matvec_grid1": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
                                 ctypes.POINTER(Groups), p, p, i32, i32, p, p,
                                 ctypes.POINTER(Debug), p],
+        "pq_moe_tile_q8_ternary": [ctypes.POINTER(TernaryW), ctypes.POINTER(TernaryW),
+                                   ctypes.POINTER(Groups), p, p, i32, i32, p, p,
+                                   ctypes.POINTER(Debug), p],
+        "pq_moe_tile_q8_grid1": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
+                                 ctypes.POINTER(Groups), p, p, i32, i32, p, p,
+                                 ctypes.POINTER(Debug), p],
         "pq_moe_gemm_dequant_tile": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
                                      ctypes.POINTER(Groups), p, i32, i32, p,
                                      ctypes.POINTER(Debug), p],
@@ -306,6 +313,18 @@ def moe_matvec_grid1(w: Grid1Weights, w_up, groups: GroupBuffers, xq, xd, act_by
                      epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
     """pq_moe_matvec_grid1 (see include/pq.h)."""
     return _matvec("pq_moe_matvec_grid1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
+
+
+def moe_tile_q8_ternary(w: TernaryWeights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,
+                        epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
+    """pq_moe_tile_q8_ternary (see include/pq.h)."""
+    return _matvec("pq_moe_tile_q8_ternary", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
+
+
+def moe_tile_q8_grid1(w: Grid1Weights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,
+                      epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
+    """pq_moe_tile_q8_grid1 (see include/pq.h)."""
+    return _matvec("pq_moe_tile_q8_grid1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
 
 
 def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: torch.Tensor,

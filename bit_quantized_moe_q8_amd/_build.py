@@ -12,7 +12,7 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pq_api.cpp", "pq_selftest.cpp", "k_prep.hip", "k_matvec.hip", "k_matvec1.hip", "k_gemm.hip"]
+SOURCES = ["pq_api.cpp", "pq_selftest.cpp", "k_prep.hip", "k_matvec.hip", "k_matvec1.hip", "k_tile_q8.hip", "k_gemm.hip"]
 
 # No fast-math: the q8 rule needs correctly rounded fp32 division.  Packed
 # fp32 VALU forms are disabled for all device code.

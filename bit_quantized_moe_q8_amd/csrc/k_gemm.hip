@@ -64,22 +64,6 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, uint4* lds_wave_bas
     __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_wave_base), 16, 0, 0);
 }
 
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) tmp[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int i = 0; i < wave; ++i) base += tmp[i];
-    __syncthreads();
-    return base + incl - v;
-}
-
 // LDS rings, one K block ahead of the MFMAs: A (activations) 2 slots and the
 // weight group indices 2 slots, both copied global -> LDS (16-byte form
 // only: the narrow forms write one dword per lane).  The slots are separate

@@ -59,6 +59,10 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kTileRows = 32;      // q8 block of the SwiGLU epilogue; tiles are 1, 2 or 4 of these
 constexpr int kMaxTileShift = 2;
 constexpr int kDepth = 4;          // row iterations of weight loads in flight per wave
+#ifndef PQ_HEAVY_MIN
+#define PQ_HEAVY_MIN 8
+#endif
+constexpr int kHeavyMin = PQ_HEAVY_MIN;   // assignments from which an expert goes to the MFMA tile
 
 template <int FMT>
 struct FmtInfo;
@@ -79,24 +83,6 @@ struct WRow {
     uint2 h;      // grid1: the 4 qh words of the chunk
     uint32_t d;   // fp16 scale bits
 };
-
-// Exclusive scan of one int per thread over the workgroup; `tmp` holds one
-// int per wave.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) tmp[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int i = 0; i < wave; ++i) base += tmp[i];
-    __syncthreads();
-    return base + incl - v;
-}
 
 // Rows per workgroup row iteration for LPR chunks per row.
 template <int LPR>
@@ -167,7 +153,9 @@ void k_matvec(ExpertArgs p) {
             int na = 0;
             if (s < n_active) {
                 const int e = p.active[s];
-                na = (p.offsets[e + 1] - p.offsets[e] + MT - 1) / MT;
+                const int cnt = p.offsets[e + 1] - p.offsets[e];
+                // experts left to the int8-MFMA tile kernel get no groups
+                na = (p.heavy_min > 0 && cnt >= p.heavy_min) ? 0 : (cnt + MT - 1) / MT;
             }
             const int ex = block_exclusive_scan(na, s_scan);
             if (s < n_active) s_apre[s] = run + ex;
@@ -517,14 +505,16 @@ hipError_t launch_mt(Epi epi, const ExpertArgs& a, hipStream_t s) {
     // One token: every expert sees one activation row.  Up to one assignment
     // per expert on average: pairs (single rows for grid1, whose codebook
     // decode already holds more registers), passes repeated for the rare
-    // heavier expert.  Otherwise groups of four assignments, spread over workgroups.
+    // heavier expert.  Otherwise pairs of assignments, each its own work item
+    // (measured faster than groups of four or eight on the skewed 64-token
+    // decode: fewer idle dot products for the many one-assignment experts).
     const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
     if (a.n_tokens <= 1) return launch_epi<FMT, LPR, 1, false>(epi, a, s);
 #ifndef PQ_MT_PAIR
 #define PQ_MT_PAIR (FMT == kGrid1 ? 1 : 2)
 #endif
     if (A <= a.n_experts) return launch_epi<FMT, LPR, PQ_MT_PAIR, false>(epi, a, s);
-    return launch_epi<FMT, LPR, 4, true>(epi, a, s);
+    return launch_epi<FMT, LPR, 2, true>(epi, a, s);
 }
 
 template <int FMT>
@@ -555,8 +545,19 @@ bool matvec_supported(Fmt fmt, int cols) {
 }
 
 hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
-    if (fmt == kTernary) return launch_fmt<kTernary>(epi, a, s);
-    return launch_fmt<kGrid1>(epi, a, s);
+    // Per-expert choice by load: with more assignments than experts (the
+    // split grouping) an expert holding at least kHeavyMin of them runs on
+    // the int8-MFMA tile kernel, the rest on the mat-vec.
+    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    ExpertArgs m = a;
+    m.heavy_min = 0;
+    if (a.n_tokens >= kHeavyMin && A > a.n_experts && tile_q8_supported(a.cols)) {
+        m.heavy_min = kHeavyMin;
+        const hipError_t err = launch_tile_q8(fmt, epi, m, s);
+        if (err != hipSuccess) return err;
+    }
+    if (fmt == kTernary) return launch_fmt<kTernary>(epi, m, s);
+    return launch_fmt<kGrid1>(epi, m, s);
 }
 
 }  // namespace pqk

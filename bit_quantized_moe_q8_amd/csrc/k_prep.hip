@@ -115,24 +115,6 @@ constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * 64;
 constexpr int kGroupMaxExperts = 1024;
 
-// Exclusive scan of one int per thread over the kGroupThreads threads of the
-// workgroup (wave scans with shuffles, then the wave totals).
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int i = 0; i < wave; ++i) base += wave_tot[i];
-    __syncthreads();
-    return base + incl - v;
-}
-
 __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ ids, int A,
                                                          int E, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted,

@@ -1,0 +1,399 @@
+// Grouped int8-MFMA tile kernel over packed 1-bit-class expert weights against
+// q8 activations: the arithmetic of the decode mat-vec (per-32 int32 block
+// sums, fp32 scale application) for experts that hold many assignments, as
+// in prefill.  The pages switch large batches from the mat-vec to a tiled
+// kernel on their own (Parakon Runtime README, "How it works"), and add an
+// int8 dot-product prefill tile for cards without fast fp16 products
+// (pxq_llama README, "Updates - 2026-07-19"); this kernel is such a tile on
+// the matrix cores, fed q8 activations so that the block sums stay exact.
+//
+// One v_mfma_i32_16x16x32_i8 covers K = 32, exactly one q8 block: its int32
+// results are the block sums sum_k w[n][k] * xq[t][k] of 16 weight rows x 16
+// assignments, bit-exact for any order of the 32 products.  Then, in fp32,
+//   blk[n][t] += xd[t][b] * isum      (8 blocks of a 256-weight scale block)
+//   tot[n][t] += d[n][B] * blk[n][t]  (once per scale block).
+//
+// Work item: (expert, chunk of up to 32 of its assignments, tile of 64
+// physical weight rows: 32 gate + 32 up rows for the SwiGLU epilogue, else 64
+// rows).  Wave w owns 16 of the 64 rows (the A operand) and both 16-column
+// assignment subtiles (the B operand).  The K loop runs over 256-weight
+// slabs: each lane loads its own weight row's packed slab straight into
+// registers one slab ahead, while the workgroup stages the chunk's q8
+// activations and scales for the next slab into LDS.
+//
+// Operand layouts (lane l: r = l % 16, lane group g = l / 16; A row r and B
+// column r carry the K slots 8g..8g+7; the result rows are 4g..4g+3 of
+// column r):
+//  - ternary: K slot j of lane group g is weight 4j + g of the block's first
+//    16 and slot 4 + j weight 16 + 4j + g, i.e. code field g of each byte of
+//    the block's two code dwords, so the A fragment is two byte lookups
+//    (v_perm_b32) with no byte shuffling, and the activations are staged
+//    byte-transposed to match;
+//  - grid1: lane group g takes group g of the block (8 weights in natural
+//    order): its 11-bit index selects one 8-byte codebook row in LDS, which
+//    is exactly the A fragment.
+//
+// Items are chosen on the device from the grouping (offsets / active): an
+// expert takes part when it holds at least `heavy_min` assignments, so the
+// decode mat-vec can take the others in a launch of its own.
+#include "pq_device.hpp"
+#include "pq_internal.hpp"
+
+namespace pqk {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTok = 32;          // assignments per item: two 16-column subtiles
+constexpr int kSub = 16;
+constexpr int kSlabK = 256;       // weights per slab: one weight-scale block
+constexpr int kSlabBlocks = kSlabK / 32;
+constexpr int kRows = 64;         // physical weight rows per item, 16 per wave
+
+template <int FMT>
+struct TileFmt;
+template <>
+struct TileFmt<kTernary> {
+    static constexpr int kWords = 4;   // 64 bytes of codes per row and slab
+};
+template <>
+struct TileFmt<kGrid1> {
+    static constexpr int kWords = 3;   // 32 bytes of qs, then 16 bytes of qh
+};
+
+template <int FMT, int EPI, bool DBG>
+__global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
+    constexpr int NMAT = (EPI == kEpiSwigluQ8) ? 2 : 1;
+    constexpr int TR = kRows / NMAT;   // output rows per item
+    constexpr int KW = TileFmt<FMT>::kWords;
+
+    // B fragments of a slab, [slot][block][lane group][assignment column]
+    __shared__ uint2 s_x[2][kSlabBlocks][4][kTok];
+    __shared__ float s_xd[2][kSlabBlocks][kTok];
+    __shared__ float s_d[2][kRows];
+    __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : 1];
+    __shared__ float s_gu[NMAT][(NMAT == 2) ? TR : 1][kTok + 1];
+    __shared__ int s_pre[kMaxExperts + 1];   // first chunk number per slot
+    __shared__ int s_scan[kWaves + 1];
+    __shared__ int s_asg[kTok];
+    __shared__ int s_arow[kTok];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int rows = p.rows, cols = p.cols, KB = cols / kSlabK;
+    const int n_active = load_uniform(p.n_active);
+    const int hmin = p.heavy_min > 0 ? p.heavy_min : 1;
+
+    if constexpr (FMT == kGrid1) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.grid);
+        uint4* dst = reinterpret_cast<uint4*>(s_grid);
+        for (int i = tid; i < kGridEntries / 2; i += kThreads) dst[i] = src[i];
+    }
+    // Chunks of up to kTok assignments of the experts that take part,
+    // numbered in slot order.
+    int run = 0;
+    for (int s0 = 0; s0 < n_active; s0 += kThreads) {
+        const int s = s0 + tid;
+        int nc = 0;
+        if (s < n_active) {
+            const int e = p.active[s];
+            const int m = p.offsets[e + 1] - p.offsets[e];
+            nc = m >= hmin ? (m + kTok - 1) / kTok : 0;
+        }
+        const int ex = block_exclusive_scan(nc, s_scan);
+        if (s < n_active) s_pre[s] = run + ex;
+        if (tid == kThreads - 1) s_scan[kWaves] = run + ex + nc;
+        __syncthreads();
+        run = s_scan[kWaves];
+        __syncthreads();
+    }
+    if (tid == 0) s_pre[n_active] = run;
+    __syncthreads();   // codebook and chunk prefix visible
+
+    const int tiles = (rows + TR - 1) / TR;
+    const int n_items = run * tiles;
+    const int64_t qs_row = (FMT == kTernary) ? cols / 4 : cols / 8;   // bytes
+    const int64_t qh_row = cols / 32;                                  // uint16
+    const int64_t d_row = cols / kSlabK;
+    const int n_sub_row = cols / 32;
+
+    // This lane's A row: physical row pr = 16 * wave + r of the item.
+    const int pr_a = 16 * wave + r;
+    const int mat_a = (NMAT == 2) ? (wave >> 1) : 0;   // uniform
+    const int off_a = (NMAT == 2) ? (pr_a & 31) : pr_a;
+
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int c = item / tiles, tile = item % tiles;
+        int lo = 0, hi = n_active - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        const int slot = __builtin_amdgcn_readfirstlane(lo);
+        const int cbeg = (c - __builtin_amdgcn_readfirstlane(s_pre[slot])) * kTok;
+        const int e = load_uniform(p.active + slot);
+        const int beg = load_uniform(p.offsets + e);
+        const int m = load_uniform(p.offsets + e + 1) - beg;
+        const int mcount = min(kTok, m - cbeg);
+        const int jn = (mcount + kSub - 1) / kSub;   // 1 or 2 live column subtiles
+        const int n0 = tile * TR;
+        if (tid < kTok) {
+            // columns past mcount repeat the last assignment and are never stored
+            const int a = p.sorted[beg + cbeg + min(tid, mcount - 1)];
+            s_asg[tid] = a;
+            s_arow[tid] = p.act_by_token ? a / p.top_k : a;
+        }
+        __syncthreads();
+
+        // ---- per-lane weight row (clamped past the end; never stored)
+        const int na = min(n0 + off_a, rows - 1);
+        const uint8_t* qsrow = (mat_a ? p.qs[1] : p.qs[0]) + (static_cast<int64_t>(e) * rows + na) * qs_row;
+        const uint16_t* qhrow = nullptr;
+        if constexpr (FMT == kGrid1)
+            qhrow = (mat_a ? p.qh[1] : p.qh[0]) + (static_cast<int64_t>(e) * rows + na) * qh_row;
+        auto wload = [&](int sb, uint4 (&w)[KW]) {
+            if constexpr (FMT == kTernary) {
+                const uint4* src = reinterpret_cast<const uint4*>(qsrow + 64 * sb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = src[i];
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(qsrow + 32 * sb);
+                w[0] = src[0];
+                w[1] = src[1];
+                w[2] = *reinterpret_cast<const uint4*>(qhrow + 8 * sb);
+            }
+        };
+
+        // ---- staging of a slab: 2 x 16 activation bytes, one block scale
+        // and (first 64 threads) one weight scale per thread
+        uint4 xr[2];
+        float xdr = 0.0f, dr = 0.0f;
+        auto sload = [&](int sb) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int unit = tid + kThreads * k;
+                const int tok = unit >> 4, uu = unit & 15;
+                xr[k] = *reinterpret_cast<const uint4*>(p.xq + static_cast<int64_t>(s_arow[tok]) * cols +
+                                                        sb * kSlabK + uu * 16);
+            }
+            xdr = p.xd[static_cast<int64_t>(s_arow[tid >> 3]) * n_sub_row + sb * kSlabBlocks + (tid & 7)];
+            if (tid < kRows) {
+                const int mr = (NMAT == 2) ? (tid >> 5) : 0;
+                const int nr = min(n0 + ((NMAT == 2) ? (tid & 31) : tid), rows - 1);
+                dr = half_bits_to_float(p.d[mr][(static_cast<int64_t>(e) * rows + nr) * d_row + sb]);
+            }
+        };
+        auto sstore = [&](int sl) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int unit = tid + kThreads * k;
+                const int tok = unit >> 4, uu = unit & 15;
+                const int q = uu >> 1, h = uu & 1;
+                const uint32_t qq[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+                if constexpr (FMT == kTernary) {
+                    // unit h of block q: dword s of its byte transpose is
+                    // the K slots 4h.. of lane group s
+                    uint32_t t[4];
+                    transpose_bytes4(qq, t);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) reinterpret_cast<uint32_t*>(&s_x[sl][q][s][tok])[h] = t[s];
+                } else {
+                    s_x[sl][q][2 * h][tok] = make_uint2(qq[0], qq[1]);
+                    s_x[sl][q][2 * h + 1][tok] = make_uint2(qq[2], qq[3]);
+                }
+            }
+            s_xd[sl][tid & 7][tid >> 3] = xdr;
+            if (tid < kRows) s_d[sl][tid] = dr;
+        };
+
+        float tot[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[j][i] = 0.0f;
+
+        auto compute = [&](int sl, const uint4 (&w)[KW], int sb) {
+            uint32_t wv[4 * KW];
+#pragma unroll
+            for (int i = 0; i < KW; ++i) {
+                wv[4 * i] = w[i].x;
+                wv[4 * i + 1] = w[i].y;
+                wv[4 * i + 2] = w[i].z;
+                wv[4 * i + 3] = w[i].w;
+            }
+            float blk[2][4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) blk[j][i] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kSlabBlocks; ++q) {
+                uint64_t afrag;
+                if constexpr (FMT == kTernary) {
+                    const uint32_t lo = static_cast<uint32_t>(ternary_decode4((wv[2 * q] >> (2 * g)) & 0x03030303u));
+                    const uint32_t hi = static_cast<uint32_t>(ternary_decode4((wv[2 * q + 1] >> (2 * g)) & 0x03030303u));
+                    afrag = (static_cast<uint64_t>(hi) << 32) | lo;
+                } else {
+                    const uint32_t lo8 = (wv[q] >> (8 * g)) & 0xffu;
+                    const uint32_t h16 = wv[8 + (q >> 1)] >> (16 * (q & 1));
+                    const uint32_t hi3 = (h16 >> (3 * g)) & 7u;
+                    const uint2 cb = s_grid[lo8 | (hi3 << 8)];
+                    afrag = (static_cast<uint64_t>(cb.y) << 32) | cb.x;
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (j < jn) {
+                        const uint2 bx = s_x[sl][q][g][kSub * j + r];
+                        const uint64_t bfrag = (static_cast<uint64_t>(bx.y) << 32) | bx.x;
+                        const v4i is = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                            static_cast<long>(afrag), static_cast<long>(bfrag), v4i{0, 0, 0, 0}, 0, 0, 0);
+                        const float xdv = s_xd[sl][q][kSub * j + r];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) blk[j][i] += xdv * static_cast<float>(is[i]);
+                        if constexpr (DBG) {
+                            int32_t* dst = p.dbg_isums[mat_a];
+                            const int col = kSub * j + r;
+                            if (dst && col < mcount) {
+                                const int a = s_asg[col];
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const int pr = 16 * wave + 4 * g + i;
+                                    const int n = n0 + ((NMAT == 2) ? (pr & 31) : pr);
+                                    if (n < rows)
+                                        dst[(static_cast<int64_t>(a) * rows + n) * n_sub_row +
+                                            sb * kSlabBlocks + q] = is[i];
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float dsc = s_d[sl][16 * wave + 4 * g + i];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) tot[j][i] += dsc * blk[j][i];
+            }
+        };
+
+        uint4 wc[KW], wn[KW];
+        wload(0, wc);
+        sload(0);
+        sstore(0);
+        __syncthreads();
+        for (int sb = 0; sb < KB; ++sb) {
+            const int sl = sb & 1;
+            const bool more = sb + 1 < KB;
+            if (more) {
+                wload(sb + 1, wn);
+                sload(sb + 1);
+            }
+            compute(sl, wc, sb);
+            if (more) {
+                sstore(sl ^ 1);
+#pragma unroll
+                for (int i = 0; i < KW; ++i) wc[i] = wn[i];
+            }
+            __syncthreads();
+        }
+
+        // ---- epilogues: lane holds physical rows 16*wave + 4g + i of
+        // columns 16j + r
+        if constexpr (EPI == kEpiSwigluQ8) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_gu[mat_a][16 * (wave & 1) + 4 * g + i][kSub * j + r] = tot[j][i];
+            __syncthreads();
+            // one 32-lane half per assignment column; lane = output row
+            for (int c0 = 0; c0 < kTok; c0 += kThreads / 32) {
+                const int col = c0 + (tid >> 5), i = tid & 31;
+                const float gg = s_gu[0][i][col], uu = s_gu[1][i][col];
+                const float h = gg / (1.0f + expf(-gg)) * uu;
+                const float amax = half_wave_max(fabsf(h));
+                const float dq = amax / 127.0f;
+                if (col < mcount) {
+                    const int a = s_asg[col];
+                    const int64_t o = static_cast<int64_t>(a) * rows + n0 + i;
+                    static_cast<int8_t*>(p.out0)[o] = static_cast<int8_t>(q8_value(h, dq));
+                    if (i == 0)
+                        static_cast<float*>(p.out1)[static_cast<int64_t>(a) * (rows / 32) + n0 / 32] = dq;
+                    if constexpr (DBG) {
+                        if (p.dbg_g) p.dbg_g[o] = gg;
+                        if (p.dbg_u) p.dbg_u[o] = uu;
+                        if (p.dbg_h) p.dbg_h[o] = h;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = kSub * j + r;
+                if (j < jn && col < mcount) {
+                    const int a = s_asg[col];
+                    const float wsel = (EPI == kEpiF32Combine) ? static_cast<const float*>(p.out1)[a] : 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = n0 + 16 * wave + 4 * g + i;
+                        if (n < rows) {
+                            if constexpr (EPI == kEpiF32) {
+                                static_cast<float*>(p.out0)[static_cast<int64_t>(a) * rows + n] = tot[j][i];
+                            } else {
+                                atomicAdd(static_cast<float*>(p.out0) + static_cast<int64_t>(a / p.top_k) * rows + n,
+                                          wsel * tot[j][i]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();   // s_asg, s_arow and the LDS slots are reused by the next item
+    }
+}
+
+template <int FMT, int EPI, bool DBG>
+hipError_t launch_one(const ExpertArgs& a, hipStream_t s) {
+    constexpr int TR = kRows / ((EPI == kEpiSwigluQ8) ? 2 : 1);
+    // Upper bound of the chunks: sum over the taking-part experts of
+    // ceil(m / kTok) <= A / kTok + (number of such experts).
+    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    const int64_t hmin = a.heavy_min > 0 ? a.heavy_min : 1;
+    int64_t heavy = A / hmin;
+    if (heavy > a.n_experts) heavy = a.n_experts;
+    const int64_t chunks = A / kTok + heavy + 1;
+    const int64_t items = chunks * ((a.rows + TR - 1) / TR);
+    const int64_t cap = static_cast<int64_t>(cu_count()) * 4;
+    int64_t grid = items < cap ? items : cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((k_tile_q8<FMT, EPI, DBG>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int EPI>
+hipError_t launch_dbg(const ExpertArgs& a, hipStream_t s) {
+    return a.debug ? launch_one<FMT, EPI, true>(a, s) : launch_one<FMT, EPI, false>(a, s);
+}
+
+template <int FMT>
+hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
+    if (epi == kEpiF32) return launch_dbg<FMT, kEpiF32>(a, s);
+    if (epi == kEpiF32Combine) return launch_dbg<FMT, kEpiF32Combine>(a, s);
+    if (epi == kEpiSwigluQ8) return launch_dbg<FMT, kEpiSwigluQ8>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool tile_q8_supported(int cols) { return cols >= kSlabK && cols % kSlabK == 0; }
+
+hipError_t launch_tile_q8(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
+    if (!tile_q8_supported(a.cols)) return hipErrorInvalidValue;
+    if (fmt == kTernary) return launch_fmt<kTernary>(epi, a, s);
+    return launch_fmt<kGrid1>(epi, a, s);
+}
+
+}  // namespace pqk

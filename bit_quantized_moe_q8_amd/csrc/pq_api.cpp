@@ -173,6 +173,110 @@ pq_status decode1_gate_up(pqk::Fmt fmt, const float* x, const float* logits, int
     return from_hip(pqk::launch_decode1_gate_up(fmt, a, ra, as_stream(stream)));
 }
 
+// Validation and argument set-up shared by the q8 expert entry points (the
+// mat-vec and the int8-MFMA tile); `supported` checks the row length for the
+// kernel family.  *run is false when there is nothing to launch.
+template <typename Supported>
+pq_status ternary_args(const pq_ternary_w* w, const pq_ternary_w* w_up, const pq_groups* g,
+                       const int8_t* xq, const float* xd, int32_t act_by_token, int32_t epilogue,
+                       void* out0, void* out1, const pq_debug* dbg, Supported supported,
+                       pqk::ExpertArgs& a, bool* run) {
+    *run = false;
+    if (!w || !w->qs || !w->d) return PQ_ERR_NULL;
+    pq_status st = check_groups(g);
+    if (st != PQ_OK) return st;
+    if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
+    if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
+        return st;
+    if (epilogue == PQ_EPI_F32_COMBINE && act_by_token) return PQ_ERR_UNSUPPORTED;
+    if (epilogue == PQ_EPI_SWIGLU_Q8) {
+        if (!w_up->qs || !w_up->d) return PQ_ERR_NULL;
+        if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
+            return PQ_ERR_SHAPE;
+        if (!aligned(w_up->qs, 16) || !aligned(w_up->d, 2)) return PQ_ERR_ALIGN;
+    }
+    if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+    if (!supported(pqk::kTernary, w->cols)) return PQ_ERR_UNSUPPORTED;
+    if (g->n_tokens == 0) return PQ_OK;
+    if (!xq || !xd) return PQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
+    a = pqk::ExpertArgs{};
+    a.qs[0] = w->qs;
+    a.d[0] = w->d;
+    a.qs[1] = w_up ? w_up->qs : nullptr;
+    a.d[1] = w_up ? w_up->d : nullptr;
+    a.rows = w->rows;
+    a.cols = w->cols;
+    fill_groups(a, g);
+    a.act_by_token = act_by_token ? 1 : 0;
+    a.xq = xq;
+    a.xd = xd;
+    a.out0 = out0;
+    a.out1 = out1;
+    fill_debug(a, dbg);
+    *run = true;
+    return PQ_OK;
+}
+
+template <typename Supported>
+pq_status grid1_args(const pq_grid1_w* w, const pq_grid1_w* w_up, const pq_groups* g,
+                     const int8_t* xq, const float* xd, int32_t act_by_token, int32_t epilogue,
+                     void* out0, void* out1, const pq_debug* dbg, Supported supported,
+                     pqk::ExpertArgs& a, bool* run) {
+    *run = false;
+    if (!w || !w->qs || !w->qh || !w->d || !w->grid) return PQ_ERR_NULL;
+    pq_status st = check_groups(g);
+    if (st != PQ_OK) return st;
+    if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
+    if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
+        return st;
+    if (epilogue == PQ_EPI_F32_COMBINE && act_by_token) return PQ_ERR_UNSUPPORTED;
+    if (epilogue == PQ_EPI_SWIGLU_Q8) {
+        if (!w_up->qs || !w_up->qh || !w_up->d) return PQ_ERR_NULL;
+        if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
+            return PQ_ERR_SHAPE;
+        if (!aligned(w_up->qs, 16) || !aligned(w_up->qh, 8) || !aligned(w_up->d, 2))
+            return PQ_ERR_ALIGN;
+    }
+    if (!aligned(w->qs, 16) || !aligned(w->qh, 8) || !aligned(w->d, 2) || !aligned(w->grid, 16))
+        return PQ_ERR_ALIGN;
+    if (!supported(pqk::kGrid1, w->cols)) return PQ_ERR_UNSUPPORTED;
+    if (g->n_tokens == 0) return PQ_OK;
+    if (!xq || !xd) return PQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
+    a = pqk::ExpertArgs{};
+    a.qs[0] = w->qs;
+    a.qh[0] = w->qh;
+    a.d[0] = w->d;
+    a.qs[1] = w_up ? w_up->qs : nullptr;
+    a.qh[1] = w_up ? w_up->qh : nullptr;
+    a.d[1] = w_up ? w_up->d : nullptr;
+    a.grid = w->grid;
+    a.rows = w->rows;
+    a.cols = w->cols;
+    fill_groups(a, g);
+    a.act_by_token = act_by_token ? 1 : 0;
+    a.xq = xq;
+    a.xd = xd;
+    a.out0 = out0;
+    a.out1 = out1;
+    fill_debug(a, dbg);
+    *run = true;
+    return PQ_OK;
+}
+
+pq_status launch_matvec_any(pqk::Fmt fmt, int32_t epilogue, const pqk::ExpertArgs& a,
+                            const pq_debug* dbg, pq_stream stream) {
+    if (a.n_tokens == 1 && !dbg)
+        return from_hip(pqk::launch_matvec_tok1(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
+    return from_hip(pqk::launch_matvec(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
+}
+
+pq_status launch_tile_all(pqk::Fmt fmt, int32_t epilogue, pqk::ExpertArgs& a, pq_stream stream) {
+    a.heavy_min = 1;   // every active expert
+    return from_hip(pqk::launch_tile_q8(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,43 +372,12 @@ pq_status pq_moe_matvec_ternary(const pq_ternary_w* w, const pq_ternary_w* w_up,
                                 int32_t act_by_token, int32_t epilogue, void* out0, void* out1,
                                 const pq_debug* dbg, pq_stream stream) {
     return guarded([&]() -> pq_status {
-        if (!w || !w->qs || !w->d) return PQ_ERR_NULL;
-        pq_status st = check_groups(g);
-        if (st != PQ_OK) return st;
-        if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
-        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
-            return st;
-        if (epilogue == PQ_EPI_F32_COMBINE && act_by_token) return PQ_ERR_UNSUPPORTED;
-        if (epilogue == PQ_EPI_SWIGLU_Q8) {
-            if (!w_up->qs || !w_up->d) return PQ_ERR_NULL;
-            if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
-                return PQ_ERR_SHAPE;
-            if (!aligned(w_up->qs, 16) || !aligned(w_up->d, 2)) return PQ_ERR_ALIGN;
-        }
-        if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
-        if (!pqk::matvec_supported(pqk::kTernary, w->cols)) return PQ_ERR_UNSUPPORTED;
-        if (g->n_tokens == 0) return PQ_OK;
-        if (!xq || !xd) return PQ_ERR_NULL;
-        if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
-        pqk::ExpertArgs a{};
-        a.qs[0] = w->qs;
-        a.d[0] = w->d;
-        a.qs[1] = w_up ? w_up->qs : nullptr;
-        a.d[1] = w_up ? w_up->d : nullptr;
-        a.rows = w->rows;
-        a.cols = w->cols;
-        fill_groups(a, g);
-        a.act_by_token = act_by_token ? 1 : 0;
-        a.xq = xq;
-        a.xd = xd;
-        a.out0 = out0;
-        a.out1 = out1;
-        fill_debug(a, dbg);
-        if (g->n_tokens == 1 && !dbg)
-            return from_hip(pqk::launch_matvec_tok1(pqk::kTernary, static_cast<pqk::Epi>(epilogue), a,
-                                                    as_stream(stream)));
-        return from_hip(pqk::launch_matvec(pqk::kTernary, static_cast<pqk::Epi>(epilogue), a,
-                                           as_stream(stream)));
+        pqk::ExpertArgs a;
+        bool run;
+        const pq_status st = ternary_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg,
+                                          pqk::matvec_supported, a, &run);
+        if (st != PQ_OK || !run) return st;
+        return launch_matvec_any(pqk::kTernary, epilogue, a, dbg, stream);
     });
 }
 
@@ -313,49 +386,42 @@ pq_status pq_moe_matvec_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, const
                               int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
                               pq_stream stream) {
     return guarded([&]() -> pq_status {
-        if (!w || !w->qs || !w->qh || !w->d || !w->grid) return PQ_ERR_NULL;
-        pq_status st = check_groups(g);
-        if (st != PQ_OK) return st;
-        if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
-        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
-            return st;
-        if (epilogue == PQ_EPI_F32_COMBINE && act_by_token) return PQ_ERR_UNSUPPORTED;
-        if (epilogue == PQ_EPI_SWIGLU_Q8) {
-            if (!w_up->qs || !w_up->qh || !w_up->d) return PQ_ERR_NULL;
-            if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
-                return PQ_ERR_SHAPE;
-            if (!aligned(w_up->qs, 16) || !aligned(w_up->qh, 8) || !aligned(w_up->d, 2))
-                return PQ_ERR_ALIGN;
-        }
-        if (!aligned(w->qs, 16) || !aligned(w->qh, 8) || !aligned(w->d, 2) ||
-            !aligned(w->grid, 16))
-            return PQ_ERR_ALIGN;
-        if (!pqk::matvec_supported(pqk::kGrid1, w->cols)) return PQ_ERR_UNSUPPORTED;
-        if (g->n_tokens == 0) return PQ_OK;
-        if (!xq || !xd) return PQ_ERR_NULL;
-        if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
-        pqk::ExpertArgs a{};
-        a.qs[0] = w->qs;
-        a.qh[0] = w->qh;
-        a.d[0] = w->d;
-        a.qs[1] = w_up ? w_up->qs : nullptr;
-        a.qh[1] = w_up ? w_up->qh : nullptr;
-        a.d[1] = w_up ? w_up->d : nullptr;
-        a.grid = w->grid;
-        a.rows = w->rows;
-        a.cols = w->cols;
-        fill_groups(a, g);
-        a.act_by_token = act_by_token ? 1 : 0;
-        a.xq = xq;
-        a.xd = xd;
-        a.out0 = out0;
-        a.out1 = out1;
-        fill_debug(a, dbg);
-        if (g->n_tokens == 1 && !dbg)
-            return from_hip(pqk::launch_matvec_tok1(pqk::kGrid1, static_cast<pqk::Epi>(epilogue), a,
-                                                    as_stream(stream)));
-        return from_hip(pqk::launch_matvec(pqk::kGrid1, static_cast<pqk::Epi>(epilogue), a,
-                                           as_stream(stream)));
+        pqk::ExpertArgs a;
+        bool run;
+        const pq_status st = grid1_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg,
+                                        pqk::matvec_supported, a, &run);
+        if (st != PQ_OK || !run) return st;
+        return launch_matvec_any(pqk::kGrid1, epilogue, a, dbg, stream);
+    });
+}
+
+pq_status pq_moe_tile_q8_ternary(const pq_ternary_w* w, const pq_ternary_w* w_up,
+                                 const pq_groups* g, const int8_t* xq, const float* xd,
+                                 int32_t act_by_token, int32_t epilogue, void* out0, void* out1,
+                                 const pq_debug* dbg, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        pqk::ExpertArgs a;
+        bool run;
+        const pq_status st = ternary_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg,
+                                          [](pqk::Fmt, int cols) { return pqk::tile_q8_supported(cols); },
+                                          a, &run);
+        if (st != PQ_OK || !run) return st;
+        return launch_tile_all(pqk::kTernary, epilogue, a, stream);
+    });
+}
+
+pq_status pq_moe_tile_q8_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, const pq_groups* g,
+                               const int8_t* xq, const float* xd, int32_t act_by_token,
+                               int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
+                               pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        pqk::ExpertArgs a;
+        bool run;
+        const pq_status st = grid1_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg,
+                                        [](pqk::Fmt, int cols) { return pqk::tile_q8_supported(cols); },
+                                        a, &run);
+        if (st != PQ_OK || !run) return st;
+        return launch_tile_all(pqk::kGrid1, epilogue, a, stream);
     });
 }
 

@@ -176,4 +176,22 @@ __device__ __forceinline__ void route_softmax_store(const float* s_val, const in
     }
 }
 
+// Exclusive scan of one int per thread over the workgroup; `tmp` holds one
+// int per wave.  Every thread of the workgroup must call.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += tmp[i];
+    __syncthreads();
+    return base + incl - v;
+}
+
 }  // namespace pqk

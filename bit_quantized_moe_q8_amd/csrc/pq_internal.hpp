@@ -60,6 +60,9 @@ struct ExpertArgs {
     float* dbg_u;
     float* dbg_h;
     bool debug;
+    // Experts with at least this many assignments are left to the int8-MFMA
+    // tile kernel (which takes exactly those); 0: the mat-vec takes all.
+    int heavy_min;
 };
 
 // Decode mat-vec; returns hipErrorInvalidValue when no kernel matches cols.
@@ -86,6 +89,11 @@ struct RouteArgs {
 };
 hipError_t launch_decode1_gate_up(Fmt fmt, const ExpertArgs& a, const RouteArgs& r, hipStream_t s);
 bool matvec_supported(Fmt fmt, int cols);
+
+// Grouped int8-MFMA tile over q8 activations: the mat-vec's arithmetic and
+// epilogues for the experts with at least a.heavy_min (>= 1) assignments.
+hipError_t launch_tile_q8(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
+bool tile_q8_supported(int cols);
 
 // Prefill dequant-per-tile GEMM (grid1, bf16 MFMA).
 hipError_t launch_gemm(Epi epi, const ExpertArgs& a, hipStream_t s);

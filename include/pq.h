@@ -222,6 +222,34 @@ pq_status pq_moe_matvec_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
                               void *out1, const pq_debug *dbg, pq_stream stream);
 
 /*
+ * Grouped int8-MFMA tile over q8 activations (a tiled kernel for large
+ * batches: Parakon Runtime README, "How it works"; an int8 prefill tile:
+ * pxq_llama README, "Updates - 2026-07-19").  Arguments, layouts, epilogues
+ * and outputs are those of pq_moe_matvec_ternary / pq_moe_matvec_grid1, and
+ * so is the arithmetic: one v_mfma_i32_16x16x32_i8 per q8 block gives the
+ * same exact int32 block sums (dbg->isums equal the mat-vec's bit for bit),
+ * scaled in fp32 as sum over 256-blocks of d * (sum over 32-blocks of
+ * xd * isum).  Only the fp32 summation order differs, within the tolerance
+ * of the fp32 result.  Every active expert is processed in chunks of up to
+ * 32 assignments and tiles of 64 weight rows (32 gate + 32 up rows for
+ * PQ_EPI_SWIGLU_Q8).  cols % 256 == 0 (any such cols); rows >= 1 (rows % 32
+ * == 0 for PQ_EPI_SWIGLU_Q8).
+ *
+ * pq_moe_matvec_* use this kernel by themselves, per expert, when the batch
+ * has more assignments than experts and at least 8 tokens: experts holding
+ * at least 8 assignments then run here, the others on the mat-vec (two
+ * launches on the stream).
+ */
+pq_status pq_moe_tile_q8_ternary(const pq_ternary_w *w, const pq_ternary_w *w_up,
+                                 const pq_groups *g, const int8_t *xq, const float *xd,
+                                 int32_t act_by_token, int32_t epilogue, void *out0,
+                                 void *out1, const pq_debug *dbg, pq_stream stream);
+pq_status pq_moe_tile_q8_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
+                               const pq_groups *g, const int8_t *xq, const float *xd,
+                               int32_t act_by_token, int32_t epilogue, void *out0,
+                               void *out1, const pq_debug *dbg, pq_stream stream);
+
+/*
  * Prefill: grouped dequant-per-tile GEMM over grid1 weights with bf16
  * activations on MFMA (Parakon Runtime README, "How it works": prompt
  * processing at large batch sizes uses a dequant-per-tile GEMM path).  Packed

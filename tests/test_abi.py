@@ -116,6 +116,27 @@ def test_grid1_validation(L):
     assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 64, 2560)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_UNSUPPORTED
 
 
+def test_tile_q8_validation(L):
+    """The int8-MFMA tile entry points share the mat-vec's checks but accept
+    any cols that is a multiple of 256 (e.g. 1280, which the mat-vec rejects)."""
+    import bit_quantized_moe_q8_amd as pq
+    b = ctypes.byref
+    g = _groups(pq)
+    for f, mk in ((L.pq_moe_tile_q8_ternary, lambda rows, cols: pq.TernaryW(A16, A16, 8, rows, cols)),
+                  (L.pq_moe_tile_q8_grid1, lambda rows, cols: pq.Grid1W(A16, A16, A16, A16, 8, rows, cols))):
+        ok_w = mk(64, 1024)
+        assert f(b(mk(64, 1000)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_SHAPE
+        assert f(b(mk(64, 128)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_SHAPE
+        assert f(b(ok_w), None, b(g), A16, A16, 1, 1, A16, A16, None, S) == pq.PQ_ERR_NULL
+        w48 = mk(48, 1024)
+        assert f(b(w48), b(w48), b(g), A16, A16, 1, 1, A16, A16, None, S) == pq.PQ_ERR_SHAPE
+        assert f(b(ok_w), None, b(g), A1, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_ALIGN
+        assert f(b(ok_w), b(ok_w), b(g), A16, A16, 1, 2, A16, A16, None, S) == pq.PQ_ERR_UNSUPPORTED
+        assert f(b(ok_w), None, b(g), A16, A16, 1, 3, A16, A16, None, S) == pq.PQ_ERR_UNSUPPORTED
+        assert f(b(ok_w), None, None, A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_NULL
+        assert f(b(mk(64, 1280)), None, b(_groups(pq, T=0)), None, None, 1, 0, A16, None, None, S) == pq.PQ_OK
+
+
 def test_combine_validation(L):
     import bit_quantized_moe_q8_amd as pq
     f = L.pq_moe_combine
