@@ -11,11 +11,13 @@
 // results are the block sums sum_k w[n][k] * xq[t][k] of 16 weight rows x 16
 // assignments, bit-exact for any order of the 32 products.  Then, in fp32,
 //   blk[n][t] += xd[t][b] * isum      (8 blocks of a 256-weight scale block)
-//   tot[n][t] += d[n][B] * blk[n][t]  (once per scale block).
+//   tot[n][t] += d[n][B] * blk[n][t]  (once per scale block),
+// both as explicit fused multiply-adds, so every build of the kernel (with
+// or without its debug outputs) rounds the same way.
 //
-// Work item: (expert, chunk of up to 32 of its assignments, tile of 64
+// Work item: (expert, chunk of up to 64 of its assignments, tile of 64
 // physical weight rows: 32 gate + 32 up rows for the SwiGLU epilogue, else 64
-// rows).  Wave w owns 16 of the 64 rows (the A operand) and both 16-column
+// rows).  Wave w owns 16 of the 64 rows (the A operand) and all live 16-column
 // assignment subtiles (the B operand).  The K loop runs over 256-weight
 // slabs: each lane loads its own weight row's packed slab straight into
 // registers one slab ahead, while the workgroup stages the chunk's q8
@@ -36,6 +38,8 @@
 // Items are chosen on the device from the grouping (offsets / active): an
 // expert takes part when it holds at least `heavy_min` assignments, so the
 // decode mat-vec can take the others in a launch of its own.
+#include <type_traits>
+
 #include "pq_device.hpp"
 #include "pq_internal.hpp"
 
@@ -47,8 +51,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTok = 32;          // assignments per item: two 16-column subtiles
+constexpr int kTok = 64;          // assignments per item: up to four 16-column subtiles
 constexpr int kSub = 16;
+constexpr int kJMax = kTok / kSub;
 constexpr int kSlabK = 256;       // weights per slab: one weight-scale block
 constexpr int kSlabBlocks = kSlabK / 32;
 constexpr int kRows = 64;         // physical weight rows per item, 16 per wave
@@ -70,9 +75,14 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
     constexpr int TR = kRows / NMAT;   // output rows per item
     constexpr int KW = TileFmt<FMT>::kWords;
 
-    // B fragments of a slab, [slot][block][lane group][assignment column]
-    __shared__ uint2 s_x[2][kSlabBlocks][4][kTok];
-    __shared__ float s_xd[2][kSlabBlocks][kTok];
+    // B fragments of a slab: entry (column c, block q, lane group g) at
+    // c * kXStride + 4q + g.  The pad of one entry per column shifts
+    // consecutive columns by two banks, so a fragment read (16 columns, one
+    // block and lane group) and the staging writes are free of bank
+    // conflicts; block scales likewise at c * 9 + q.
+    constexpr int kXStride = 4 * kSlabBlocks + 1;
+    __shared__ uint2 s_x[2][kTok * kXStride];
+    __shared__ float s_xd[2][kTok * (kSlabBlocks + 1)];
     __shared__ float s_d[2][kRows];
     __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : 1];
     __shared__ float s_gu[NMAT][(NMAT == 2) ? TR : 1][kTok + 1];
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
         const int beg = load_uniform(p.offsets + e);
         const int m = load_uniform(p.offsets + e + 1) - beg;
         const int mcount = min(kTok, m - cbeg);
-        const int jn = (mcount + kSub - 1) / kSub;   // 1 or 2 live column subtiles
+        const int jn = (mcount + kSub - 1) / kSub;   // live column subtiles, 1..4
         const int n0 = tile * TR;
         if (tid < kTok) {
             // columns past mcount repeat the last assignment and are never stored
@@ -168,55 +178,72 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
             }
         };
 
-        // ---- staging of a slab: 2 x 16 activation bytes, one block scale
-        // and (first 64 threads) one weight scale per thread
-        uint4 xr[2];
-        float xdr = 0.0f, dr = 0.0f;
+        // ---- staging of a slab: thread (column c, block q) for two (c, q)
+        // pairs moves the 32 activation bytes of block q and its scale; the
+        // first 64 threads also move one weight scale
+        uint4 xr[2][2];
+        float xdr[2];
+        uint32_t dr = 0;   // fp16 bits: converted only when stored, so that no
+                           // instruction waits on the loads before the compute
         auto sload = [&](int sb) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int unit = tid + kThreads * k;
-                const int tok = unit >> 4, uu = unit & 15;
-                xr[k] = *reinterpret_cast<const uint4*>(p.xq + static_cast<int64_t>(s_arow[tok]) * cols +
-                                                        sb * kSlabK + uu * 16);
+                const int pair = tid + kThreads * k;
+                const int c = pair >> 3, q = pair & 7;
+                const int64_t row = s_arow[c];
+                const uint4* src = reinterpret_cast<const uint4*>(p.xq + row * cols + sb * kSlabK + q * 32);
+                xr[k][0] = src[0];
+                xr[k][1] = src[1];
+                xdr[k] = p.xd[row * n_sub_row + sb * kSlabBlocks + q];
             }
-            xdr = p.xd[static_cast<int64_t>(s_arow[tid >> 3]) * n_sub_row + sb * kSlabBlocks + (tid & 7)];
             if (tid < kRows) {
-                const int mr = (NMAT == 2) ? (tid >> 5) : 0;
+                // (a select of the two scalar pointers: indexing p.d by a lane
+                // value would load the pointer from the argument block and
+                // wait for every load in flight)
+                const uint16_t* dbase = (NMAT == 2 && tid >= 32) ? p.d[1] : p.d[0];
                 const int nr = min(n0 + ((NMAT == 2) ? (tid & 31) : tid), rows - 1);
-                dr = half_bits_to_float(p.d[mr][(static_cast<int64_t>(e) * rows + nr) * d_row + sb]);
+                dr = dbase[(static_cast<int64_t>(e) * rows + nr) * d_row + sb];
             }
         };
         auto sstore = [&](int sl) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int unit = tid + kThreads * k;
-                const int tok = unit >> 4, uu = unit & 15;
-                const int q = uu >> 1, h = uu & 1;
-                const uint32_t qq[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+                const int pair = tid + kThreads * k;
+                const int c = pair >> 3, q = pair & 7;
+                uint2* dst = &s_x[sl][c * kXStride + 4 * q];
+                const uint32_t lo[4] = {xr[k][0].x, xr[k][0].y, xr[k][0].z, xr[k][0].w};
+                const uint32_t hi[4] = {xr[k][1].x, xr[k][1].y, xr[k][1].z, xr[k][1].w};
                 if constexpr (FMT == kTernary) {
-                    // unit h of block q: dword s of its byte transpose is
-                    // the K slots 4h.. of lane group s
-                    uint32_t t[4];
-                    transpose_bytes4(qq, t);
+                    // dword s of the byte transpose of each 16-byte half holds
+                    // the K slots of lane group s
+                    uint32_t t0[4], t1[4];
+                    transpose_bytes4(lo, t0);
+                    transpose_bytes4(hi, t1);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) reinterpret_cast<uint32_t*>(&s_x[sl][q][s][tok])[h] = t[s];
+                    for (int g2 = 0; g2 < 4; ++g2) dst[g2] = make_uint2(t0[g2], t1[g2]);
                 } else {
-                    s_x[sl][q][2 * h][tok] = make_uint2(qq[0], qq[1]);
-                    s_x[sl][q][2 * h + 1][tok] = make_uint2(qq[2], qq[3]);
+                    dst[0] = make_uint2(lo[0], lo[1]);
+                    dst[1] = make_uint2(lo[2], lo[3]);
+                    dst[2] = make_uint2(hi[0], hi[1]);
+                    dst[3] = make_uint2(hi[2], hi[3]);
                 }
+                s_xd[sl][c * (kSlabBlocks + 1) + q] = xdr[k];
             }
-            s_xd[sl][tid & 7][tid >> 3] = xdr;
-            if (tid < kRows) s_d[sl][tid] = dr;
+            if (tid < kRows) s_d[sl][tid] = half_bits_to_float(static_cast<uint16_t>(dr));
         };
 
-        float tot[2][4];
+        float tot[kJMax][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kJMax; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) tot[j][i] = 0.0f;
 
-        auto compute = [&](int sl, const uint4 (&w)[KW], int sb) {
+        // One slab, in two halves of 4 blocks: the A fragments of the half,
+        // its 4 x JN MFMAs into their own accumulators, then their fp32
+        // scaling (so the MFMAs issue back to back instead of each waiting
+        // for its result).
+        auto compute = [&](auto jn_c, int sl, const uint4 (&w)[KW], int sb) {
+            constexpr int JN = decltype(jn_c)::value;
             uint32_t wv[4 * KW];
 #pragma unroll
             for (int i = 0; i < KW; ++i) {
@@ -225,37 +252,47 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
                 wv[4 * i + 2] = w[i].z;
                 wv[4 * i + 3] = w[i].w;
             }
-            float blk[2][4];
+            float blk[JN][4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < JN; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) blk[j][i] = 0.0f;
 #pragma unroll
-            for (int q = 0; q < kSlabBlocks; ++q) {
-                uint64_t afrag;
-                if constexpr (FMT == kTernary) {
-                    const uint32_t lo = static_cast<uint32_t>(ternary_decode4((wv[2 * q] >> (2 * g)) & 0x03030303u));
-                    const uint32_t hi = static_cast<uint32_t>(ternary_decode4((wv[2 * q + 1] >> (2 * g)) & 0x03030303u));
-                    afrag = (static_cast<uint64_t>(hi) << 32) | lo;
-                } else {
-                    const uint32_t lo8 = (wv[q] >> (8 * g)) & 0xffu;
-                    const uint32_t h16 = wv[8 + (q >> 1)] >> (16 * (q & 1));
-                    const uint32_t hi3 = (h16 >> (3 * g)) & 7u;
-                    const uint2 cb = s_grid[lo8 | (hi3 << 8)];
-                    afrag = (static_cast<uint64_t>(cb.y) << 32) | cb.x;
+            for (int half = 0; half < 2; ++half) {
+                v4i is[4][JN];
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int q = 4 * half + qq;
+                    uint64_t afrag;
+                    if constexpr (FMT == kTernary) {
+                        const uint32_t lo = static_cast<uint32_t>(ternary_decode4((wv[2 * q] >> (2 * g)) & 0x03030303u));
+                        const uint32_t hi = static_cast<uint32_t>(ternary_decode4((wv[2 * q + 1] >> (2 * g)) & 0x03030303u));
+                        afrag = (static_cast<uint64_t>(hi) << 32) | lo;
+                    } else {
+                        const uint32_t lo8 = (wv[q] >> (8 * g)) & 0xffu;
+                        const uint32_t h16 = wv[8 + (q >> 1)] >> (16 * (q & 1));
+                        const uint32_t hi3 = (h16 >> (3 * g)) & 7u;
+                        const uint2 cb = s_grid[lo8 | (hi3 << 8)];
+                        afrag = (static_cast<uint64_t>(cb.y) << 32) | cb.x;
+                    }
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) {
+                        const uint2 bx = s_x[sl][(kSub * j + r) * kXStride + 4 * q + g];
+                        const uint64_t bfrag = (static_cast<uint64_t>(bx.y) << 32) | bx.x;
+                        is[qq][j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                            static_cast<long>(afrag), static_cast<long>(bfrag), v4i{0, 0, 0, 0}, 0, 0, 0);
+                    }
                 }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (j < jn) {
-                        const uint2 bx = s_x[sl][q][g][kSub * j + r];
-                        const uint64_t bfrag = (static_cast<uint64_t>(bx.y) << 32) | bx.x;
-                        const v4i is = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                            static_cast<long>(afrag), static_cast<long>(bfrag), v4i{0, 0, 0, 0}, 0, 0, 0);
-                        const float xdv = s_xd[sl][q][kSub * j + r];
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int q = 4 * half + qq;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) blk[j][i] += xdv * static_cast<float>(is[i]);
+                    for (int j = 0; j < JN; ++j) {
+                        const float xdv = s_xd[sl][(kSub * j + r) * (kSlabBlocks + 1) + q];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) blk[j][i] = fmaf(xdv, static_cast<float>(is[qq][j][i]), blk[j][i]);
                         if constexpr (DBG) {
-                            int32_t* dst = p.dbg_isums[mat_a];
+                            int32_t* dst = (NMAT == 2 && mat_a) ? p.dbg_isums[1] : p.dbg_isums[0];
                             const int col = kSub * j + r;
                             if (dst && col < mcount) {
                                 const int a = s_asg[col];
@@ -264,8 +301,8 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
                                     const int pr = 16 * wave + 4 * g + i;
                                     const int n = n0 + ((NMAT == 2) ? (pr & 31) : pr);
                                     if (n < rows)
-                                        dst[(static_cast<int64_t>(a) * rows + n) * n_sub_row +
-                                            sb * kSlabBlocks + q] = is[i];
+                                        dst[(static_cast<int64_t>(a) * rows + n) * n_sub_row + sb * kSlabBlocks + q] =
+                                            is[qq][j][i];
                                 }
                             }
                         }
@@ -276,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
             for (int i = 0; i < 4; ++i) {
                 const float dsc = s_d[sl][16 * wave + 4 * g + i];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) tot[j][i] += dsc * blk[j][i];
+                for (int j = 0; j < JN; ++j) tot[j][i] = fmaf(dsc, blk[j][i], tot[j][i]);
             }
         };
 
@@ -292,7 +329,12 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
                 wload(sb + 1, wn);
                 sload(sb + 1);
             }
-            compute(sl, wc, sb);
+            switch (jn) {
+                case 1: compute(std::integral_constant<int, 1>{}, sl, wc, sb); break;
+                case 2: compute(std::integral_constant<int, 2>{}, sl, wc, sb); break;
+                case 3: compute(std::integral_constant<int, 3>{}, sl, wc, sb); break;
+                default: compute(std::integral_constant<int, 4>{}, sl, wc, sb); break;
+            }
             if (more) {
                 sstore(sl ^ 1);
 #pragma unroll
@@ -305,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
         // columns 16j + r
         if constexpr (EPI == kEpiSwigluQ8) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < kJMax; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s_gu[mat_a][16 * (wave & 1) + 4 * g + i][kSub * j + r] = tot[j][i];
             __syncthreads();
@@ -331,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kJMax; ++j) {
                 const int col = kSub * j + r;
                 if (j < jn && col < mcount) {
                     const int a = s_asg[col];
