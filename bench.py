@@ -3,7 +3,9 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 decode: q8(x) -> top-k route -> group -> fused gate/up mat-vec (SwiGLU + q8)
 -> down mat-vec -> weighted combine; prefill: route -> group -> gate/up GEMM
-(SwiGLU, bf16 h) -> down GEMM -> combine.  Each step uses the weights of a
+(SwiGLU, bf16 h) -> down GEMM -> combine; q8 prefill: the decode sequence at
+2048 tokens, where the mat-vec entry points hand every expert with 8 or more
+assignments to the int8-MFMA tile kernel.  Each step uses the weights of a
 different layer from a rotating pool sized so that the packed bytes touched
 between two visits of a layer exceed the 256 MB last-level cache several
 times over: the weights are read from HBM, not from cache.  Steps are
@@ -11,9 +13,9 @@ captured in HIP graphs (several layers per graph, as a model's decode step
 would be) and replayed.
 
 value: packed weight bytes of the experts touched per step / step time (GB/s).
-roofline: the dominant kernel (fused gate/up), its algorithmic bytes per
-launch over its average launch time, measured with HIP events around each
-launch on the launch stream.
+roofline: the dominant kernel (fused gate/up), its algorithmic bytes (decode)
+or operations (prefill) per launch over its average launch time, measured
+with HIP events around the launches on the launch stream.
 cpu_baseline: the CPU oracle on a bounded sample of the same steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
 MALL_BYTES = 256 << 20
 
 
@@ -119,6 +122,7 @@ def main():
     seed = cfg["seed"] if args.seed is None else args.seed
     fmt, T, H, I, E, k = cfg["fmt"], cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
     prefill = cfg["kind"] == "prefill"
+    q8_prefill = cfg["kind"] == "prefill_q8"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -238,6 +242,12 @@ def main():
         layer.use_state(states[l])
         if prefill:
             layer.gate_up(xs[l], layers[l]["gate"], layers[l]["up"])
+        elif q8_prefill:
+            # the int8-MFMA tile alone (the mat-vec entry point adds a launch
+            # for the experts under 8 assignments; at 2048 tokens it has none)
+            tile = pq.moe_tile_q8_ternary if fmt == "ternary" else pq.moe_tile_q8_grid1
+            tile(layers[l]["gate"], layers[l]["up"], layer.groups, layer.xq, layer.xd, True,
+                 pq.PQ_EPI_SWIGLU_Q8, layer.hq, layer.hd)
         elif decode1:
             # one token: the gate/up launch that routes and quantizes itself
             st = states[l]
@@ -268,8 +278,13 @@ def main():
         torch.cuda.synchronize()
         kms = [k0.elapsed_time(k1) / R] * R
     roofline = None
-    kfile = "k_gemm.hip" if prefill else ("k_matvec1.hip" if decode1 else "k_matvec.hip")
-    srcs = [kfile, "pq_device.hpp", "pq_internal.hpp"]
+    # the mat-vec entry point hands experts with 8+ assignments to the tile
+    # kernel when a batch of 8+ tokens has more assignments than experts
+    heavy_split = (not prefill and not q8_prefill and not decode1 and T >= 8 and T * k > E)
+    kfiles = (["k_gemm.hip"] if prefill else ["k_tile_q8.hip"] if q8_prefill
+              else ["k_matvec1.hip"] if decode1
+              else ["k_matvec.hip", "k_tile_q8.hip"] if heavy_split else ["k_matvec.hip"])
+    srcs = kfiles + ["pq_device.hpp", "pq_internal.hpp"]
     traffic = measured_traffic(args.workload, srcs)
     if R:
         avg_ms = sum(kms) / R
@@ -282,9 +297,19 @@ def main():
                         "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                         "avg_launch_us": round(avg_ms * 1e3, 3), "flop_per_launch": flops}
+        elif q8_prefill:
+            # algorithmic int8 operations of the gate/up tile: 2 * A * (2 * I) * H
+            ops = 2.0 * T * k * 2 * I * H
+            ach = ops / (avg_ms * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "kernel": "k_tile_q8 (gate/up, int8 MFMA, SwiGLU+q8 epilogue)",
+                        "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                        "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                        "avg_launch_us": round(avg_ms * 1e3, 3), "op_per_launch": ops}
         else:
             ach = avg_bytes / (avg_ms * 1e-3) / 1e9
             kname = ("k_matvec_tok1 (one token: routing, q8, gate/up, SwiGLU+q8 epilogue)" if decode1
+                     else "k_tile_q8 + k_matvec (gate/up, SwiGLU+q8 epilogue; experts with 8+ "
+                          "assignments on the int8-MFMA tile, the rest on the mat-vec)" if heavy_split
                      else "k_matvec (gate/up, SwiGLU+q8 epilogue)")
             roofline = {"bound": "hbm", "kernel": kname,
                         "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -296,7 +321,7 @@ def main():
     # ---- CPU oracle baseline on a bounded sample of the same steps
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(args, cfg, layers, xs, lg, n_active, per_expert, fmt, prefill, L, log)
+        cpu = cpu_baseline(args, cfg, layers, xs, lg, n_active, per_expert, fmt, prefill, q8_prefill, L, log)
 
     out = {
         "metric": "decode expert mat-vec GB/s (packed bytes) & % HBM peak; prefill GEMM % MFMA peak",
@@ -316,7 +341,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(args, cfg, layers, xs, lg, n_active, per_expert, fmt, prefill, L, log):
+def cpu_baseline(args, cfg, layers, xs, lg, n_active, per_expert, fmt, prefill, q8_prefill, L, log):
     """The oracle, as it stands, on whole steps of the same workload until the budget is spent."""
     import numpy as np
 
@@ -350,14 +375,17 @@ def cpu_baseline(args, cfg, layers, xs, lg, n_active, per_expert, fmt, prefill, 
             inp["x_bf16"] = xs[l].cpu().numpy().view(np.uint16)
         else:
             inp["x"] = xs[l].cpu().numpy()
-        if prefill:
+        if prefill or q8_prefill:
             # a fixed sample of assignments per step; the step time is scaled
             # up by A / sample (the oracle's work is linear in assignments)
             A = T * k
             ns = min(A, 16)
             sub = np.linspace(0, A - 1, ns).astype(np.int64)
             t0 = time.perf_counter()
-            moe.prefill_ffn(inp, assign_subset=sub)
+            if prefill:
+                moe.prefill_ffn(inp, assign_subset=sub)
+            else:
+                moe.decode_ffn(inp, want_isums=False, assign_subset=sub)
             spent += (time.perf_counter() - t0) * (A / ns)
         else:
             t0 = time.perf_counter()
@@ -370,7 +398,7 @@ def cpu_baseline(args, cfg, layers, xs, lg, n_active, per_expert, fmt, prefill, 
     gbs = done_bytes / spent / 1e9
     log("cpu oracle: %d steps in %.1f s, %.3f GB/s, %d threads" % (done_steps, spent, gbs, oracle.num_threads()))
     what = ("%d steps, 16 of %d assignments each, time scaled to the whole step" % (done_steps, T * k)
-            if prefill else "%d whole steps" % done_steps)
+            if prefill or q8_prefill else "%d whole steps" % done_steps)
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%s (layers 0..%d of the pool), %.1f s" % (what, done_steps - 1, spent),
             "tokens_per_s": round(done_steps * T / spent, 3)}

@@ -84,8 +84,11 @@ def grouped_matvec_bf16(fmt, planes, grid, ids, x_rows_bf16, row_of_assign, K,
     return y, t
 
 
-def decode_ffn(inp: dict, want_isums: bool = True) -> dict:
-    """Free-running oracle chain of one decode MoE FFN layer."""
+def decode_ffn(inp: dict, want_isums: bool = True, assign_subset=None) -> dict:
+    """Free-running oracle chain of one decode MoE FFN layer.
+
+    assign_subset restricts the expert work to those assignments (rows of the
+    others are left NaN / 0) and skips the combine (y is None)."""
     cfg = inp["cfg"]
     fmt, k, H, I, E = cfg["fmt"], cfg["top_k"], cfg["H"], cfg["I"], cfg["E"]
     grid = inp.get("grid")
@@ -95,13 +98,28 @@ def decode_ffn(inp: dict, want_isums: bool = True) -> dict:
     r["offsets"], r["sorted"], r["active"] = group(r["ids"], E)
     A = r["ids"].size
     tok = np.arange(A) // k
-    r["g"], r["tg"], r["isum_g"] = grouped_matvec_q8(fmt, inp["gate"], grid, r["ids"], r["xq"], r["xd"], tok, H, want_isums)
-    r["u"], r["tu"], r["isum_u"] = grouped_matvec_q8(fmt, inp["up"], grid, r["ids"], r["xq"], r["xd"], tok, H, want_isums)
-    h64 = swiglu(r["g"].astype(np.float32), r["u"].astype(np.float32))
+    sub = assign_subset
+    r["g"], r["tg"], r["isum_g"] = grouped_matvec_q8(fmt, inp["gate"], grid, r["ids"], r["xq"], r["xd"], tok, H,
+                                                     want_isums, assign_subset=sub)
+    r["u"], r["tu"], r["isum_u"] = grouped_matvec_q8(fmt, inp["up"], grid, r["ids"], r["xq"], r["xd"], tok, H,
+                                                     want_isums, assign_subset=sub)
+    if sub is None:
+        h64 = swiglu(r["g"].astype(np.float32), r["u"].astype(np.float32))
+        r["hq"], r["hd"] = quantize_q8(h64.astype(np.float32))
+    else:
+        sub = np.asarray(sub)
+        h64 = np.full((A, I), np.nan)
+        h64[sub] = swiglu(r["g"][sub].astype(np.float32), r["u"][sub].astype(np.float32))
+        r["hq"] = np.zeros((A, I), np.int8)
+        r["hd"] = np.zeros((A, I // 32), np.float32)
+        r["hq"][sub], r["hd"][sub] = quantize_q8(h64[sub].astype(np.float32))
     r["h"] = h64
-    r["hq"], r["hd"] = quantize_q8(h64.astype(np.float32))
-    r["out"], r["tout"], r["isum_d"] = grouped_matvec_q8(fmt, inp["down"], grid, r["ids"], r["hq"], r["hd"], np.arange(A), I, want_isums)
-    r["y"], r["ty"] = combine(r["out"].astype(np.float32), r["w"].astype(np.float32), k)
+    r["out"], r["tout"], r["isum_d"] = grouped_matvec_q8(fmt, inp["down"], grid, r["ids"], r["hq"], r["hd"],
+                                                         np.arange(A), I, want_isums, assign_subset=sub)
+    if sub is None:
+        r["y"], r["ty"] = combine(r["out"].astype(np.float32), r["w"].astype(np.float32), k)
+    else:
+        r["y"], r["ty"] = None, None
     return r
 
 

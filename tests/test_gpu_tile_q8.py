@@ -186,3 +186,38 @@ def test_tile_q8_single_assignment():
         torch.cuda.synchronize()
         y_ref, t_ref, _ = moe.grouped_matvec_q8(fmt, planes, grid, ids, xq, xd, np.arange(1), K, want_isums=False)
         assert_tol(to_host(out), y_ref, t_ref, "y")
+
+
+@pytest.mark.parametrize("name", ["ternary_moe_prefill_q8_t2048", "grid1_moe_prefill_q8_t2048"])
+def test_q8_prefill_full_size_sampled(name):
+    """2048 tokens through all 256 experts with q8 activations, in the layer
+    sequence the benchmark times (the mat-vec entry points hand every expert
+    with 8+ assignments to the tile kernel).  Six tokens (48 assignments) are
+    checked: routing exactly, q8(h) against the free-running oracle (up to
+    rounding ties), the down outputs on the GPU's own q8(h), and y."""
+    from bit_quantized_moe_q8_amd.layer import DecodeLayer
+    from gpu_util import q8_rows_equal_ignoring_ties
+    say("q8 prefill full size", name)
+    inp = wl.make_workload(name)
+    cfg = inp["cfg"]
+    fmt, T, H, I, E, k = cfg["fmt"], cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
+    grid = inp.get("grid")
+    layer = DecodeLayer(fmt, T, H, I, E, k, dev())
+    assert not layer.fused and not layer.fused_combine
+    W = {n: weights_to_device(fmt, inp[n], grid) for n in ("gate", "up", "down")}
+    layer(to_dev(inp["x"]), to_dev(inp["logits"]), W["gate"], W["up"], W["down"])
+    torch.cuda.synchronize()
+    toks = np.array([0, 1, 511, 1024, 1500, T - 1])
+    sub = (toks[:, None] * k + np.arange(k)).ravel()
+    ref = moe.decode_ffn(inp, want_isums=False, assign_subset=sub)
+    assert_equal(to_host(layer.ids), ref["ids"], "ids")
+    hq, hd = to_host(layer.hq), to_host(layer.hd)
+    ok = q8_rows_equal_ignoring_ties(hq[sub], ref["hq"][sub], ref["h"][sub], ref["hd"][sub])
+    assert ok.all(), "q8(h): %d of %d codes differ beyond rounding ties" % ((~ok).sum(), ok.size)
+    o_ref, to, _ = moe.grouped_matvec_q8(fmt, inp["down"], grid, ref["ids"], hq, hd, np.arange(T * k), I,
+                                         want_isums=False, assign_subset=sub)
+    out = to_host(layer.out)
+    assert_tol(out[sub], o_ref[sub], to[sub], "out")
+    w = to_host(layer.w)
+    y_ref, ty = oracle.combine(out[sub], w[toks], k)
+    assert_tol(to_host(layer.y)[toks], y_ref, ty, "y")

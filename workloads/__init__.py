@@ -65,6 +65,13 @@ WORKLOADS = {
     # prefill: 2048 tokens through 256 grid-codebook experts, bf16 activations
     "grid1_moe_prefill_t2048": dict(kind="prefill", fmt="grid1", E=256, H=4096, I=1536,
                                     T=2048, top_k=8, logits="uniform", seed=104),
+    # the same 2048-token batches with q8 activations (fp32 x as for decode),
+    # for the exact-block-sum int8-MFMA tile path: grid1 with the prefill
+    # shapes, ternary with the 64-token decode shapes and uniform routing
+    "grid1_moe_prefill_q8_t2048": dict(kind="prefill_q8", fmt="grid1", E=256, H=4096, I=1536,
+                                       T=2048, top_k=8, logits="uniform", seed=105),
+    "ternary_moe_prefill_q8_t2048": dict(kind="prefill_q8", fmt="ternary", E=256, H=2048, I=768,
+                                         T=2048, top_k=8, logits="uniform", seed=106),
 }
 
 # The 81 byte values whose four 2-bit fields all lie in {0, 1, 2}; a uniform
