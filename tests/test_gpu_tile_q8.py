@@ -221,3 +221,39 @@ def test_q8_prefill_full_size_sampled(name):
     w = to_host(layer.w)
     y_ref, ty = oracle.combine(out[sub], w[toks], k)
     assert_tol(to_host(layer.y)[toks], y_ref, ty, "y")
+
+
+def test_heavy_split_layer_in_captured_graph():
+    """A layer step whose mat-vec entry points launch the tile kernel for a
+    heavy expert and the mat-vec for the rest, captured in a graph, replays
+    to the eager step's bits, three times, with eager work on the same
+    buffers between the replays."""
+    from bit_quantized_moe_q8_amd.layer import DecodeLayer
+    say("heavy split layer in graph")
+    fmt, T, H, I, E, k = "ternary", 16, 512, 256, 8, 2
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 0] += 8.0          # expert 0 in every token's top-2: 16 assignments
+    planes = {n: wl.stack_experts(fmt, 5, n, E, *((I, H) if n != "down" else (H, I))) for n in ("gate", "up", "down")}
+    W = {n: weights_to_device(fmt, planes[n]) for n in planes}
+    x = to_dev(wl.activations_f32(5, T, H))
+    lg = to_dev(logits)
+    layer = DecodeLayer(fmt, T, H, I, E, k, dev())
+    layer(x, lg, W["gate"], W["up"], W["down"])
+    torch.cuda.synchronize()
+    ref_hq, ref_y = to_host(layer.hq), to_host(layer.y)
+    assert (to_host(layer.ids)[:, 0] == 0).all()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x, lg, W["gate"], W["up"], W["down"])
+    for rep in range(3):
+        layer.hq.zero_()
+        layer.y.zero_()
+        layer(x, lg, W["gate"], W["up"], W["down"])   # eager work between replays
+        layer.hq.zero_()
+        layer.y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_equal(to_host(layer.hq), ref_hq, "hq (replay %d)" % rep)
+        assert_equal(to_host(layer.y), ref_y, "y (replay %d)" % rep)
