@@ -62,6 +62,7 @@ def lib():
         L.or_unpack_ternary.argtypes = [p, i64, i64, p]
         L.or_unpack_ternary.restype = i64
         L.or_unpack_grid1.argtypes = [p, p, p, i64, i64, p]
+        L.or_unpack_sign1.argtypes = [p, p, i64, i64, p]
         L.or_matvec_q8.argtypes = [p, p, i64, i64, p, p, p, p, p]
         L.or_matvec_bf16.argtypes = [p, p, i64, i64, p, p, p]
         L.or_route_topk.argtypes = [p, i64, i64, ctypes.c_int, p, p]
@@ -164,6 +165,20 @@ def unpack_grid1(qs: np.ndarray, qh: np.ndarray, grid: np.ndarray, k: int) -> np
     rc = lib().or_unpack_grid1(_p(qs), _p(qh), _p(grid), n, k, _p(w))
     if rc != 0:
         raise OracleError("or_unpack_grid1 failed (%d)" % rc)
+    return w
+
+
+def unpack_sign1(signs: np.ndarray, sc: np.ndarray, k: int) -> np.ndarray:
+    """Integer weights sc * (+-1) of the sub-scaled sign format, rows of k
+    weights (signs k/8 bytes, sub-scales k/32 bytes per row); the per-row
+    anchor is applied by the mat-vec as the row's scale."""
+    signs = _c(signs, np.uint8)
+    sc = _c(sc, np.uint8)
+    n = signs.size // (k // 8)
+    w = np.empty((n, k), np.int8)
+    rc = lib().or_unpack_sign1(_p(signs), _p(sc), n, k, _p(w))
+    if rc != 0:
+        raise OracleError("or_unpack_sign1 failed (%d)" % rc)
     return w
 
 

@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (combine, float_to_bf16, group, matvec_bf16, matvec_q8, quantize_q8, route_topk,
+from . import (combine, float_to_bf16, group, matvec_bf16, matvec_q8, quantize_q8, route_topk, unpack_sign1,
                swiglu, unpack_grid1, unpack_ternary)
 
 
@@ -34,7 +34,17 @@ def unpack_expert(fmt: str, planes: dict, e: int, K: int, grid=None) -> np.ndarr
         return unpack_ternary(planes["qs"][e], K)
     if fmt == "grid1":
         return unpack_grid1(planes["qs"][e], planes["qh"][e], grid, K)
+    if fmt == "sign1":
+        return unpack_sign1(planes["signs"][e], planes["sc"][e], K)
     raise ValueError(fmt)
+
+
+def expert_scales(fmt: str, planes: dict, e: int, K: int) -> np.ndarray:
+    """fp16 bits [N][K/256] of expert e: the per-256-block scales, or for the
+    sub-scaled sign format its per-row anchor repeated over the row's blocks."""
+    if fmt == "sign1":
+        return np.repeat(planes["d"][e][:, None], K // 256, axis=1)
+    return planes["d"][e]
 
 
 def grouped_matvec_q8(fmt, planes, grid, ids, xq_rows, xd_rows, row_of_assign, K,
@@ -54,7 +64,7 @@ def grouped_matvec_q8(fmt, planes, grid, ids, xq_rows, xd_rows, row_of_assign, K
     assigns = np.arange(A) if assign_subset is None else np.asarray(assign_subset)
     for e in np.unique(ids[assigns]):
         W = unpack_expert(fmt, planes, int(e), K, grid)[sel_rows]
-        d16 = planes["d"][int(e)][sel_rows]
+        d16 = expert_scales(fmt, planes, int(e), K)[sel_rows]
         for a in assigns[ids[assigns] == e]:
             r = row_of_assign[a]
             ya, ta, ia = matvec_q8(W, d16, xq_rows[r], xd_rows[r], want_isums)
@@ -76,7 +86,7 @@ def grouped_matvec_bf16(fmt, planes, grid, ids, x_rows_bf16, row_of_assign, K,
     assigns = np.arange(A) if assign_subset is None else np.asarray(assign_subset)
     for e in np.unique(ids[assigns]):
         W = unpack_expert(fmt, planes, int(e), K, grid)[sel_rows]
-        d16 = planes["d"][int(e)][sel_rows]
+        d16 = expert_scales(fmt, planes, int(e), K)[sel_rows]
         for a in assigns[ids[assigns] == e]:
             ya, ta = matvec_bf16(W, d16, x_rows_bf16[row_of_assign[a]])
             y[a, sel_rows] = ya

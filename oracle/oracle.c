@@ -169,6 +169,27 @@ int or_unpack_grid1(const uint8_t *qs, const uint16_t *qh, const int8_t *grid,
 }
 
 /*
+ * Sub-scaled sign unpack (1-bit sign codes with one fp16 anchor per row and a
+ * 4-bit sub-scale per 16 weights: pxq_llama README, "What's PXQ?", the PXQ1
+ * tier).  Weight c of row r is the integer
+ *   sc * (s ? -1 : +1),   s  = (signs[r][c / 8] >> (c % 8)) & 1,
+ *                         sc = (sc_bytes[r][c / 32] >> (4 * ((c / 16) % 2))) & 15,
+ * times the row's anchor, which the caller applies as the row's scale in
+ * every 256-weight block of the mat-vec.  |w| <= 15.
+ */
+int or_unpack_sign1(const uint8_t *signs, const uint8_t *sc, int64_t n, int64_t k, int8_t *w) {
+    if (k % 32 != 0) return OR_ERR_SHAPE;
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t c = 0; c < k; ++c) {
+            const unsigned s = (signs[r * (k / 8) + c / 8] >> (c % 8)) & 1u;
+            const unsigned m = (sc[r * (k / 32) + c / 32] >> (4 * ((c / 16) % 2))) & 15u;
+            w[r * k + c] = (int8_t)(s ? -(int)m : (int)m);
+        }
+    }
+    return OR_OK;
+}
+
+/*
  * Mat-vec of R unpacked weight rows w int8 [R][K] (scales d16 fp16 [R][K/256])
  * against one q8 activation row (xq int8 [K], xd float [K/32]):
  *   isum[r][s] = sum_{j<32} w[r][32s+j] * xq[32s+j]          (exact integer)

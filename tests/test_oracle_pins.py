@@ -195,7 +195,54 @@ def test_grid1_exhaustive_index_positions():
             assert np.array_equal(w[:, 256 * blk + 8 * g: 256 * blk + 8 * g + 8], grid[idx])
 
 
+def test_sign1_golden_rows():
+    g = _load("sign1_rows.json")
+    for row in g["rows"]:
+        w = oracle.unpack_sign1(np.array([row["signs"]], np.uint8), np.array([row["sc"]], np.uint8), 32)
+        assert list(w[0]) == row["w"], row
+
+
+def test_sign1_exhaustive_bytes():
+    # every sign byte at every byte position of a 32-weight block, against
+    # numpy's little-endian bit unpacking; every sub-scale byte likewise
+    for pos in range(4):
+        signs = np.zeros((256, 8), np.uint8)
+        signs[:, 4 + pos] = np.arange(256)                   # second 32-block of a 64-weight row
+        sc = np.full((256, 2), 0x57, np.uint8)               # 7 for weights 0..15 of a block, 5 for 16..31
+        w = oracle.unpack_sign1(signs, sc, 64)
+        bits = np.unpackbits(np.arange(256, dtype=np.uint8)[:, None], axis=1, bitorder="little")
+        mag = 7 if pos < 2 else 5
+        assert np.array_equal(w[:, 32 + 8 * pos: 40 + 8 * pos], np.where(bits == 1, -mag, mag))
+        assert np.array_equal(w[:, :32], np.where(np.arange(32) < 16, 7, 5)[None, :].repeat(256, 0))
+    sc = np.arange(256, dtype=np.uint8)[:, None]
+    w = oracle.unpack_sign1(np.zeros((256, 4), np.uint8), sc, 32)
+    assert np.array_equal(w[:, 0], np.arange(256) & 15) and np.array_equal(w[:, 31], np.arange(256) >> 4)
+    assert np.abs(oracle.unpack_sign1(np.full((4, 32), 255, np.uint8), np.full((4, 8), 255, np.uint8), 256)).max() == 15
+
+
+def test_sign1_matvec_closed_forms_and_dequant():
+    K = 512
+    rng = np.random.default_rng(21)
+    xq, xd = oracle.quantize_q8(wl.activations_f32(21, 1, K))
+    x = xq[0].astype(np.float64) * np.repeat(xd[0].astype(np.float64), 32)
+    one = np.full((3, K // 256), 0x3C00, np.uint16)          # anchor 1.0 in every block
+    # all signs positive, sub-scale 15: y = 15 * sum(xq * xd); all negative: the negation; sub-scale 0: 0
+    for sgn, scb, want in ((0, 0xFF, 15 * x.sum()), (255, 0xFF, -15 * x.sum()), (0x5A, 0x00, 0.0)):
+        w = oracle.unpack_sign1(np.full((3, K // 8), sgn, np.uint8), np.full((3, K // 32), scb, np.uint8), K)
+        y, t, _ = oracle.matvec_q8(w, one, xq[0], xd[0])
+        assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
+    # random planes through the MoE helper against a numpy dequantization with the row anchors
+    planes = wl.stack_experts("sign1", 21, "w", 2, 40, K)
+    ids = np.array([[1]], np.int32)
+    y, t, _ = moe.grouped_matvec_q8("sign1", planes, None, ids, xq, xd, np.array([0]), K)
+    W = oracle.unpack_sign1(planes["signs"][1], planes["sc"][1], K).astype(np.float64)
+    Wd = W * planes["d"][1].view(np.float16).astype(np.float64)[:, None]
+    assert np.all(np.abs(y[0] - Wd @ x) <= 1e-12 * t[0] + 1e-300)
+
+
 def test_packed_sizes_and_bpw():
+    # sub-scaled signs: 1 + 4/16 bits per weight plus one fp16 per row
+    assert abs(wl.packed_bytes_per_matrix("sign1", 768, 2048) * 8 / (768 * 2048) - 1.26) < 0.005
     assert wl.packed_bytes_per_matrix("ternary", 1024, 1024) == 270336
     assert wl.packed_bytes_per_matrix("ternary", 768, 2048) == 405504
     assert wl.packed_bytes_per_matrix("grid1", 1536, 4096) == 1228800

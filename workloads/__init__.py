@@ -14,6 +14,10 @@ Storage planes (structure of arrays, one contiguous plane per field):
 * grid1: ``qs`` uint8 [E][N][K/8] (low 8 bits of each 8-weight group index),
   ``qh`` uint16 [E][N][K/32] (bits 3j..3j+2 hold the high 3 index bits of group
   4i+j; bits 12..15 zero), ``d`` as above; codebook int8 [2048][8].
+* sign1 (sub-scaled sign codes): ``signs`` uint8 [E][N][K/8] (bit j of byte i
+  is the sign of weight 8i+j, 1 = negative), ``sc`` uint8 [E][N][K/32] (the
+  4-bit sub-scales of 16-weight blocks 2i and 2i+1 in the low and high nibble
+  of byte i), ``d`` uint16 [E][N] (IEEE half bits, one anchor per row).
 
 The pages (Parakon Runtime README, "How it works"; pxq_llama README, "What's
 PXQ?") describe 1-bit-class codebook and ternary expert formats without a byte
@@ -25,6 +29,8 @@ Distributions:
   grid indices i.i.d. uniform over [0, 2048); codebook entries i.i.d. uniform
   over {-1, 0, +1};
 * weight scales fp32 U(0.005, 0.05) rounded to fp16 (round to nearest even);
+  sign1: sign bits i.i.d. fair, sub-scales i.i.d. uniform over 0..15, row
+  anchors fp32 U(0.001, 0.006) rounded to fp16;
 * decode activations fp32 N(0,1), each entry independently multiplied by 20
   with probability 0.01; prefill activations bf16 = RNE(fp32 N(0,1));
 * router logits: fp32 N(0,1), fp32 U(0,1), or Zipf(1.1) with Gumbel noise
@@ -65,6 +71,10 @@ WORKLOADS = {
     # prefill: 2048 tokens through 256 grid-codebook experts, bf16 activations
     "grid1_moe_prefill_t2048": dict(kind="prefill", fmt="grid1", E=256, H=4096, I=1536,
                                     T=2048, top_k=8, logits="uniform", seed=104),
+    # sub-scaled sign codes at the 8-token grid1 decode shapes (the cost of
+    # the second, per-16 scale against grid1's single per-256 scale)
+    "sign1_moe_decode_t8": dict(kind="decode", fmt="sign1", E=256, H=4096, I=1536,
+                                T=8, top_k=8, logits="uniform", seed=107),
     # the same 2048-token batches with q8 activations (fp32 x as for decode),
     # for the exact-block-sum int8-MFMA tile path: grid1 with the prefill
     # shapes, ternary with the 64-token decode shapes and uniform routing
@@ -113,6 +123,16 @@ def grid1_expert(seed: int, tag: str, e: int, N: int, K: int):
     return qs, qh, d
 
 
+def sign1_expert(seed: int, tag: str, e: int, N: int, K: int):
+    """Sub-scaled sign planes of one expert matrix [N][K]: (signs [N][K/8], sc [N][K/32], d [N])."""
+    assert K % 256 == 0
+    rng = rng_for(seed, tag, e)
+    signs = rng.integers(0, 256, size=(N, K // 8), dtype=np.uint8)
+    sc = rng.integers(0, 256, size=(N, K // 32), dtype=np.uint8)
+    d = rng.uniform(0.001, 0.006, size=N).astype(np.float32).astype(np.float16).view(np.uint16)
+    return signs, sc, d
+
+
 def stack_experts(fmt: str, seed: int, tag: str, E: int, N: int, K: int,
                   experts=None) -> dict:
     """All planes of an [E][N][K] expert tensor.
@@ -134,6 +154,13 @@ def stack_experts(fmt: str, seed: int, tag: str, E: int, N: int, K: int,
         for e in ids:
             qs[e], qh[e], d[e] = grid1_expert(seed, tag, e, N, K)
         return dict(qs=qs, qh=qh, d=d)
+    if fmt == "sign1":
+        signs = np.zeros((E, N, K // 8), np.uint8)
+        sc = np.zeros((E, N, K // 32), np.uint8)
+        d = np.zeros((E, N), np.uint16)
+        for e in ids:
+            signs[e], sc[e], d[e] = sign1_expert(seed, tag, e, N, K)
+        return dict(signs=signs, sc=sc, d=d)
     raise ValueError(fmt)
 
 
@@ -224,6 +251,8 @@ def packed_bytes_per_matrix(fmt: str, N: int, K: int) -> int:
         return N * K // 4 + N * (K // 256) * 2
     if fmt == "grid1":
         return N * K // 8 + N * (K // 32) * 2 + N * (K // 256) * 2
+    if fmt == "sign1":
+        return N * K // 8 + N * (K // 32) + N * 2
     raise ValueError(fmt)
 
 
@@ -246,6 +275,15 @@ def torch_grid1_planes(gen, E: int, N: int, K: int, device):
     qh = torch.randint(0, 4096, (E, N, K // 32), generator=gen, device=device, dtype=torch.int32).to(torch.int16)
     d = torch_scales_f16(gen, (E, N, K // 256), device)
     return dict(qs=qs.contiguous(), qh=qh.contiguous(), d=d)
+
+
+def torch_sign1_planes(gen, E: int, N: int, K: int, device):
+    import torch
+    signs = torch.randint(0, 256, (E, N, K // 8), generator=gen, device=device, dtype=torch.int32).to(torch.uint8)
+    sc = torch.randint(0, 256, (E, N, K // 32), generator=gen, device=device, dtype=torch.int32).to(torch.uint8)
+    v = torch.rand((E, N), generator=gen, device=device, dtype=torch.float32) * 0.005 + 0.001
+    d = v.to(torch.float16).view(torch.int16).contiguous()
+    return dict(signs=signs.contiguous(), sc=sc.contiguous(), d=d)
 
 
 def torch_scales_f16(gen, shape, device):
