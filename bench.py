@@ -144,6 +144,8 @@ def main():
     for _ in range(L):
         if fmt == "ternary":
             mk = lambda n, kk: pq.TernaryWeights(**wl.torch_ternary_planes(gen, E, n, kk, dev))
+        elif fmt == "sign1":
+            mk = lambda n, kk: pq.Sign1Weights(**wl.torch_sign1_planes(gen, E, n, kk, dev))
         else:
             grid = torch.from_numpy(wl.codebook(seed)).to(dev)
             mk = lambda n, kk: pq.Grid1Weights(grid=grid, **wl.torch_grid1_planes(gen, E, n, kk, dev))
@@ -360,11 +362,11 @@ def cpu_baseline(args, cfg, layers, xs, lg, n_active, per_expert, fmt, prefill, 
         for name in ("gate", "up", "down"):
             Wt = layers[l][name]
             planes = {}
-            for f in ("qs", "qh", "d"):
+            for f in ("qs", "qh", "signs", "sc", "d"):
                 if not hasattr(Wt, f):
                     continue
                 src = getattr(Wt, f)
-                host = np.zeros(tuple(src.shape), dtype=np.uint8 if f == "qs" else np.uint16)
+                host = np.zeros(tuple(src.shape), dtype=np.uint8 if f in ("qs", "signs", "sc") else np.uint16)
                 sel = src[torch_index(touched)].cpu().numpy()
                 host[touched] = sel.view(host.dtype)
                 planes[f] = host

@@ -22,7 +22,8 @@ PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 
 
 EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
-    "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_tile_q8_ternary", "pq_moe_tile_q8_grid1",
+    "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_matvec_sign1",
+    "pq_moe_tile_q8_ternary", "pq_moe_tile_q8_grid1",
     "pq_moe_gemm_dequant_tile",
     "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1", "pq_validate_ternary",
     "pq_selftest", "pq_status_str", "pq_abi_version",
@@ -43,6 +44,11 @@ class TernaryW(ctypes.Structure):
 class Grid1W(ctypes.Structure):
     _fields_ = [("qs", ctypes.c_void_p), ("qh", ctypes.c_void_p), ("d", ctypes.c_void_p),
                 ("grid", ctypes.c_void_p),
+                ("n_experts", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class Sign1W(ctypes.Structure):
+    _fields_ = [("signs", ctypes.c_void_p), ("sc", ctypes.c_void_p), ("d", ctypes.c_void_p),
                 ("n_experts", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
 
 
@@ -72,6 +78,9 @@ def _load():
                                   ctypes.POINTER(Groups), p, p, i32, i32, p, p,
                                   ctypes.POINTER(Debug), p],
         "pq_moe_matvec_grid1": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
+                                ctypes.POINTER(Groups), p, p, i32, i32, p, p,
+                                ctypes.POINTER(Debug), p],
+        "pq_moe_matvec_sign1": [ctypes.POINTER(Sign1W), ctypes.POINTER(Sign1W),
                                 ctypes.POINTER(Groups), p, p, i32, i32, p, p,
                                 ctypes.POINTER(Debug), p],
         "pq_moe_tile_q8_ternary": [ctypes.POINTER(TernaryW), ctypes.POINTER(TernaryW),
@@ -164,6 +173,27 @@ class TernaryWeights:
         _dt(self.d, torch.int16, torch.float16, torch.uint16)
         E, rows, cols = self.shape
         return TernaryW(_ptr(self.qs), _ptr(self.d), E, rows, cols)
+
+
+@dataclass
+class Sign1Weights:
+    """Sub-scaled sign expert tensor: signs uint8 [E][rows][cols/8], sc uint8
+    [E][rows][cols/32] (4-bit sub-scales), d fp16 bits [E][rows] (row anchors)."""
+    signs: torch.Tensor
+    sc: torch.Tensor
+    d: torch.Tensor
+
+    @property
+    def shape(self):
+        E, rows, q = self.signs.shape
+        return E, rows, q * 8
+
+    def cstruct(self) -> Sign1W:
+        _dt(self.signs, torch.uint8)
+        _dt(self.sc, torch.uint8)
+        _dt(self.d, torch.int16, torch.float16, torch.uint16)
+        E, rows, cols = self.shape
+        return Sign1W(_ptr(self.signs), _ptr(self.sc), _ptr(self.d), E, rows, cols)
 
 
 @dataclass
@@ -313,6 +343,12 @@ def moe_matvec_grid1(w: Grid1Weights, w_up, groups: GroupBuffers, xq, xd, act_by
                      epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
     """pq_moe_matvec_grid1 (see include/pq.h)."""
     return _matvec("pq_moe_matvec_grid1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
+
+
+def moe_matvec_sign1(w: Sign1Weights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,
+                     epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
+    """pq_moe_matvec_sign1 (see include/pq.h)."""
+    return _matvec("pq_moe_matvec_sign1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
 
 
 def moe_tile_q8_ternary(w: TernaryWeights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,

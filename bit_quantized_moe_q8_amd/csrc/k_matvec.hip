@@ -45,6 +45,17 @@
 // group's 11-bit index selects one 8-byte row (ds_read_b64) and two
 // v_dot4_i32_i8 accumulate its products.
 //
+// Sub-scaled sign arithmetic (1-bit sign codes, a 4-bit sub-scale per 16
+// weights and one fp16 anchor per row: pxq_llama README, "What's PXQ?",
+// PXQ1).  Each sign byte selects one 8-byte row of the 256 +-1 patterns,
+// built in LDS at kernel start; two v_dot4_i32_i8 per byte give the +-1 sum
+// of 8 weights, and the two 16-weight sums of a q8 block combine with their
+// sub-scales in integer arithmetic (sc_lo * s_lo + sc_hi * s_hi, exact), so
+// the per-block int32 sums and everything after them are those of the other
+// formats, with the row's anchor as the scale of every block.  The sub-scale
+// multiply-add is the second scale step the pages measure against
+// single-scale blocks.
+//
 // Scale application in fp32: partial = d_w * (sum over the lane's blocks of
 // xd * isum), then the cross-lane sum.
 #include "pq_device.hpp"
@@ -76,11 +87,17 @@ struct FmtInfo<kGrid1> {
     static constexpr int kChunkWeights = 128;  // 16 group indices (low bytes)
     static constexpr int kSubs = 4;
 };
+template <>
+struct FmtInfo<kSign1> {
+    static constexpr int kChunkWeights = 128;  // 16 sign bytes
+    static constexpr int kSubs = 4;
+};
+constexpr int kSignPatterns = 256;
 
 // One lane's packed weights of one row iteration.
 struct WRow {
     uint4 q;      // 16 bytes of qs
-    uint2 h;      // grid1: the 4 qh words of the chunk
+    uint2 h;      // grid1: the 4 qh words of the chunk; sign1: h.x = 4 sub-scale bytes
     uint32_t d;   // fp16 scale bits
 };
 
@@ -109,7 +126,7 @@ constexpr int kGrid1WavesPerSimd = 3;
 
 template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((FMT == kGrid1 && MT == 1 && !DBG) ? kGrid1WavesPerSimd : 1)))
+__attribute__((amdgpu_waves_per_eu((FMT != kTernary && MT == 1 && !DBG) ? kGrid1WavesPerSimd : 1)))
 void k_matvec(ExpertArgs p) {
     using FI = FmtInfo<FMT>;
     constexpr int LS = RowGeom<LPR>::LS;
@@ -123,7 +140,7 @@ void k_matvec(ExpertArgs p) {
     constexpr int SUBS = FI::kSubs;
     constexpr int ACT_DW = FI::kChunkWeights / 4;  // activation dwords per chunk
 
-    __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : 1];
+    __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : (FMT == kSign1) ? kSignPatterns : 1];
     __shared__ float s_gu[NMAT][MT][TR];
     __shared__ int s_apre[SPLIT ? kMaxExperts + 1 : 1];   // first group number per slot
     __shared__ int s_scan[kWaves + 1];
@@ -141,6 +158,18 @@ void k_matvec(ExpertArgs p) {
         const uint4* src = reinterpret_cast<const uint4*>(p.grid);
         uint4* dst = reinterpret_cast<uint4*>(s_grid);
         for (int i = tid; i < kGridEntries / 2; i += kThreads) dst[i] = src[i];
+    }
+    if constexpr (FMT == kSign1) {
+        // pattern i: byte j is -1 where bit j of i is set, else +1
+        for (int i = tid; i < kSignPatterns; i += kThreads) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo |= (((i >> j) & 1) ? 0xFFu : 0x01u) << (8 * j);
+                hi |= (((i >> (j + 4)) & 1) ? 0xFFu : 0x01u) << (8 * j);
+            }
+            s_grid[i] = make_uint2(lo, hi);
+        }
     }
 
     // Item count.  SPLIT: slot s owns ceil(m_s / MT) assignment groups,
@@ -171,8 +200,8 @@ void k_matvec(ExpertArgs p) {
     const int n_items = n_groups * tiles;
 
     const int64_t qs_row_bytes = (FMT == kTernary) ? cols / 4 : cols / 8;
-    const int64_t qh_row = cols / 32;
-    const int64_t d_row = cols / 256;
+    const int64_t qh_row = cols / 32;                      // grid1 qh words; sign1 sub-scale bytes
+    const int64_t d_row = (FMT == kSign1) ? 1 : cols / 256;
     const int64_t qs_e = static_cast<int64_t>(rows) * qs_row_bytes;
     const int64_t qh_e = static_cast<int64_t>(rows) * qh_row;
     const int64_t d_e = static_cast<int64_t>(rows) * d_row;
@@ -211,6 +240,11 @@ void k_matvec(ExpertArgs p) {
             w.h = *reinterpret_cast<const uint2*>(
                 qhb + static_cast<uint32_t>(nc * static_cast<int>(qh_row) + cc * 4));
             w.d = db[static_cast<uint32_t>(nc * static_cast<int>(d_row) + cc / 2)];
+        } else if constexpr (FMT == kSign1) {
+            const uint8_t* scb = ((NMAT == 2 && mat == 1) ? p.sc[1] : p.sc[0]) + e * qh_e;
+            w.h = make_uint2(*reinterpret_cast<const uint32_t*>(
+                                 scb + static_cast<uint32_t>(nc * static_cast<int>(qh_row) + cc * 4)), 0u);
+            w.d = db[static_cast<uint32_t>(nc)];
         } else {
             w.h = make_uint2(0, 0);
             w.d = db[static_cast<uint32_t>(nc * static_cast<int>(d_row) + cc / 4)];
@@ -337,6 +371,34 @@ void k_matvec(ExpertArgs p) {
                             for (int j = 0; j < MT; ++j)
                                 isum[j][i >> 1] = dot4(wdec[s], static_cast<int>(act[j][4 * i + s]),
                                                        isum[j][i >> 1]);
+                    }
+                } else if constexpr (FMT == kSign1) {
+                    // per 16 weights: the +-1 sum (two sign bytes), then
+                    // times its sub-scale into the q8 block's sum
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        uint2 pat[8];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int gi = 8 * hf + q;
+                            pat[q] = s_grid[(wv[gi >> 2] >> (8 * (gi & 3))) & 0xffu];
+                        }
+#pragma unroll
+                        for (int sub = 0; sub < 4; ++sub) {   // 16-weight blocks of this half
+                            const int sb16 = 4 * hf + sub;     // 0..7 in the chunk
+                            const uint32_t scv = (cur.h.x >> (4 * sb16)) & 15u;
+#pragma unroll
+                            for (int j = 0; j < MT; ++j) {
+                                int s16 = 0;
+#pragma unroll
+                                for (int q = 2 * sub; q < 2 * sub + 2; ++q) {
+                                    const int gi = 8 * hf + q;
+                                    s16 = dot4(static_cast<int>(pat[q].x), static_cast<int>(act[j][2 * gi]), s16);
+                                    s16 = dot4(static_cast<int>(pat[q].y), static_cast<int>(act[j][2 * gi + 1]), s16);
+                                }
+                                isum[j][sb16 >> 1] += static_cast<int>(scv) * s16;
+                            }
+                        }
                     }
                 } else {
                     const uint32_t hv[2] = {cur.h.x, cur.h.y};
@@ -536,7 +598,7 @@ hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
 }  // namespace
 
 bool matvec_supported(Fmt fmt, int cols) {
-    const int cw = (fmt == kTernary) ? 64 : 128;
+    const int cw = (fmt == kTernary) ? 64 : 128;   // grid1 and sign1: 128
     if (cols % 256 != 0) return false;
     switch (cols / cw) {
         case 2: case 4: case 8: case 12: case 16: case 24: case 32: case 48: case 64: return true;
@@ -551,12 +613,13 @@ hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
     const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
     ExpertArgs m = a;
     m.heavy_min = 0;
-    if (a.n_tokens >= kHeavyMin && A > a.n_experts && tile_q8_supported(a.cols)) {
+    if (fmt != kSign1 && a.n_tokens >= kHeavyMin && A > a.n_experts && tile_q8_supported(a.cols)) {
         m.heavy_min = kHeavyMin;
         const hipError_t err = launch_tile_q8(fmt, epi, m, s);
         if (err != hipSuccess) return err;
     }
     if (fmt == kTernary) return launch_fmt<kTernary>(epi, m, s);
+    if (fmt == kSign1) return launch_fmt<kSign1>(epi, m, s);
     return launch_fmt<kGrid1>(epi, m, s);
 }
 

@@ -265,9 +265,52 @@ pq_status grid1_args(const pq_grid1_w* w, const pq_grid1_w* w_up, const pq_group
     return PQ_OK;
 }
 
+pq_status sign1_args(const pq_sign1_w* w, const pq_sign1_w* w_up, const pq_groups* g,
+                     const int8_t* xq, const float* xd, int32_t act_by_token, int32_t epilogue,
+                     void* out0, void* out1, const pq_debug* dbg, pqk::ExpertArgs& a, bool* run) {
+    *run = false;
+    if (!w || !w->signs || !w->sc || !w->d) return PQ_ERR_NULL;
+    pq_status st = check_groups(g);
+    if (st != PQ_OK) return st;
+    if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
+    if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, true)) != PQ_OK)
+        return st;
+    if (epilogue == PQ_EPI_F32_COMBINE && act_by_token) return PQ_ERR_UNSUPPORTED;
+    if (epilogue == PQ_EPI_SWIGLU_Q8) {
+        if (!w_up->signs || !w_up->sc || !w_up->d) return PQ_ERR_NULL;
+        if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
+            return PQ_ERR_SHAPE;
+        if (!aligned(w_up->signs, 16) || !aligned(w_up->sc, 4) || !aligned(w_up->d, 2))
+            return PQ_ERR_ALIGN;
+    }
+    if (!aligned(w->signs, 16) || !aligned(w->sc, 4) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+    if (!pqk::matvec_supported(pqk::kSign1, w->cols)) return PQ_ERR_UNSUPPORTED;
+    if (g->n_tokens == 0) return PQ_OK;
+    if (!xq || !xd) return PQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
+    a = pqk::ExpertArgs{};
+    a.qs[0] = w->signs;
+    a.sc[0] = w->sc;
+    a.d[0] = w->d;
+    a.qs[1] = w_up ? w_up->signs : nullptr;
+    a.sc[1] = w_up ? w_up->sc : nullptr;
+    a.d[1] = w_up ? w_up->d : nullptr;
+    a.rows = w->rows;
+    a.cols = w->cols;
+    fill_groups(a, g);
+    a.act_by_token = act_by_token ? 1 : 0;
+    a.xq = xq;
+    a.xd = xd;
+    a.out0 = out0;
+    a.out1 = out1;
+    fill_debug(a, dbg);
+    *run = true;
+    return PQ_OK;
+}
+
 pq_status launch_matvec_any(pqk::Fmt fmt, int32_t epilogue, const pqk::ExpertArgs& a,
                             const pq_debug* dbg, pq_stream stream) {
-    if (a.n_tokens == 1 && !dbg)
+    if (a.n_tokens == 1 && !dbg && fmt != pqk::kSign1)
         return from_hip(pqk::launch_matvec_tok1(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
     return from_hip(pqk::launch_matvec(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
 }
@@ -392,6 +435,19 @@ pq_status pq_moe_matvec_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, const
                                         pqk::matvec_supported, a, &run);
         if (st != PQ_OK || !run) return st;
         return launch_matvec_any(pqk::kGrid1, epilogue, a, dbg, stream);
+    });
+}
+
+pq_status pq_moe_matvec_sign1(const pq_sign1_w* w, const pq_sign1_w* w_up, const pq_groups* g,
+                              const int8_t* xq, const float* xd, int32_t act_by_token,
+                              int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
+                              pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        pqk::ExpertArgs a;
+        bool run;
+        const pq_status st = sign1_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg, a, &run);
+        if (st != PQ_OK || !run) return st;
+        return launch_matvec_any(pqk::kSign1, epilogue, a, dbg, stream);
     });
 }
 

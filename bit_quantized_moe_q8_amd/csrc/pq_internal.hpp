@@ -35,14 +35,15 @@ hipError_t launch_validate_ternary(const uint8_t* qs, int64_t n_bytes, int32_t* 
 hipError_t launch_combine(const float* out, const float* w, int n_tokens, int top_k, int rows,
                           float* y, hipStream_t s);
 
-enum Fmt { kTernary = 0, kGrid1 = 1 };
+enum Fmt { kTernary = 0, kGrid1 = 1, kSign1 = 2 };
 enum Epi { kEpiF32 = 0, kEpiSwigluQ8 = 1, kEpiSwigluBf16 = 2, kEpiF32Combine = 3 };
 
 // Everything an expert kernel needs; index 0 is `w`, index 1 is `w_up`.
 struct ExpertArgs {
     const uint8_t* qs[2];
     const uint16_t* qh[2];
-    const uint16_t* d[2];
+    const uint16_t* d[2];   // sign1: one anchor per row
+    const uint8_t* sc[2];   // sign1: 4-bit sub-scales, two per byte
     const int8_t* grid;
     int rows, cols, n_experts;
     const int32_t* offsets;

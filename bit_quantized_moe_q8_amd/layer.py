@@ -22,9 +22,9 @@ from __future__ import annotations
 import torch
 
 from . import (PQ_EPI_F32, PQ_EPI_F32_COMBINE, PQ_EPI_SWIGLU_BF16, PQ_EPI_SWIGLU_Q8,
-               GroupBuffers, Grid1Weights, TernaryWeights, decode_prep, decode_prep_supported,
+               GroupBuffers, Grid1Weights, Sign1Weights, TernaryWeights, decode_prep, decode_prep_supported,
                group_tokens_by_expert, moe_combine, moe_decode1_gate_up, moe_gemm_dequant_tile,
-               moe_matvec_grid1, moe_matvec_ternary, moe_route_topk, quantize_act_q8)
+               moe_matvec_grid1, moe_matvec_sign1, moe_matvec_ternary, moe_route_topk, quantize_act_q8)
 
 # When the decode layer fuses the prep kernels (tokens x experts up to one
 # key per thread of the fused kernel), and the combine into the down mat-vec
@@ -52,7 +52,8 @@ class DecodeLayer:
         self.fused_combine = self.fused and bool(fused_combine)
         if decode1 is None:
             decode1 = self.fused_combine
-        self.decode1 = bool(decode1) and n_tokens == 1
+        # (the routed one-token launch exists for the ternary and grid1 formats)
+        self.decode1 = bool(decode1) and n_tokens == 1 and fmt != "sign1"
         A = n_tokens * top_k
         f32, i8 = torch.float32, torch.int8
         self.use_state(self.new_route_state())
@@ -60,7 +61,7 @@ class DecodeLayer:
         self.hd = torch.empty((A, inter // 32), dtype=f32, device=device)
         self.out = torch.empty((A, hidden), dtype=f32, device=device)
         self.y = torch.empty((n_tokens, hidden), dtype=f32, device=device)
-        self._mv = moe_matvec_ternary if fmt == "ternary" else moe_matvec_grid1
+        self._mv = {"ternary": moe_matvec_ternary, "grid1": moe_matvec_grid1, "sign1": moe_matvec_sign1}[fmt]
 
     def new_route_state(self) -> dict:
         """A separate set of q8 / routing / grouping buffers."""
@@ -165,4 +166,6 @@ def weights_to_device(fmt: str, planes: dict, grid=None, device="cuda"):
 
     if fmt == "ternary":
         return TernaryWeights(t(planes["qs"]), t(planes["d"]))
+    if fmt == "sign1":
+        return Sign1Weights(t(planes["signs"]), t(planes["sc"]), t(planes["d"]))
     return Grid1Weights(t(planes["qs"]), t(planes["qh"]), t(planes["d"]), t(grid))

@@ -100,6 +100,21 @@ typedef struct pq_grid1_w {
     int32_t n_experts, rows, cols;
 } pq_grid1_w;
 
+/* Sub-scaled sign expert tensor [n_experts][rows][cols] (1-bit sign codes, a
+   4-bit sub-scale per 16 weights, one fp16 anchor per row: pxq_llama README,
+   "What's PXQ?", the PXQ1 tier).  signs uint8 [E][rows][cols/8]: bit j of
+   byte i is the sign of weight 8i+j (1 = negative); sc uint8
+   [E][rows][cols/32]: byte i holds the sub-scales (0..15) of weights 32i..
+   32i+15 (low nibble) and 32i+16..32i+31 (high nibble); d fp16 bits
+   [E][rows]: the row's anchor.  Weight = d * sc * (+-1).  signs 16-byte, sc
+   4-byte, d 2-byte aligned. */
+typedef struct pq_sign1_w {
+    const uint8_t *signs;
+    const uint8_t *sc;
+    const uint16_t *d;
+    int32_t n_experts, rows, cols;
+} pq_sign1_w;
+
 /* Output of pq_group_tokens_by_expert, consumed by the expert kernels. */
 typedef struct pq_groups {
     const int32_t *expert_offsets; /* [n_experts+1] */
@@ -217,6 +232,19 @@ pq_status pq_moe_matvec_ternary(const pq_ternary_w *w, const pq_ternary_w *w_up,
  * {2,4,8,12,16,24,32,48,64} (cols 256..8192).
  */
 pq_status pq_moe_matvec_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
+                              const pq_groups *g, const int8_t *xq, const float *xd,
+                              int32_t act_by_token, int32_t epilogue, void *out0,
+                              void *out1, const pq_debug *dbg, pq_stream stream);
+
+/*
+ * The same over sub-scaled sign weights (pq_sign1_w): the 16-weight +-1 sums
+ * times their sub-scales give the exact int32 sum of each q8 block, and the
+ * row's anchor is the scale of every block, so the outputs are those of the
+ * other formats' definition with w = d * sc * (+-1).  cols % 256 == 0 and
+ * cols/128 in {2,4,8,12,16,24,32,48,64} (cols 256..8192).  Every token count
+ * runs the grouped mat-vec (no one-token or tile variant for this format).
+ */
+pq_status pq_moe_matvec_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                               const pq_groups *g, const int8_t *xq, const float *xd,
                               int32_t act_by_token, int32_t epilogue, void *out0,
                               void *out1, const pq_debug *dbg, pq_stream stream);

@@ -116,6 +116,22 @@ def test_grid1_validation(L):
     assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 64, 2560)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_UNSUPPORTED
 
 
+def test_sign1_validation(L):
+    import bit_quantized_moe_q8_amd as pq
+    f = L.pq_moe_matvec_sign1
+    b = ctypes.byref
+    g = _groups(pq)
+    ok_w = pq.Sign1W(A16, A16, A16, 8, 64, 1024)
+    assert f(b(pq.Sign1W(A16, None, A16, 8, 64, 1024)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_NULL
+    assert f(b(pq.Sign1W(A16, A16, A16, 8, 64, 1000)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_SHAPE
+    assert f(b(pq.Sign1W(A16, A1, A16, 8, 64, 1024)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_ALIGN
+    assert f(b(pq.Sign1W(A1, A16, A16, 8, 64, 1024)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_ALIGN
+    assert f(b(pq.Sign1W(A16, A16, A16, 8, 64, 2560)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_UNSUPPORTED
+    assert f(b(ok_w), None, b(g), A16, A16, 1, 1, A16, A16, None, S) == pq.PQ_ERR_NULL
+    assert f(b(ok_w), b(ok_w), b(g), A16, A16, 1, 2, A16, A16, None, S) == pq.PQ_ERR_UNSUPPORTED
+    assert f(b(ok_w), None, b(_groups(pq, T=0)), None, None, 1, 0, A16, None, None, S) == pq.PQ_OK
+
+
 def test_tile_q8_validation(L):
     """The int8-MFMA tile entry points share the mat-vec's checks but accept
     any cols that is a multiple of 256 (e.g. 1280, which the mat-vec rejects)."""

@@ -138,7 +138,7 @@ def _single(fmt, E, N, K, T, k, act_by_token, seed, want_dbg=True, ids=None):
     W = weights_to_device(fmt, planes, grid)
     A = T * k
     isums = torch.zeros((A, N, K // 32), dtype=torch.int32, device=dev()) if want_dbg else None
-    mv = pq.moe_matvec_ternary if fmt == "ternary" else pq.moe_matvec_grid1
+    mv = {"ternary": pq.moe_matvec_ternary, "grid1": pq.moe_matvec_grid1, "sign1": pq.moe_matvec_sign1}[fmt]
     out, _ = mv(W, None, g, to_dev(xq), to_dev(xd), act_by_token, pq.PQ_EPI_F32,
                 dbg={"isums": isums} if want_dbg else None)
     rows_of = (np.arange(A) // k) if act_by_token else np.arange(A)
@@ -185,6 +185,11 @@ def test_ternary_matvec_1024_single_matrix():
     ("ternary", 4, 33, 3072, 2, 2, False),    # 48 chunks per row
     ("grid1", 8, 40, 3072, 3, 2, True),       # 24 chunks per row
     ("grid1", 4, 20, 6144, 2, 2, False),      # 48 chunks per row
+    ("sign1", 4, 96, 256, 1, 2, True),        # sub-scaled signs: 2 lanes per row
+    ("sign1", 8, 40, 1536, 3, 2, False),
+    ("sign1", 16, 50, 4096, 9, 4, True),      # pairs of assignments per pass
+    ("sign1", 8, 64, 1024, 40, 3, True),      # split groups of assignments
+    ("sign1", 4, 20, 6144, 2, 2, False),      # 48 chunks per row
 ])
 def test_grouped_matvec(fmt, E, N, K, T, k, abt):
     say("matvec", fmt, E, N, K, T, k, abt)
@@ -210,6 +215,8 @@ def test_matvec_one_expert_many_tokens():
     ("ternary", 1536, 8, True),    # 24 lanes per row
     ("grid1", 3072, 4, False),
     ("grid1", 6144, 2, True),      # 48 lanes per row
+    ("sign1", 2048, 8, True),      # (the grouped kernel at one token)
+    ("sign1", 1536, 8, False),
 ])
 def test_matvec_one_token(fmt, K, k, abt):
     """The one-token production kernel (no debug outputs), ragged row tiles."""
@@ -361,6 +368,9 @@ def _check_layer(inp, gpu):
     ("ternary_moe_decode_t1", dict(T=4, E=16, H=768, I=256, top_k=4), True),
     ("grid1_moe_decode_t8", dict(T=3, E=8, H=1024, I=512, top_k=2), False),
     ("grid1_moe_decode_t8", dict(T=16, E=256, H=1024, I=256, top_k=16), True),
+    ("sign1_moe_decode_t8", {}, False),
+    ("sign1_moe_decode_t8", dict(T=1, E=64, H=2048, I=1536, top_k=8), True),
+    ("sign1_moe_decode_t8", dict(T=48, E=16, H=1024, I=512, top_k=4), False),
 ])
 def test_decode_layer(name, override, fused):
     say("decode layer", name, override, "fused" if fused else "separate")
