@@ -378,6 +378,45 @@ def test_decode_layer(name, override, fused):
     _check_layer(inp, gpu)
 
 
+def test_one_token_layer_in_captured_graph():
+    """The one-token layer (two launches: routed gate/up, down with the fused
+    combine) captured in a graph and replayed three times, with eager steps
+    on other inputs between the replays: routing, q8(h) and y of every replay
+    match the oracle (y within tolerance: the fused combine adds the top-k
+    terms with atomics, so its last bits can differ between runs)."""
+    say("one-token layer in graph")
+    inp = decode_inputs("ternary_moe_decode_t1")
+    cfg = inp["cfg"]
+    T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
+    layer = DecodeLayer("ternary", T, H, I, E, k, dev())
+    assert layer.decode1
+    W = {n: weights_to_device("ternary", inp[n]) for n in ("gate", "up", "down")}
+    x, logits = to_dev(inp["x"]), to_dev(inp["logits"])
+    other_x = to_dev(wl.activations_f32(77, T, H))
+    other_lg = to_dev(wl.router_logits(77, T, E, "normal"))
+    ref = moe.decode_ffn(inp, want_isums=False)
+    layer(x, logits, W["gate"], W["up"], W["down"])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x, logits, W["gate"], W["up"], W["down"])
+    for rep in range(3):
+        layer(other_x, other_lg, W["gate"], W["up"], W["down"])   # eager step on other inputs
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_equal(to_host(layer.ids), ref["ids"], "ids (replay %d)" % rep)
+        hq, hd = to_host(layer.hq), to_host(layer.hd)
+        ok = q8_rows_equal_ignoring_ties(hq, ref["hq"], ref["h"], ref["hd"])
+        assert ok.all(), "q8(h) (replay %d)" % rep
+        o_ref, to, _ = moe.grouped_matvec_q8("ternary", inp["down"], None, ref["ids"], hq, hd,
+                                             np.arange(T * k), I, want_isums=False)
+        w = to_host(layer.w)
+        y_ref, ty = oracle.combine(o_ref.astype(np.float32), w, k)
+        ty = ty + np.einsum("tj,tjn->tn", np.abs(w.astype(np.float64)), to.reshape(T, k, H))
+        assert_tol(to_host(layer.y), y_ref, ty, "y (replay %d)" % rep)
+
+
 def _prep_case(T, E, H, k, logits=None, seed=0):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((T, H)).astype(np.float32)
