@@ -70,10 +70,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kTileRows = 32;      // q8 block of the SwiGLU epilogue; tiles are 1, 2 or 4 of these
 constexpr int kMaxTileShift = 2;
 constexpr int kDepth = 4;          // row iterations of weight loads in flight per wave
-#ifndef PQ_HEAVY_MIN
-#define PQ_HEAVY_MIN 8
-#endif
-constexpr int kHeavyMin = PQ_HEAVY_MIN;   // assignments from which an expert goes to the MFMA tile
+// Assignments from which an expert goes to the int8-MFMA tile kernel
+// (measured on the skewed 64-token decode: 6 and 8 best, 4 and 16 slower).
+constexpr int kHeavyMin = 8;
 
 template <int FMT>
 struct FmtInfo;
@@ -565,17 +564,15 @@ hipError_t launch_epi(Epi epi, const ExpertArgs& a, hipStream_t s) {
 template <int FMT, int LPR>
 hipError_t launch_mt(Epi epi, const ExpertArgs& a, hipStream_t s) {
     // One token: every expert sees one activation row.  Up to one assignment
-    // per expert on average: pairs (single rows for grid1, whose codebook
-    // decode already holds more registers), passes repeated for the rare
+    // per expert on average: pairs (single rows for grid1 and sign1, whose
+    // table lookups already hold more registers), passes repeated for the rare
     // heavier expert.  Otherwise pairs of assignments, each its own work item
     // (measured faster than groups of four or eight on the skewed 64-token
     // decode: fewer idle dot products for the many one-assignment experts).
     const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
     if (a.n_tokens <= 1) return launch_epi<FMT, LPR, 1, false>(epi, a, s);
-#ifndef PQ_MT_PAIR
-#define PQ_MT_PAIR (FMT == kGrid1 ? 1 : 2)
-#endif
-    if (A <= a.n_experts) return launch_epi<FMT, LPR, PQ_MT_PAIR, false>(epi, a, s);
+    constexpr int kMtPair = (FMT == kTernary) ? 2 : 1;
+    if (A <= a.n_experts) return launch_epi<FMT, LPR, kMtPair, false>(epi, a, s);
     return launch_epi<FMT, LPR, 2, true>(epi, a, s);
 }
 
