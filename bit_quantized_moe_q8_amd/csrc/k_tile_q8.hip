@@ -15,10 +15,10 @@
 // both as explicit fused multiply-adds, so every build of the kernel (with
 // or without its debug outputs) rounds the same way.
 //
-// Work item: (expert, chunk of up to 64 of its assignments, tile of 64
-// physical weight rows: 32 gate + 32 up rows for the SwiGLU epilogue, else 64
-// rows).  Wave w owns 16 of the 64 rows (the A operand) and all live 16-column
-// assignment subtiles (the B operand).  The K loop runs over 256-weight
+// Work item: (expert, chunk of up to 64 of its assignments (32 for small
+// batches), tile of 64 physical weight rows: 32 gate + 32 up rows for the
+// SwiGLU epilogue, else 64 rows).  Wave w owns 16 of the 64 rows (the A
+// operand) and all live 16-column assignment subtiles (the B operand).  The K loop runs over 256-weight
 // slabs: each lane loads its own weight row's packed slab straight into
 // registers one slab ahead, while the workgroup stages the chunk's q8
 // activations and scales for the next slab into LDS.
@@ -51,12 +51,15 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTok = 64;          // assignments per item: up to four 16-column subtiles
-constexpr int kSub = 16;
-constexpr int kJMax = kTok / kSub;
+constexpr int kSub = 16;          // assignments per MFMA column subtile
 constexpr int kSlabK = 256;       // weights per slab: one weight-scale block
 constexpr int kSlabBlocks = kSlabK / 32;
 constexpr int kRows = 64;         // physical weight rows per item, 16 per wave
+// Chunks of up to 64 assignments (four column subtiles) at two waves per
+// SIMD for large batches; of up to 32 at three waves per SIMD (fewer
+// registers and LDS) when the batch is small and the few heavy experts'
+// items are latency-bound.
+constexpr int kSmallChunkMaxAssign = 2048;
 
 template <int FMT>
 struct TileFmt;
@@ -69,8 +72,14 @@ struct TileFmt<kGrid1> {
     static constexpr int kWords = 3;   // 32 bytes of qs, then 16 bytes of qh
 };
 
-template <int FMT, int EPI, bool DBG>
-__global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
+template <int FMT, int EPI, bool DBG, int TOK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((TOK == 32 && !DBG) ? 3 : 1)))
+void k_tile_q8(ExpertArgs p) {
+    constexpr int kTok = TOK;                 // assignments per item
+    constexpr int kJMax = kTok / kSub;        // column subtiles
+    // (column, block) pairs of a slab's activation staging per thread
+    constexpr int kStagePairs = kTok * kSlabBlocks / kThreads;
+    static_assert(kStagePairs * kThreads == kTok * kSlabBlocks, "staging covers every (column, block) pair once");
     constexpr int NMAT = (EPI == kEpiSwigluQ8) ? 2 : 1;
     constexpr int TR = kRows / NMAT;   // output rows per item
     constexpr int KW = TileFmt<FMT>::kWords;
@@ -178,16 +187,16 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
             }
         };
 
-        // ---- staging of a slab: thread (column c, block q) for two (c, q)
-        // pairs moves the 32 activation bytes of block q and its scale; the
+        // ---- staging of a slab: thread (column c, block q) for kStagePairs
+        // (c, q) pairs moves the 32 activation bytes of block q and its scale; the
         // first 64 threads also move one weight scale
-        uint4 xr[2][2];
-        float xdr[2];
+        uint4 xr[kStagePairs][2];
+        float xdr[kStagePairs];
         uint32_t dr = 0;   // fp16 bits: converted only when stored, so that no
                            // instruction waits on the loads before the compute
         auto sload = [&](int sb) {
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < kStagePairs; ++k) {
                 const int pair = tid + kThreads * k;
                 const int c = pair >> 3, q = pair & 7;
                 const int64_t row = s_arow[c];
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
         };
         auto sstore = [&](int sl) {
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < kStagePairs; ++k) {
                 const int pair = tid + kThreads * k;
                 const int c = pair >> 3, q = pair & 7;
                 uint2* dst = &s_x[sl][c * kXStride + 4 * q];
@@ -329,11 +338,18 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
                 wload(sb + 1, wn);
                 sload(sb + 1);
             }
-            switch (jn) {
-                case 1: compute(std::integral_constant<int, 1>{}, sl, wc, sb); break;
-                case 2: compute(std::integral_constant<int, 2>{}, sl, wc, sb); break;
-                case 3: compute(std::integral_constant<int, 3>{}, sl, wc, sb); break;
-                default: compute(std::integral_constant<int, 4>{}, sl, wc, sb); break;
+            if constexpr (kJMax == 2) {
+                if (jn == 1)
+                    compute(std::integral_constant<int, 1>{}, sl, wc, sb);
+                else
+                    compute(std::integral_constant<int, 2>{}, sl, wc, sb);
+            } else {
+                switch (jn) {
+                    case 1: compute(std::integral_constant<int, 1>{}, sl, wc, sb); break;
+                    case 2: compute(std::integral_constant<int, 2>{}, sl, wc, sb); break;
+                    case 3: compute(std::integral_constant<int, 3>{}, sl, wc, sb); break;
+                    default: compute(std::integral_constant<int, 4>{}, sl, wc, sb); break;
+                }
             }
             if (more) {
                 sstore(sl ^ 1);
@@ -397,27 +413,30 @@ __global__ __launch_bounds__(kThreads) void k_tile_q8(ExpertArgs p) {
     }
 }
 
-template <int FMT, int EPI, bool DBG>
+template <int FMT, int EPI, bool DBG, int TOK>
 hipError_t launch_one(const ExpertArgs& a, hipStream_t s) {
     constexpr int TR = kRows / ((EPI == kEpiSwigluQ8) ? 2 : 1);
     // Upper bound of the chunks: sum over the taking-part experts of
-    // ceil(m / kTok) <= A / kTok + (number of such experts).
+    // ceil(m / TOK) <= A / TOK + (number of such experts).
     const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
     const int64_t hmin = a.heavy_min > 0 ? a.heavy_min : 1;
     int64_t heavy = A / hmin;
     if (heavy > a.n_experts) heavy = a.n_experts;
-    const int64_t chunks = A / kTok + heavy + 1;
+    const int64_t chunks = A / TOK + heavy + 1;
     const int64_t items = chunks * ((a.rows + TR - 1) / TR);
     const int64_t cap = static_cast<int64_t>(cu_count()) * 4;
     int64_t grid = items < cap ? items : cap;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_tile_q8<FMT, EPI, DBG>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_tile_q8<FMT, EPI, DBG, TOK>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 template <int FMT, int EPI>
 hipError_t launch_dbg(const ExpertArgs& a, hipStream_t s) {
-    return a.debug ? launch_one<FMT, EPI, true>(a, s) : launch_one<FMT, EPI, false>(a, s);
+    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    if (A <= kSmallChunkMaxAssign)
+        return a.debug ? launch_one<FMT, EPI, true, 32>(a, s) : launch_one<FMT, EPI, false, 32>(a, s);
+    return a.debug ? launch_one<FMT, EPI, true, 64>(a, s) : launch_one<FMT, EPI, false, 64>(a, s);
 }
 
 template <int FMT>

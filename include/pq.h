@@ -259,7 +259,8 @@ pq_status pq_moe_matvec_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
  * scaled in fp32 as sum over 256-blocks of d * (sum over 32-blocks of
  * xd * isum).  Only the fp32 summation order differs, within the tolerance
  * of the fp32 result.  Every active expert is processed in chunks of up to
- * 32 assignments and tiles of 64 weight rows (32 gate + 32 up rows for
+ * 32 assignments (batches of at most 2048 assignments) or 64 (larger
+ * batches), and tiles of 64 weight rows (32 gate + 32 up rows for
  * PQ_EPI_SWIGLU_Q8).  cols % 256 == 0 (any such cols); rows >= 1 (rows % 32
  * == 0 for PQ_EPI_SWIGLU_Q8).
  *

@@ -51,6 +51,8 @@ def _mv_fn(fmt):
     ("grid1", 4, 40, 4096, 17, 2, False),
     ("grid1", 8, 130, 1024, 20, 3, True),      # 3 row tiles, ragged
     ("grid1", 2, 40, 6144, 20, 1, True),       # 24 slabs
+    ("ternary", 3, 100, 512, 2100, 1, True),   # > 2048 assignments: chunks of 64, ragged
+    ("grid1", 5, 64, 768, 1100, 2, False),     # > 2048 assignments, activation row per assignment
 ])
 def test_tile_q8_f32(fmt, E, N, K, T, k, abt):
     say("tile q8 f32", fmt, E, N, K, T, k, abt)
@@ -80,6 +82,7 @@ def test_tile_q8_f32(fmt, E, N, K, T, k, abt):
     ("ternary", 1, 32, 256, 33, 1),
     ("grid1", 2, 256, 1024, 70, 1),
     ("grid1", 8, 64, 2048, 24, 3),
+    ("ternary", 4, 64, 256, 1040, 2),         # > 2048 assignments: chunks of 64
 ])
 def test_tile_q8_swiglu(fmt, E, I, H, T, k):
     """Gate/up with the SwiGLU + q8 epilogue (rows = I, cols = H)."""
