@@ -190,6 +190,8 @@ def test_ternary_matvec_1024_single_matrix():
     ("sign1", 16, 50, 4096, 9, 4, True),      # pairs of assignments per pass
     ("sign1", 8, 64, 1024, 40, 3, True),      # split groups of assignments
     ("sign1", 4, 20, 6144, 2, 2, False),      # 48 chunks per row
+    ("sign1", 2, 16, 8192, 3, 2, True),       # 64 chunks per row (the widest)
+    ("sign1", 1024, 40, 512, 20, 8, True),    # 1024 experts (the limit)
 ])
 def test_grouped_matvec(fmt, E, N, K, T, k, abt):
     say("matvec", fmt, E, N, K, T, k, abt)

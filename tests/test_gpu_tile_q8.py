@@ -51,6 +51,8 @@ def _mv_fn(fmt):
     ("grid1", 4, 40, 4096, 17, 2, False),
     ("grid1", 8, 130, 1024, 20, 3, True),      # 3 row tiles, ragged
     ("grid1", 2, 40, 6144, 20, 1, True),       # 24 slabs
+    ("ternary", 2, 64, 8192, 40, 1, True),     # 32 slabs (the widest rows of the mat-vec)
+    ("grid1", 1024, 32, 256, 24, 8, True),     # 1024 experts (the limit), most with one assignment
     ("ternary", 3, 100, 512, 2100, 1, True),   # > 2048 assignments: chunks of 64, ragged
     ("grid1", 5, 64, 768, 1100, 2, False),     # > 2048 assignments, activation row per assignment
 ])
@@ -144,15 +146,17 @@ def test_tile_q8_combine(fmt, E, H, I, T, k):
     assert_tol(to_host(y), y_ref, ty + np.abs(y_ref) * 1e-6, "y")
 
 
-@pytest.mark.parametrize("fmt,K", [("ternary", 768), ("grid1", 1024)])
-def test_matvec_hands_heavy_experts_to_tile(fmt, K):
-    """Through pq_moe_matvec_*: 40 tokens, top-2 of 16 experts, every token's
-    first choice expert 0 (40 assignments) and the second spread over the
+@pytest.mark.parametrize("fmt,K,E,T", [("ternary", 768, 16, 40), ("grid1", 1024, 16, 40), ("ternary", 512, 1024, 600)])
+def test_matvec_hands_heavy_experts_to_tile(fmt, K, E, T):
+    """Through pq_moe_matvec_*: T tokens, top-2 of E experts (more
+    assignments than experts, so the split grouping runs), every token's
+    first choice expert 0 (T assignments) and the second spread over the
     others (a few each).  Block sums and outputs match the oracle for all;
     expert 0's outputs are the tile kernel's own bits."""
-    say("matvec dispatch", fmt, K)
-    E, N, T, k = 16, 96, 40, 2
-    seed = _seed("dispatch", fmt, K)
+    say("matvec dispatch", fmt, K, E, T)
+    N, k = 96, 2
+    assert T * k > E
+    seed = _seed("dispatch", fmt, K, E)
     rng = np.random.default_rng(seed)
     ids = np.stack([np.zeros(T, np.int32), rng.integers(1, E, size=T).astype(np.int32)], axis=1)
     planes = wl.stack_experts(fmt, seed, "w", E, N, K)
