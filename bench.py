@@ -106,7 +106,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
-              "(expert-parallel sharding is described in DESIGN.md, not built).", file=sys.stderr)
+              "(expert-parallel sharding is a design note only, not built).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
