@@ -25,7 +25,8 @@ EXPORTS = (
     "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_matvec_sign1",
     "pq_moe_tile_q8_ternary", "pq_moe_tile_q8_grid1",
     "pq_moe_gemm_dequant_tile",
-    "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1", "pq_validate_ternary",
+    "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1",
+    "pq_moe_decode1_gate_up_sign1", "pq_validate_ternary",
     "pq_selftest", "pq_status_str", "pq_abi_version",
 )
 
@@ -95,6 +96,8 @@ def _load():
         "pq_moe_combine": [p, p, i32, i32, i32, p, p],
         "pq_moe_decode1_gate_up_ternary": [p, p, i32, i32, ctypes.POINTER(TernaryW),
                                            ctypes.POINTER(TernaryW)] + [p] * 10,
+        "pq_moe_decode1_gate_up_sign1": [p, p, i32, i32, ctypes.POINTER(Sign1W),
+                                         ctypes.POINTER(Sign1W)] + [p] * 10,
         "pq_moe_decode1_gate_up_grid1": [p, p, i32, i32, ctypes.POINTER(Grid1W),
                                          ctypes.POINTER(Grid1W)] + [p] * 10,
         "pq_validate_ternary": [ctypes.POINTER(TernaryW), p, p],
@@ -411,14 +414,16 @@ def selftest() -> int:
 
 def moe_decode1_gate_up(gate, up, x: torch.Tensor, logits: torch.Tensor, top_k: int, ids, w, groups,
                         hq, hd, y_zero=None):
-    """pq_moe_decode1_gate_up_{ternary,grid1}: one token's routing, q8 and gate/up
+    """pq_moe_decode1_gate_up_{ternary,grid1,sign1}: one token's routing, q8 and gate/up
     (SwiGLU + q8) in one launch.  x float32 [1][H], logits float32 [1][E];
     writes ids int32 [1][k], w float32 [1][k], groups (GroupBuffers), hq int8
     [k][I], hd float32 [k][I/32], and zeros y_zero float32 [1][H] if given."""
     _dt(x, torch.float32)
     _dt(logits, torch.float32)
     E = logits.shape[-1]
-    fn = "pq_moe_decode1_gate_up_ternary" if isinstance(gate, TernaryWeights) else "pq_moe_decode1_gate_up_grid1"
+    fn = ("pq_moe_decode1_gate_up_ternary" if isinstance(gate, TernaryWeights)
+          else "pq_moe_decode1_gate_up_sign1" if isinstance(gate, Sign1Weights)
+          else "pq_moe_decode1_gate_up_grid1")
     cg, cu = gate.cstruct(), up.cstruct()
     rc = getattr(_lib, fn)(_ptr(x), _ptr(logits), E, top_k, ctypes.byref(cg), ctypes.byref(cu),
                            _ptr(ids), _ptr(w), _ptr(groups.expert_offsets), _ptr(groups.sorted_assign),

@@ -436,7 +436,7 @@ void k_matvec(ExpertArgs p) {
                     float f = 0.0f;
 #pragma unroll
                     for (int s = 0; s < SUBS; ++s) f += xs[j][s] * static_cast<float>(isum[j][s]);
-                    part[j] = seg_sum<LS>(lane_on ? dw * f : 0.0f);
+                    part[j] = seg_sum<LS>(lane_on ? mul_rounded(dw, f) : 0.0f);
                     if constexpr (DBG) {
                         int32_t* dst = p.dbg_isums[mat];
                         if (dst && lane_on && rok && j < mcount) {

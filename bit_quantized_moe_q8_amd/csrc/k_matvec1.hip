@@ -24,7 +24,10 @@
 // The arithmetic per row is that of the general grouped kernel: ternary
 // codes decoded with one byte permute per four weights into int8 and
 // accumulated with v_dot4_i32_i8 against byte-transposed activations; grid1
-// groups looked up in the 2048-entry codebook held in LDS; exact int32
+// groups looked up in the 2048-entry codebook held in LDS; sub-scaled signs
+// (pxq_llama README, "What's PXQ?", PXQ1: 1-bit sign codes under a per-row fp16
+// anchor with a 4-bit scale per 16 weights) as +-1 byte patterns from a
+// 256-entry LDS table, each 16-weight sum times its sub-scale; exact int32
 // sums per 32-weight block; fp32 scale application; DPP row reductions.
 #include "pq_device.hpp"
 #include "pq_internal.hpp"
@@ -87,6 +90,12 @@ struct Chunk<kGrid1> {
     static constexpr int kWeights = 128;  // 16 group indices
     static constexpr int kSubs = 4;
 };
+template <>
+struct Chunk<kSign1> {
+    static constexpr int kWeights = 128;  // 16 sign bytes
+    static constexpr int kSubs = 4;
+};
+constexpr int kSignPatterns = 256;
 
 // ROUTE (gate/up with the SwiGLU epilogue only): the workgroup computes the
 // routing and the q8 activations itself from the token's logits and fp32
@@ -108,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
     constexpr int kMaxCols = 64 * CK::kWeights;       // widest row the launcher accepts
     static_assert(!ROUTE || (ABT && EPI == kEpiSwigluQ8), "routing only in the gate/up kernel");
 
-    __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : 1];
+    // grid1: the codebook; sign1: the 256 byte patterns of +-1
+    __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : (FMT == kSign1) ? kSignPatterns : 1];
     __shared__ float s_gu[NMAT][kTile];
     __shared__ uint64_t s_key64[(ROUTE && NK <= 4) ? 4 * kWave : 1];
     __shared__ int s_part[(ROUTE && NK <= 4) ? 2 : 1][(ROUTE && NK <= 4) ? 2 * kWave : 1];
@@ -135,6 +145,18 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
         for (int k = 0; k < kGridEntries / 2 / kThreads; ++k)
             __builtin_amdgcn_global_load_lds(src + k * kThreads + tid,
                                              (lds_void*)(dst + k * kThreads + wave * kWave), 16, 0, 0);
+    }
+    if constexpr (FMT == kSign1) {
+        // pattern i: byte j is -1 where bit j of i is set, else +1
+        if (tid < kSignPatterns) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo |= (((tid >> j) & 1) ? 0xFFu : 0x01u) << (8 * j);
+                hi |= (((tid >> (j + 4)) & 1) ? 0xFFu : 0x01u) << (8 * j);
+            }
+            s_grid[tid] = make_uint2(lo, hi);
+        }
     }
 
     // ---- activation slice of row r (this lane's chunk)
@@ -272,7 +294,9 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
 
     // ---- every weight row of the tile
     const uint32_t qs_row = (FMT == kTernary) ? cols / 4 : cols / 8;
-    const uint32_t qh_row = cols / 32, d_row = cols / 256;
+    // grid1 qh: one uint16 per 32 weights; sign1 sub-scales: one byte per
+    // 32 weights, and one anchor d per row
+    const uint32_t qh_row = cols / 32, d_row = (FMT == kSign1) ? 1 : cols / 256;
     const int64_t qs_e = static_cast<int64_t>(rows) * qs_row;
     const int64_t qh_e = static_cast<int64_t>(rows) * qh_row;
     const int64_t d_e = static_cast<int64_t>(rows) * d_row;
@@ -294,6 +318,10 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
             const uint16_t* qhb = ((NMAT == 2 && mat == 1) ? p.qh[1] : p.qh[0]) + e * qh_e;
             wh[it] = *reinterpret_cast<const uint2*>(qhb + (nc * qh_row + cc * 4u));
             wd[it] = db[nc * d_row + cc / 2u];
+        } else if constexpr (FMT == kSign1) {
+            const uint8_t* scb = ((NMAT == 2 && mat == 1) ? p.sc[1] : p.sc[0]) + e * qh_e;
+            wh[it] = make_uint2(*reinterpret_cast<const uint32_t*>(scb + (nc * qh_row + cc * 4u)), 0u);
+            wd[it] = db[nc];
         } else {
             wh[it] = make_uint2(0, 0);
             wd[it] = db[nc * d_row + cc / 4u];
@@ -335,6 +363,8 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
     if constexpr (FMT == kGrid1) {
         __builtin_amdgcn_s_waitcnt(kWaitVmem0);   // this wave's codebook copies landed
         __syncthreads();
+    } else if constexpr (FMT == kSign1) {
+        __syncthreads();   // the sign patterns
     }
 
     float part[ITERS];
@@ -370,6 +400,31 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
                     for (int s = 0; s < 4; ++s)
                         isum[i >> 1] = dot4(wdec[s], static_cast<int>(act[4 * i + s]), isum[i >> 1]);
                 }
+            } else if constexpr (FMT == kSign1) {
+                // per 16 weights: the +-1 sum (two sign bytes), then times
+                // its 4-bit sub-scale into the q8 block's sum
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    uint2 pat[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int gi = 8 * hf + q;
+                        pat[q] = s_grid[(wv[gi >> 2] >> (8 * (gi & 3))) & 0xffu];
+                    }
+#pragma unroll
+                    for (int sub = 0; sub < 4; ++sub) {
+                        const int sb16 = 4 * hf + sub;   // 16-weight block of the chunk
+                        const uint32_t scv = (wh[it].x >> (4 * sb16)) & 15u;
+                        int s16 = 0;
+#pragma unroll
+                        for (int q = 2 * sub; q < 2 * sub + 2; ++q) {
+                            const int gi = 8 * hf + q;
+                            s16 = dot4(static_cast<int>(pat[q].x), static_cast<int>(act[2 * gi]), s16);
+                            s16 = dot4(static_cast<int>(pat[q].y), static_cast<int>(act[2 * gi + 1]), s16);
+                        }
+                        isum[sb16 >> 1] += static_cast<int>(scv) * s16;
+                    }
+                }
             } else {
                 const uint32_t hv[2] = {wh[it].x, wh[it].y};
 #pragma unroll
@@ -397,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
 #pragma unroll
             for (int s = 0; s < SUBS; ++s) f += xs[s] * static_cast<float>(isum[s]);
             const float dw = half_bits_to_float(static_cast<uint16_t>(wd[it]));
-            part[it] = seg_sum<LS>(lane_on ? dw * f : 0.0f);
+            part[it] = seg_sum<LS>(lane_on ? mul_rounded(dw, f) : 0.0f);
         }
     };
 
@@ -552,11 +607,13 @@ hipError_t launch_route_fmt(const ExpertArgs& a, const RouteArgs& r, hipStream_t
 
 hipError_t launch_decode1_gate_up(Fmt fmt, const ExpertArgs& a, const RouteArgs& r, hipStream_t s) {
     if (fmt == kTernary) return launch_route_fmt<kTernary>(a, r, s);
+    if (fmt == kSign1) return launch_route_fmt<kSign1>(a, r, s);
     return launch_route_fmt<kGrid1>(a, r, s);
 }
 
 hipError_t launch_matvec_tok1(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
     if (fmt == kTernary) return launch_fmt<kTernary>(epi, a, s);
+    if (fmt == kSign1) return launch_fmt<kSign1>(epi, a, s);
     return launch_fmt<kGrid1>(epi, a, s);
 }
 

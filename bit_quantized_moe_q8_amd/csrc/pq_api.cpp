@@ -114,7 +114,13 @@ pq_status guarded(F&& f) {
     }
 }
 
-// One-token gate/up with its own routing and q8; W is pq_ternary_w or pq_grid1_w.
+// The packed code plane of an expert tensor (ternary/grid1 qs, sign1 signs).
+const uint8_t* codes_of(const pq_ternary_w* w) { return w->qs; }
+const uint8_t* codes_of(const pq_grid1_w* w) { return w->qs; }
+const uint8_t* codes_of(const pq_sign1_w* w) { return w->signs; }
+
+// One-token gate/up with its own routing and q8; W is pq_ternary_w,
+// pq_grid1_w or pq_sign1_w.
 template <typename W>
 pq_status decode1_gate_up(pqk::Fmt fmt, const float* x, const float* logits, int32_t n_experts,
                           int32_t top_k, const W* gate, const W* up, int32_t* topk_ids,
@@ -126,11 +132,19 @@ pq_status decode1_gate_up(pqk::Fmt fmt, const float* x, const float* logits, int
         return PQ_ERR_NULL;
     const W* ws[2] = {gate, up};
     for (const W* w : ws) {
-        if (!w->qs || !w->d) return PQ_ERR_NULL;
-        if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+        if (!codes_of(w) || !w->d) return PQ_ERR_NULL;
+        if (!aligned(codes_of(w), 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
     }
     const int8_t* grid = nullptr;
     const uint16_t* qh[2] = {nullptr, nullptr};
+    const uint8_t* sc[2] = {nullptr, nullptr};
+    if constexpr (std::is_same<W, pq_sign1_w>::value) {
+        for (int i = 0; i < 2; ++i) {
+            if (!ws[i]->sc) return PQ_ERR_NULL;
+            if (!aligned(ws[i]->sc, 4)) return PQ_ERR_ALIGN;
+            sc[i] = ws[i]->sc;
+        }
+    }
     if constexpr (std::is_same<W, pq_grid1_w>::value) {
         for (int i = 0; i < 2; ++i) {
             if (!ws[i]->qh || !ws[i]->grid) return PQ_ERR_NULL;
@@ -153,12 +167,14 @@ pq_status decode1_gate_up(pqk::Fmt fmt, const float* x, const float* logits, int
         return PQ_ERR_ALIGN;
 
     pqk::ExpertArgs a{};
-    a.qs[0] = gate->qs;
-    a.qs[1] = up->qs;
+    a.qs[0] = codes_of(gate);
+    a.qs[1] = codes_of(up);
     a.d[0] = gate->d;
     a.d[1] = up->d;
     a.qh[0] = qh[0];
     a.qh[1] = qh[1];
+    a.sc[0] = sc[0];
+    a.sc[1] = sc[1];
     a.grid = grid;
     a.rows = I;
     a.cols = H;
@@ -310,7 +326,7 @@ pq_status sign1_args(const pq_sign1_w* w, const pq_sign1_w* w_up, const pq_group
 
 pq_status launch_matvec_any(pqk::Fmt fmt, int32_t epilogue, const pqk::ExpertArgs& a,
                             const pq_debug* dbg, pq_stream stream) {
-    if (a.n_tokens == 1 && !dbg && fmt != pqk::kSign1)
+    if (a.n_tokens == 1 && !dbg)
         return from_hip(pqk::launch_matvec_tok1(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
     return from_hip(pqk::launch_matvec(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
 }
@@ -559,6 +575,19 @@ pq_status pq_moe_decode1_gate_up_grid1(const float* x, const float* logits, int3
                                        pq_stream stream) {
     return guarded([&]() -> pq_status {
         return decode1_gate_up(pqk::kGrid1, x, logits, n_experts, top_k, gate, up, topk_ids, topk_w,
+                               expert_offsets, sorted_assign, active_experts, n_active, hq, hd,
+                               y_zero, stream);
+    });
+}
+
+pq_status pq_moe_decode1_gate_up_sign1(const float* x, const float* logits, int32_t n_experts,
+                                       int32_t top_k, const pq_sign1_w* gate, const pq_sign1_w* up,
+                                       int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                       int32_t* sorted_assign, int32_t* active_experts,
+                                       int32_t* n_active, int8_t* hq, float* hd, float* y_zero,
+                                       pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        return decode1_gate_up(pqk::kSign1, x, logits, n_experts, top_k, gate, up, topk_ids, topk_w,
                                expert_offsets, sorted_assign, active_experts, n_active, hq, hd,
                                y_zero, stream);
     });

@@ -97,6 +97,16 @@ constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each 16
 constexpr int kDppBcast15 = 0x142;    // lane 15 of a row -> next row
 constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3
 
+// a * b rounded on its own, never fused into a following add: the lanes of a
+// row sum then add rounded products, so the sum has the same bits in every
+// kernel and instantiation that forms it (a fused multiply-add of one lane's
+// product with its partner's rounded one differs in the last bit, and the
+// compiler fuses or not depending on the surrounding code).
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 // Sum over aligned segments of LS lanes (LS a power of two, <= 64) with DPP
 // moves only.  The full segment sum ends up in the last lane of each segment
 // (for LS <= 16 in every lane of it).

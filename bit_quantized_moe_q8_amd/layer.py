@@ -52,8 +52,7 @@ class DecodeLayer:
         self.fused_combine = self.fused and bool(fused_combine)
         if decode1 is None:
             decode1 = self.fused_combine
-        # (the routed one-token launch exists for the ternary and grid1 formats)
-        self.decode1 = bool(decode1) and n_tokens == 1 and fmt != "sign1"
+        self.decode1 = bool(decode1) and n_tokens == 1
         A = n_tokens * top_k
         f32, i8 = torch.float32, torch.int8
         self.use_state(self.new_route_state())

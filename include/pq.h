@@ -241,8 +241,9 @@ pq_status pq_moe_matvec_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
  * times their sub-scales give the exact int32 sum of each q8 block, and the
  * row's anchor is the scale of every block, so the outputs are those of the
  * other formats' definition with w = d * sc * (+-1).  cols % 256 == 0 and
- * cols/128 in {2,4,8,12,16,24,32,48,64} (cols 256..8192).  Every token count
- * runs the grouped mat-vec (no one-token or tile variant for this format).
+ * cols/128 in {2,4,8,12,16,24,32,48,64} (cols 256..8192).  One token
+ * (without dbg) runs the one-token kernel, every other token count the
+ * grouped mat-vec (no int8-MFMA tile variant for this format).
  */
 pq_status pq_moe_matvec_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                               const pq_groups *g, const int8_t *xq, const float *xd,
@@ -321,7 +322,7 @@ pq_status pq_moe_combine(const float *out_assign, const float *topk_w, int32_t n
  *   y_zero (may be NULL): float [H] set to zero for that fused combine.
  * x float [H] (16-byte aligned), logits float [n_experts], gate and up
  * [n_experts][I][H] (grid1: gate's codebook serves both, as in the mat-vec
- * with w_up); H as the mat-vec accepts
+ * with w_up; sign1: sc 4-byte aligned); H as the mat-vec accepts
  * for cols, I % 32 == 0; n_experts <= 1024, 1 <= top_k <= min(16,
  * n_experts).  Inputs finite.
  */
@@ -333,6 +334,12 @@ pq_status pq_moe_decode1_gate_up_ternary(const float *x, const float *logits, in
                                          float *hd, float *y_zero, pq_stream stream);
 pq_status pq_moe_decode1_gate_up_grid1(const float *x, const float *logits, int32_t n_experts,
                                        int32_t top_k, const pq_grid1_w *gate, const pq_grid1_w *up,
+                                       int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                                       int32_t *sorted_assign, int32_t *active_experts,
+                                       int32_t *n_active, int8_t *hq, float *hd, float *y_zero,
+                                       pq_stream stream);
+pq_status pq_moe_decode1_gate_up_sign1(const float *x, const float *logits, int32_t n_experts,
+                                       int32_t top_k, const pq_sign1_w *gate, const pq_sign1_w *up,
                                        int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
                                        int32_t *sorted_assign, int32_t *active_experts,
                                        int32_t *n_active, int8_t *hq, float *hd, float *y_zero,

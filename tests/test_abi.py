@@ -192,3 +192,12 @@ def test_decode1_gate_up_validation(L):
     gw = pq.Grid1W(A16, None, A16, A16, 8, 256, 1024)
     f2 = L.pq_moe_decode1_gate_up_grid1
     assert f2(A16, A16, 8, 2, b(gw), b(gw), *([A16] * 8), A16, S) == pq.PQ_ERR_NULL
+    f3 = L.pq_moe_decode1_gate_up_sign1
+    sw = pq.Sign1W(A16, A16, A16, 8, 256, 1024)
+    assert f3(A16, A16, 8, 2, b(pq.Sign1W(A16, None, A16, 8, 256, 1024)), b(sw), *([A16] * 8), A16, S) \
+        == pq.PQ_ERR_NULL                                                      # no sub-scales
+    assert f3(A16, A16, 8, 2, b(pq.Sign1W(A16, ctypes.c_void_p(0x10002), A16, 8, 256, 1024)), b(sw),
+              *([A16] * 8), A16, S) == pq.PQ_ERR_ALIGN                          # sc not 4-byte aligned
+    assert f3(A16, A16, 8, 2, b(pq.Sign1W(A16, A16, A16, 8, 256, 768)), b(pq.Sign1W(A16, A16, A16, 8, 256, 768)),
+              *([A16] * 8), A16, S) == pq.PQ_ERR_UNSUPPORTED                    # cols/128 = 6
+    assert f3(A16, A16, 8, 9, b(sw), b(sw), *([A16] * 8), A16, S) == pq.PQ_ERR_SHAPE   # top_k > E

@@ -217,8 +217,11 @@ def test_matvec_one_expert_many_tokens():
     ("ternary", 1536, 8, True),    # 24 lanes per row
     ("grid1", 3072, 4, False),
     ("grid1", 6144, 2, True),      # 48 lanes per row
-    ("sign1", 2048, 8, True),      # (the grouped kernel at one token)
-    ("sign1", 1536, 8, False),
+    ("sign1", 2048, 8, True),
+    ("sign1", 1536, 8, False),     # 12 lanes per row
+    ("sign1", 256, 4, True),       # 2 lanes per row
+    ("sign1", 6144, 2, False),     # 48 lanes per row
+    ("sign1", 8192, 1, True),      # 64 lanes per row
 ])
 def test_matvec_one_token(fmt, K, k, abt):
     """The one-token production kernel (no debug outputs), ragged row tiles."""
@@ -226,7 +229,7 @@ def test_matvec_one_token(fmt, K, k, abt):
     _single(fmt, 16, 72, K, 1, k, abt, seed=K + k, want_dbg=False)
 
 
-@pytest.mark.parametrize("fmt", ["ternary", "grid1"])
+@pytest.mark.parametrize("fmt", ["ternary", "grid1", "sign1"])
 def test_matvec_one_token_repeated_ids(fmt):
     """One token whose top-k list repeats an expert (fewer active experts than
     assignments): every epilogue of the one-token kernel against the oracle."""
@@ -240,7 +243,7 @@ def test_matvec_one_token_repeated_ids(fmt):
     up = wl.stack_experts(fmt, 3, "up", E, N, K)
     xq, xd = oracle.quantize_q8(wl.activations_f32(3, 1, K))
     g = pq.group_tokens_by_expert(to_dev(ids), E)
-    mv = pq.moe_matvec_ternary if fmt == "ternary" else pq.moe_matvec_grid1
+    mv = {"ternary": pq.moe_matvec_ternary, "grid1": pq.moe_matvec_grid1, "sign1": pq.moe_matvec_sign1}[fmt]
     hq, hd = mv(weights_to_device(fmt, gate, grid), weights_to_device(fmt, up, grid), g,
                 to_dev(xq), to_dev(xd), True, pq.PQ_EPI_SWIGLU_Q8)
     tok = np.zeros(k, np.int64)
@@ -497,6 +500,9 @@ def test_combine():
     ("ternary", 1024, 512, 32, 16, "normal"),     # most experts, top-16
     ("ternary", 5, 4096, 256, 1, "ties"),
     ("ternary", 300, 1536, 64, 6, "normal"),     # rank over 300 keys, 24 lanes per row
+    ("sign1", 64, 2048, 1536, 8, "normal"),       # sub-scaled signs
+    ("sign1", 512, 4096, 96, 4, "ties"),          # ranking by wave maxima, equal logits
+    ("sign1", 8, 256, 32, 2, "uniform"),          # smallest shapes
 ])
 def test_decode1_gate_up(fmt, E, H, I, k, kind):
     """The routed one-token gate/up against the oracle, and bit for bit
@@ -530,7 +536,7 @@ def test_decode1_gate_up(fmt, E, H, I, k, kind):
     xq2 = torch.empty((1, H), dtype=torch.int8, device=dev())
     xs2 = torch.empty((1, H // 32), device=dev())
     pq.decode_prep(xd_, lg_, k, xq2, xs2, ids2, w2, g2)
-    mv = pq.moe_matvec_ternary if fmt == "ternary" else pq.moe_matvec_grid1
+    mv = {"ternary": pq.moe_matvec_ternary, "grid1": pq.moe_matvec_grid1, "sign1": pq.moe_matvec_sign1}[fmt]
     hq2, hd2 = mv(Wg, Wu, g2, xq2, xs2, True, pq.PQ_EPI_SWIGLU_Q8)
     torch.cuda.synchronize()
     na = int(to_host(g.n_active)[0])
