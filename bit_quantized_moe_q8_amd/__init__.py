@@ -23,7 +23,7 @@ PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 
 EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
     "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_matvec_sign1",
-    "pq_moe_tile_q8_ternary", "pq_moe_tile_q8_grid1",
+    "pq_moe_tile_q8_ternary", "pq_moe_tile_q8_grid1", "pq_moe_tile_q8_sign1",
     "pq_moe_gemm_dequant_tile",
     "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1",
     "pq_moe_decode1_gate_up_sign1", "pq_validate_ternary",
@@ -88,6 +88,9 @@ def _load():
                                    ctypes.POINTER(Groups), p, p, i32, i32, p, p,
                                    ctypes.POINTER(Debug), p],
         "pq_moe_tile_q8_grid1": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
+                                 ctypes.POINTER(Groups), p, p, i32, i32, p, p,
+                                 ctypes.POINTER(Debug), p],
+        "pq_moe_tile_q8_sign1": [ctypes.POINTER(Sign1W), ctypes.POINTER(Sign1W),
                                  ctypes.POINTER(Groups), p, p, i32, i32, p, p,
                                  ctypes.POINTER(Debug), p],
         "pq_moe_gemm_dequant_tile": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
@@ -364,6 +367,12 @@ def moe_tile_q8_grid1(w: Grid1Weights, w_up, groups: GroupBuffers, xq, xd, act_b
                       epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
     """pq_moe_tile_q8_grid1 (see include/pq.h)."""
     return _matvec("pq_moe_tile_q8_grid1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
+
+
+def moe_tile_q8_sign1(w: Sign1Weights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,
+                      epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
+    """pq_moe_tile_q8_sign1 (see include/pq.h)."""
+    return _matvec("pq_moe_tile_q8_sign1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
 
 
 def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: torch.Tensor,

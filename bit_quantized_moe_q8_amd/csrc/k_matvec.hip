@@ -610,7 +610,7 @@ hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
     const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
     ExpertArgs m = a;
     m.heavy_min = 0;
-    if (fmt != kSign1 && a.n_tokens >= kHeavyMin && A > a.n_experts && tile_q8_supported(a.cols)) {
+    if (a.n_tokens >= kHeavyMin && A > a.n_experts && tile_q8_supported(a.cols)) {
         m.heavy_min = kHeavyMin;
         const hipError_t err = launch_tile_q8(fmt, epi, m, s);
         if (err != hipSuccess) return err;

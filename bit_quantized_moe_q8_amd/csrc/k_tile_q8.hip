@@ -33,7 +33,13 @@
 //    byte-transposed to match;
 //  - grid1: lane group g takes group g of the block (8 weights in natural
 //    order): its 11-bit index selects one 8-byte codebook row in LDS, which
-//    is exactly the A fragment.
+//    is exactly the A fragment;
+//  - sub-scaled signs: lane group g takes weights 8g..8g+7 of the block as
+//    int8 sign * sc (sc the 4-bit sub-scale of their 16-weight half), built
+//    by two v_perm_b32 choosing byte by byte between sc and -sc, with the
+//    selectors (the sign byte's bits as 0/1 bytes) from a 256-entry LDS
+//    table; the MFMA block sums are then the sub-scaled sums, and the row's
+//    anchor takes the place of the per-256 scale.
 //
 // Items are chosen on the device from the grouping (offsets / active): an
 // expert takes part when it holds at least `heavy_min` assignments, so the
@@ -71,6 +77,11 @@ template <>
 struct TileFmt<kGrid1> {
     static constexpr int kWords = 3;   // 32 bytes of qs, then 16 bytes of qh
 };
+template <>
+struct TileFmt<kSign1> {
+    static constexpr int kWords = 3;   // 32 sign bytes, then 8 sub-scale bytes
+};
+constexpr int kSignPatterns = 256;
 
 template <int FMT, int EPI, bool DBG, int TOK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((TOK == 32 && !DBG) ? 3 : 1)))
@@ -93,7 +104,9 @@ void k_tile_q8(ExpertArgs p) {
     __shared__ uint2 s_x[2][kTok * kXStride];
     __shared__ float s_xd[2][kTok * (kSlabBlocks + 1)];
     __shared__ float s_d[2][kRows];
-    __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : 1];
+    // grid1: the codebook; sign1: per sign byte, its 8 bits as 0/1 bytes
+    // (v_perm selectors between +sc and -sc)
+    __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : (FMT == kSign1) ? kSignPatterns : 1];
     __shared__ float s_gu[NMAT][(NMAT == 2) ? TR : 1][kTok + 1];
     __shared__ int s_pre[kMaxExperts + 1];   // first chunk number per slot
     __shared__ int s_scan[kWaves + 1];
@@ -111,6 +124,17 @@ void k_tile_q8(ExpertArgs p) {
         const uint4* src = reinterpret_cast<const uint4*>(p.grid);
         uint4* dst = reinterpret_cast<uint4*>(s_grid);
         for (int i = tid; i < kGridEntries / 2; i += kThreads) dst[i] = src[i];
+    }
+    if constexpr (FMT == kSign1) {
+        if (tid < kSignPatterns) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo |= ((tid >> j) & 1u) << (8 * j);
+                hi |= ((tid >> (j + 4)) & 1u) << (8 * j);
+            }
+            s_grid[tid] = make_uint2(lo, hi);
+        }
     }
     // Chunks of up to kTok assignments of the experts that take part,
     // numbered in slot order.
@@ -136,8 +160,9 @@ void k_tile_q8(ExpertArgs p) {
     const int tiles = (rows + TR - 1) / TR;
     const int n_items = run * tiles;
     const int64_t qs_row = (FMT == kTernary) ? cols / 4 : cols / 8;   // bytes
-    const int64_t qh_row = cols / 32;                                  // uint16
-    const int64_t d_row = cols / kSlabK;
+    const int64_t qh_row = cols / 32;   // grid1: uint16 qh; sign1: sub-scale bytes
+    // weight scales per row: one per slab (sign1: one anchor per row)
+    const int64_t d_row = (FMT == kSign1) ? 1 : cols / kSlabK;
     const int n_sub_row = cols / 32;
 
     // This lane's A row: physical row pr = 16 * wave + r of the item.
@@ -174,11 +199,20 @@ void k_tile_q8(ExpertArgs p) {
         const uint16_t* qhrow = nullptr;
         if constexpr (FMT == kGrid1)
             qhrow = (mat_a ? p.qh[1] : p.qh[0]) + (static_cast<int64_t>(e) * rows + na) * qh_row;
+        const uint8_t* scrow = nullptr;
+        if constexpr (FMT == kSign1)
+            scrow = (mat_a ? p.sc[1] : p.sc[0]) + (static_cast<int64_t>(e) * rows + na) * qh_row;
         auto wload = [&](int sb, uint4 (&w)[KW]) {
             if constexpr (FMT == kTernary) {
                 const uint4* src = reinterpret_cast<const uint4*>(qsrow + 64 * sb);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) w[i] = src[i];
+            } else if constexpr (FMT == kSign1) {
+                const uint4* src = reinterpret_cast<const uint4*>(qsrow + 32 * sb);
+                w[0] = src[0];
+                w[1] = src[1];
+                const uint32_t* sc4 = reinterpret_cast<const uint32_t*>(scrow + 8 * sb);
+                w[2] = make_uint4(sc4[0], sc4[1], 0u, 0u);
             } else {
                 const uint4* src = reinterpret_cast<const uint4*>(qsrow + 32 * sb);
                 w[0] = src[0];
@@ -211,7 +245,7 @@ void k_tile_q8(ExpertArgs p) {
                 // wait for every load in flight)
                 const uint16_t* dbase = (NMAT == 2 && tid >= 32) ? p.d[1] : p.d[0];
                 const int nr = min(n0 + ((NMAT == 2) ? (tid & 31) : tid), rows - 1);
-                dr = dbase[(static_cast<int64_t>(e) * rows + nr) * d_row + sb];
+                dr = dbase[(static_cast<int64_t>(e) * rows + nr) * d_row + ((FMT == kSign1) ? 0 : sb)];
             }
         };
         auto sstore = [&](int sl) {
@@ -276,6 +310,18 @@ void k_tile_q8(ExpertArgs p) {
                     if constexpr (FMT == kTernary) {
                         const uint32_t lo = static_cast<uint32_t>(ternary_decode4((wv[2 * q] >> (2 * g)) & 0x03030303u));
                         const uint32_t hi = static_cast<uint32_t>(ternary_decode4((wv[2 * q + 1] >> (2 * g)) & 0x03030303u));
+                        afrag = (static_cast<uint64_t>(hi) << 32) | lo;
+                    } else if constexpr (FMT == kSign1) {
+                        // weights 8g..8g+7 of block q as int8 (+-sc): the sign
+                        // byte selects, byte by byte, sc or -sc of the
+                        // 16-weight sub-block (sub-scale nibble g >> 1 of byte q)
+                        const uint32_t sgn = (wv[q] >> (8 * g)) & 0xffu;
+                        const uint32_t scb = (wv[8 + (q >> 2)] >> (8 * (q & 3))) & 0xffu;
+                        const uint32_t sc = (scb >> (4 * (g >> 1))) & 15u;
+                        const uint32_t pm = sc | (((0u - sc) & 0xffu) << 8);
+                        const uint2 sel = s_grid[sgn];
+                        const uint32_t lo = __builtin_amdgcn_perm(pm, pm, sel.x);
+                        const uint32_t hi = __builtin_amdgcn_perm(pm, pm, sel.y);
                         afrag = (static_cast<uint64_t>(hi) << 32) | lo;
                     } else {
                         const uint32_t lo8 = (wv[q] >> (8 * g)) & 0xffu;
@@ -454,6 +500,7 @@ bool tile_q8_supported(int cols) { return cols >= kSlabK && cols % kSlabK == 0; 
 hipError_t launch_tile_q8(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
     if (!tile_q8_supported(a.cols)) return hipErrorInvalidValue;
     if (fmt == kTernary) return launch_fmt<kTernary>(epi, a, s);
+    if (fmt == kSign1) return launch_fmt<kSign1>(epi, a, s);
     return launch_fmt<kGrid1>(epi, a, s);
 }
 

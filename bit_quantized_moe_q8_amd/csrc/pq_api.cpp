@@ -281,9 +281,11 @@ pq_status grid1_args(const pq_grid1_w* w, const pq_grid1_w* w_up, const pq_group
     return PQ_OK;
 }
 
+template <typename Supported>
 pq_status sign1_args(const pq_sign1_w* w, const pq_sign1_w* w_up, const pq_groups* g,
                      const int8_t* xq, const float* xd, int32_t act_by_token, int32_t epilogue,
-                     void* out0, void* out1, const pq_debug* dbg, pqk::ExpertArgs& a, bool* run) {
+                     void* out0, void* out1, const pq_debug* dbg, Supported supported,
+                     pqk::ExpertArgs& a, bool* run) {
     *run = false;
     if (!w || !w->signs || !w->sc || !w->d) return PQ_ERR_NULL;
     pq_status st = check_groups(g);
@@ -300,7 +302,7 @@ pq_status sign1_args(const pq_sign1_w* w, const pq_sign1_w* w_up, const pq_group
             return PQ_ERR_ALIGN;
     }
     if (!aligned(w->signs, 16) || !aligned(w->sc, 4) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
-    if (!pqk::matvec_supported(pqk::kSign1, w->cols)) return PQ_ERR_UNSUPPORTED;
+    if (!supported(pqk::kSign1, w->cols)) return PQ_ERR_UNSUPPORTED;
     if (g->n_tokens == 0) return PQ_OK;
     if (!xq || !xd) return PQ_ERR_NULL;
     if (!aligned(xq, 16) || !aligned(xd, 4)) return PQ_ERR_ALIGN;
@@ -461,7 +463,8 @@ pq_status pq_moe_matvec_sign1(const pq_sign1_w* w, const pq_sign1_w* w_up, const
     return guarded([&]() -> pq_status {
         pqk::ExpertArgs a;
         bool run;
-        const pq_status st = sign1_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg, a, &run);
+        const pq_status st = sign1_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg,
+                                        pqk::matvec_supported, a, &run);
         if (st != PQ_OK || !run) return st;
         return launch_matvec_any(pqk::kSign1, epilogue, a, dbg, stream);
     });
@@ -494,6 +497,21 @@ pq_status pq_moe_tile_q8_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, cons
                                         a, &run);
         if (st != PQ_OK || !run) return st;
         return launch_tile_all(pqk::kGrid1, epilogue, a, stream);
+    });
+}
+
+pq_status pq_moe_tile_q8_sign1(const pq_sign1_w* w, const pq_sign1_w* w_up, const pq_groups* g,
+                               const int8_t* xq, const float* xd, int32_t act_by_token,
+                               int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
+                               pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        pqk::ExpertArgs a;
+        bool run;
+        const pq_status st = sign1_args(w, w_up, g, xq, xd, act_by_token, epilogue, out0, out1, dbg,
+                                        [](pqk::Fmt, int cols) { return pqk::tile_q8_supported(cols); },
+                                        a, &run);
+        if (st != PQ_OK || !run) return st;
+        return launch_tile_all(pqk::kSign1, epilogue, a, stream);
     });
 }
 

@@ -242,8 +242,9 @@ pq_status pq_moe_matvec_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
  * row's anchor is the scale of every block, so the outputs are those of the
  * other formats' definition with w = d * sc * (+-1).  cols % 256 == 0 and
  * cols/128 in {2,4,8,12,16,24,32,48,64} (cols 256..8192).  One token
- * (without dbg) runs the one-token kernel, every other token count the
- * grouped mat-vec (no int8-MFMA tile variant for this format).
+ * (without dbg) runs the one-token kernel, other token counts the grouped
+ * mat-vec, with the experts of 8+ assignments of a large batch on the
+ * int8-MFMA tile (pq_moe_tile_q8_sign1) as for the other formats.
  */
 pq_status pq_moe_matvec_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                               const pq_groups *g, const int8_t *xq, const float *xd,
@@ -254,12 +255,14 @@ pq_status pq_moe_matvec_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
  * Grouped int8-MFMA tile over q8 activations (a tiled kernel for large
  * batches: Parakon Runtime README, "How it works"; an int8 prefill tile:
  * pxq_llama README, "Updates - 2026-07-19").  Arguments, layouts, epilogues
- * and outputs are those of pq_moe_matvec_ternary / pq_moe_matvec_grid1, and
- * so is the arithmetic: one v_mfma_i32_16x16x32_i8 per q8 block gives the
- * same exact int32 block sums (dbg->isums equal the mat-vec's bit for bit),
+ * and outputs are those of pq_moe_matvec_ternary / _grid1 / _sign1, and so
+ * is the arithmetic: one v_mfma_i32_16x16x32_i8 per q8 block gives the same
+ * exact int32 block sums (dbg->isums equal the mat-vec's bit for bit),
  * scaled in fp32 as sum over 256-blocks of d * (sum over 32-blocks of
- * xd * isum).  Only the fp32 summation order differs, within the tolerance
- * of the fp32 result.  Every active expert is processed in chunks of up to
+ * xd * isum).  Sub-scaled signs enter the MFMA as int8 weights sign * sc
+ * (|w| <= 15), so its block sums are the per-16 sums times their
+ * sub-scales, and the row's anchor is d for every 256-block.  Only the fp32
+ * summation order differs, within the tolerance of the fp32 result.  Every active expert is processed in chunks of up to
  * 32 assignments (batches of at most 2048 assignments) or 64 (larger
  * batches), and tiles of 64 weight rows (32 gate + 32 up rows for
  * PQ_EPI_SWIGLU_Q8).  cols % 256 == 0 (any such cols); rows >= 1 (rows % 32
@@ -275,6 +278,10 @@ pq_status pq_moe_tile_q8_ternary(const pq_ternary_w *w, const pq_ternary_w *w_up
                                  int32_t act_by_token, int32_t epilogue, void *out0,
                                  void *out1, const pq_debug *dbg, pq_stream stream);
 pq_status pq_moe_tile_q8_grid1(const pq_grid1_w *w, const pq_grid1_w *w_up,
+                               const pq_groups *g, const int8_t *xq, const float *xd,
+                               int32_t act_by_token, int32_t epilogue, void *out0,
+                               void *out1, const pq_debug *dbg, pq_stream stream);
+pq_status pq_moe_tile_q8_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                                const pq_groups *g, const int8_t *xq, const float *xd,
                                int32_t act_by_token, int32_t epilogue, void *out0,
                                void *out1, const pq_debug *dbg, pq_stream stream);

@@ -139,7 +139,8 @@ def test_tile_q8_validation(L):
     b = ctypes.byref
     g = _groups(pq)
     for f, mk in ((L.pq_moe_tile_q8_ternary, lambda rows, cols: pq.TernaryW(A16, A16, 8, rows, cols)),
-                  (L.pq_moe_tile_q8_grid1, lambda rows, cols: pq.Grid1W(A16, A16, A16, A16, 8, rows, cols))):
+                  (L.pq_moe_tile_q8_grid1, lambda rows, cols: pq.Grid1W(A16, A16, A16, A16, 8, rows, cols)),
+                  (L.pq_moe_tile_q8_sign1, lambda rows, cols: pq.Sign1W(A16, A16, A16, 8, rows, cols))):
         ok_w = mk(64, 1024)
         assert f(b(mk(64, 1000)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_SHAPE
         assert f(b(mk(64, 128)), None, b(g), A16, A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_SHAPE

@@ -32,11 +32,11 @@ def _ids(rng, E, T, k):
 
 
 def _tile_fn(fmt):
-    return pq.moe_tile_q8_ternary if fmt == "ternary" else pq.moe_tile_q8_grid1
+    return {"ternary": pq.moe_tile_q8_ternary, "grid1": pq.moe_tile_q8_grid1, "sign1": pq.moe_tile_q8_sign1}[fmt]
 
 
 def _mv_fn(fmt):
-    return pq.moe_matvec_ternary if fmt == "ternary" else pq.moe_matvec_grid1
+    return {"ternary": pq.moe_matvec_ternary, "grid1": pq.moe_matvec_grid1, "sign1": pq.moe_matvec_sign1}[fmt]
 
 
 @pytest.mark.parametrize("fmt,E,N,K,T,k,abt", [
@@ -55,6 +55,12 @@ def _mv_fn(fmt):
     ("grid1", 1024, 32, 256, 24, 8, True),     # 1024 experts (the limit), most with one assignment
     ("ternary", 3, 100, 512, 2100, 1, True),   # > 2048 assignments: chunks of 64, ragged
     ("grid1", 5, 64, 768, 1100, 2, False),     # > 2048 assignments, activation row per assignment
+    ("sign1", 2, 64, 256, 40, 1, True),        # sub-scaled signs as int8 sign * sc
+    ("sign1", 4, 40, 4096, 17, 2, False),
+    ("sign1", 8, 130, 768, 20, 3, True),       # a width the mat-vec has no variant for
+    ("sign1", 2, 64, 8192, 40, 1, True),       # 32 slabs
+    ("sign1", 3, 100, 512, 2100, 1, True),     # > 2048 assignments: chunks of 64
+    ("sign1", 1024, 32, 256, 24, 8, True),     # 1024 experts
 ])
 def test_tile_q8_f32(fmt, E, N, K, T, k, abt):
     say("tile q8 f32", fmt, E, N, K, T, k, abt)
@@ -85,6 +91,8 @@ def test_tile_q8_f32(fmt, E, N, K, T, k, abt):
     ("grid1", 2, 256, 1024, 70, 1),
     ("grid1", 8, 64, 2048, 24, 3),
     ("ternary", 4, 64, 256, 1040, 2),         # > 2048 assignments: chunks of 64
+    ("sign1", 2, 256, 1024, 70, 1),
+    ("sign1", 4, 64, 256, 1040, 2),
 ])
 def test_tile_q8_swiglu(fmt, E, I, H, T, k):
     """Gate/up with the SwiGLU + q8 epilogue (rows = I, cols = H)."""
@@ -123,7 +131,8 @@ def test_tile_q8_swiglu(fmt, E, I, H, T, k):
     assert_equal(to_host(hd2), to_host(hd), "hd debug vs production")
 
 
-@pytest.mark.parametrize("fmt,E,H,I,T,k", [("ternary", 4, 200, 512, 20, 2), ("grid1", 2, 64, 1536, 40, 1)])
+@pytest.mark.parametrize("fmt,E,H,I,T,k", [("ternary", 4, 200, 512, 20, 2), ("grid1", 2, 64, 1536, 40, 1),
+                                             ("sign1", 2, 64, 1536, 40, 1)])
 def test_tile_q8_combine(fmt, E, H, I, T, k):
     """Down projection with the weighted combine fused in (rows = H, cols = I)."""
     say("tile q8 combine", fmt, E, H, I, T, k)
@@ -146,7 +155,8 @@ def test_tile_q8_combine(fmt, E, H, I, T, k):
     assert_tol(to_host(y), y_ref, ty + np.abs(y_ref) * 1e-6, "y")
 
 
-@pytest.mark.parametrize("fmt,K,E,T", [("ternary", 768, 16, 40), ("grid1", 1024, 16, 40), ("ternary", 512, 1024, 600)])
+@pytest.mark.parametrize("fmt,K,E,T", [("ternary", 768, 16, 40), ("grid1", 1024, 16, 40), ("ternary", 512, 1024, 600),
+                                       ("sign1", 1024, 16, 40), ("sign1", 2048, 256, 300)])
 def test_matvec_hands_heavy_experts_to_tile(fmt, K, E, T):
     """Through pq_moe_matvec_*: T tokens, top-2 of E experts (more
     assignments than experts, so the split grouping runs), every token's
@@ -181,7 +191,7 @@ def test_matvec_hands_heavy_experts_to_tile(fmt, K, E, T):
 def test_tile_q8_single_assignment():
     """One token on one expert of two (one chunk with one live column)."""
     say("tile q8 single")
-    for fmt in ("ternary", "grid1"):
+    for fmt in ("ternary", "grid1", "sign1"):
         E, N, K = 2, 64, 512
         planes = wl.stack_experts(fmt, 3, "w", E, N, K)
         grid = wl.codebook(3) if fmt == "grid1" else None
