@@ -247,7 +247,8 @@ def main():
         elif q8_prefill:
             # the int8-MFMA tile alone (the mat-vec entry point adds a launch
             # for the experts under 8 assignments; at 2048 tokens it has none)
-            tile = pq.moe_tile_q8_ternary if fmt == "ternary" else pq.moe_tile_q8_grid1
+            tile = {"ternary": pq.moe_tile_q8_ternary, "grid1": pq.moe_tile_q8_grid1,
+                    "sign1": pq.moe_tile_q8_sign1}[fmt]
             tile(layers[l]["gate"], layers[l]["up"], layer.groups, layer.xq, layer.xd, True,
                  pq.PQ_EPI_SWIGLU_Q8, layer.hq, layer.hd)
         elif decode1:

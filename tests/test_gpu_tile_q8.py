@@ -205,7 +205,8 @@ def test_tile_q8_single_assignment():
         assert_tol(to_host(out), y_ref, t_ref, "y")
 
 
-@pytest.mark.parametrize("name", ["ternary_moe_prefill_q8_t2048", "grid1_moe_prefill_q8_t2048"])
+@pytest.mark.parametrize("name", ["ternary_moe_prefill_q8_t2048", "grid1_moe_prefill_q8_t2048",
+                                  "sign1_moe_prefill_q8_t2048"])
 def test_q8_prefill_full_size_sampled(name):
     """2048 tokens through all 256 experts with q8 activations, in the layer
     sequence the benchmark times (the mat-vec entry points hand every expert
