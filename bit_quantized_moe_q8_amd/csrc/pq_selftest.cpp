@@ -188,6 +188,30 @@ pq_status run(hipStream_t s) {
                                        nullptr, st));
         check_out();
     }
+    // ---- sub-scaled signs: every sign positive, every sub-scale 1, anchors 1
+    std::vector<uint8_t> ssg(static_cast<size_t>(kE) * kRows * kH / 8, 0);
+    std::vector<uint8_t> ssc(static_cast<size_t>(kE) * kRows * kH / 32, 0x11);
+    std::vector<uint16_t> sanc(static_cast<size_t>(kE) * kRows, kHalfOne);
+    DevBuf dssg, dssc, dsanc;
+    ok(dssg.put(ssg) && dssc.put(ssc) && dsanc.put(sanc));
+    const pq_sign1_w sw{dssg.as<uint8_t>(), dssc.as<uint8_t>(), dsanc.as<uint16_t>(), kE, kRows, kH};
+    hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
+    pq_ok(pq_moe_matvec_sign1(&sw, nullptr, &g, dxq.as<int8_t>(), dxd.as<float>(), 1, PQ_EPI_F32,
+                              dout.p, nullptr, nullptr, st));
+    check_out();
+    // ---- the int8-MFMA tile in all three formats (same answers)
+    hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
+    pq_ok(pq_moe_tile_q8_ternary(&tw, nullptr, &g, dxq.as<int8_t>(), dxd.as<float>(), 1, PQ_EPI_F32,
+                                 dout.p, nullptr, nullptr, st));
+    check_out();
+    hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
+    pq_ok(pq_moe_tile_q8_grid1(&gw, nullptr, &g, dxq.as<int8_t>(), dxd.as<float>(), 1, PQ_EPI_F32,
+                               dout.p, nullptr, nullptr, st));
+    check_out();
+    hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
+    pq_ok(pq_moe_tile_q8_sign1(&sw, nullptr, &g, dxq.as<int8_t>(), dxd.as<float>(), 1, PQ_EPI_F32,
+                               dout.p, nullptr, nullptr, st));
+    check_out();
 
     // ---- combine: separate (out = the exact sums above), and fused into the
     // mat-vec (activation row = assignment: use the q8 rows of token a/k)
