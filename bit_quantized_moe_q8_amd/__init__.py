@@ -24,7 +24,7 @@ EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
     "pq_moe_matvec_ternary", "pq_moe_matvec_grid1", "pq_moe_matvec_sign1",
     "pq_moe_tile_q8_ternary", "pq_moe_tile_q8_grid1", "pq_moe_tile_q8_sign1",
-    "pq_moe_gemm_dequant_tile",
+    "pq_moe_gemm_dequant_tile", "pq_moe_gemm_dequant_tile_sign1",
     "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1",
     "pq_moe_decode1_gate_up_sign1", "pq_validate_ternary",
     "pq_selftest", "pq_status_str", "pq_abi_version",
@@ -96,6 +96,9 @@ def _load():
         "pq_moe_gemm_dequant_tile": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
                                      ctypes.POINTER(Groups), p, i32, i32, p,
                                      ctypes.POINTER(Debug), p],
+        "pq_moe_gemm_dequant_tile_sign1": [ctypes.POINTER(Sign1W), ctypes.POINTER(Sign1W),
+                                           ctypes.POINTER(Groups), p, i32, i32, p,
+                                           ctypes.POINTER(Debug), p],
         "pq_moe_combine": [p, p, i32, i32, i32, p, p],
         "pq_moe_decode1_gate_up_ternary": [p, p, i32, i32, ctypes.POINTER(TernaryW),
                                            ctypes.POINTER(TernaryW)] + [p] * 10,
@@ -377,7 +380,8 @@ def moe_tile_q8_sign1(w: Sign1Weights, w_up, groups: GroupBuffers, xq, xd, act_b
 
 def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: torch.Tensor,
                           act_by_token: bool, epilogue: int = PQ_EPI_F32, out0=None, dbg: dict = None):
-    """pq_moe_gemm_dequant_tile: x bf16 (torch.bfloat16 or int16 bits)."""
+    """pq_moe_gemm_dequant_tile (grid1) or pq_moe_gemm_dequant_tile_sign1 (Sign1Weights):
+    x bf16 (torch.bfloat16 or int16 bits)."""
     _dt(x_bf16, torch.bfloat16, torch.int16, torch.uint16)
     E, rows, cols = w.shape
     A = groups.n_tokens * groups.top_k
@@ -387,10 +391,11 @@ def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: t
     ws = w.cstruct()
     wu = w_up.cstruct() if w_up is not None else None
     gs = groups.cstruct()
-    rc = _lib.pq_moe_gemm_dequant_tile(ctypes.byref(ws), ctypes.byref(wu) if wu is not None else None,
-                                       ctypes.byref(gs), _ptr(x_bf16), int(act_by_token), int(epilogue),
-                                       _ptr(out0), _debug_struct(dbg), _stream())
-    _check("pq_moe_gemm_dequant_tile", rc)
+    fn = "pq_moe_gemm_dequant_tile_sign1" if isinstance(w, Sign1Weights) else "pq_moe_gemm_dequant_tile"
+    rc = getattr(_lib, fn)(ctypes.byref(ws), ctypes.byref(wu) if wu is not None else None,
+                           ctypes.byref(gs), _ptr(x_bf16), int(act_by_token), int(epilogue),
+                           _ptr(out0), _debug_struct(dbg), _stream())
+    _check(fn, rc)
     return out0
 
 

@@ -1,7 +1,11 @@
-// Prefill: grouped dequant-per-tile GEMM over grid1 expert weights with bf16
-// activations on MFMA (Parakon Runtime README, "How it works": prompt
-// processing at large batch sizes uses a dequant-per-tile GEMM path; the
-// packed blocks are never expanded in memory).
+// Prefill: grouped dequant-per-tile GEMM over grid1 (or sub-scaled sign)
+// expert weights with bf16 activations on MFMA (Parakon Runtime README, "How
+// it works": prompt processing at large batch sizes uses a dequant-per-tile
+// GEMM path; the packed blocks are never expanded in memory).  Sub-scaled
+// signs (pxq_llama README, "What's PXQ?", PXQ1) take the same path: a lane's
+// 8 weights are the bf16 of their 4-bit sub-scale (exact) with the sign bits
+// of their sign byte ORed in from a 256-entry mask table in LDS, and the
+// row's fp16 anchor is the scale of every block.
 //
 // out[a][n] = sum_b d[e][n][b] * sum_{k in block b} x[r(a)][k] * w[e][n][k]
 //
@@ -98,7 +102,12 @@ struct BCur {
 
 // One row chunk x one column tile, all K blocks, MS = 16-row subtiles in the
 // chunk (compile-time, so the inner loops have no branches).
-template <int EPI, bool DBG, int MS>
+// Sub-scaled signs: a column's sub-scale row has K/32 bytes, 8 per block;
+// block kb's bytes are staged with its neighbour's as the 16-byte unit at
+// byte 8 * (kb & ~1) of the row (K % 512 == 0, so every unit is 16-byte
+// aligned and inside the row), in half kb & 1 of it.
+
+template <int FMT, int EPI, bool DBG, int MS>
 __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict__ a0,
                                           uint4* __restrict__ a1, uint4* __restrict__ q0,
                                           uint4* __restrict__ q1, uint4* __restrict__ h0,
@@ -113,7 +122,9 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
     const int lg = lane >> 4, lc = lane & 15;
     const int N = p.rows, K = p.cols, KB = K / 256;
-    const int qs_row = K / 8, qh_row = K / 32, d_row = K / 256;
+    // grid1: qh uint16 per 32 weights and one scale per 256; sign1: one
+    // sub-scale byte per 32 weights and one anchor per row
+    const int qs_row = K / 8, qh_row = K / 32, d_row = (FMT == kSign1) ? 1 : K / 256;
 
     // activation row of each A copy this lane issues (fixed for the item)
     constexpr int ACOPIES = MS * 8 / kWaves;   // A copies per wave per block
@@ -164,8 +175,13 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
         const int pi = u0 + lane;
         int n = ntt * TILE_N + (pi % TILE_N);
         n = n < N ? n : N - 1;
-        const uint16_t* base = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
-        copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qh_row + kb * 8, dh + u0);
+        if constexpr (FMT == kSign1) {
+            const uint8_t* base = (NMAT == 1 || m == 0) ? p.sc[0] : p.sc[1];
+            copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qh_row + 8 * (kb & ~1), dh + u0);
+        } else {
+            const uint16_t* base = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
+            copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qh_row + kb * 8, dh + u0);
+        }
     };
     auto issue_b = [&](int kb, uint4* dq, uint4* dh) {
 #pragma unroll
@@ -220,7 +236,7 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int w = 0; w < NW; ++w) dbits[m][w] = p.d[m][doff[w] + kb];
+            for (int w = 0; w < NW; ++w) dbits[m][w] = p.d[m][doff[w] + ((FMT == kSign1) ? 0 : kb)];
         const int kp = kb + 1 < KB ? kb + 1 : KB - 1;
 
         BCur<NMAT, NW> cur;
@@ -230,7 +246,13 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
             for (int w = 0; w < NW; ++w) {
                 const int pi = m * TILE_N + (wave * NW + w) * 16 + lc;
                 cur.q[m][w] = reinterpret_cast<const uint2*>(qc)[pi * 4 + lg];
-                cur.h[m][w] = reinterpret_cast<const uint32_t*>(hc)[pi * 4 + lg];
+                if constexpr (FMT == kSign1) {
+                    // the two sub-scale bytes of lane group lg's 64 weights, in
+                    // the half of the staged unit that holds block kb
+                    cur.h[m][w] = reinterpret_cast<const uint16_t*>(hc)[pi * 8 + 4 * (kb & 1) + lg];
+                } else {
+                    cur.h[m][w] = reinterpret_cast<const uint32_t*>(hc)[pi * 4 + lg];
+                }
             }
 
         auto frag_b = [&](int ks, bf16x8 (&bf)[NMAT][NW]) {
@@ -240,8 +262,18 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
                 for (int w = 0; w < NW; ++w) {
                     const uint32_t qword = (ks < 4) ? cur.q[m][w].x : cur.q[m][w].y;
                     const uint32_t lo8 = (qword >> (8 * (ks & 3))) & 0xffu;
-                    const uint32_t hi3 = (cur.h[m][w] >> (16 * (ks >> 2) + 3 * (ks & 3))) & 7u;
-                    bf[m][w] = __builtin_bit_cast(bf16x8, s_cb[lo8 | (hi3 << 8)]);
+                    if constexpr (FMT == kSign1) {
+                        // 8 weights: bf16 of their sub-scale (exact), with the
+                        // sign bits of their sign byte from the mask table
+                        const uint32_t sc = (cur.h[m][w] >> (8 * (ks >> 2) + 4 * ((ks >> 1) & 1))) & 15u;
+                        const uint32_t sb = __builtin_bit_cast(uint32_t, static_cast<float>(sc)) >> 16;
+                        const uint32_t pr = sb | (sb << 16);
+                        const uint4 mk = s_cb[lo8];
+                        bf[m][w] = __builtin_bit_cast(bf16x8, make_uint4(pr | mk.x, pr | mk.y, pr | mk.z, pr | mk.w));
+                    } else {
+                        const uint32_t hi3 = (cur.h[m][w] >> (16 * (ks >> 2) + 3 * (ks & 3))) & 7u;
+                        bf[m][w] = __builtin_bit_cast(bf16x8, s_cb[lo8 | (hi3 << 8)]);
+                    }
                 }
         };
         auto frag_a = [&](int ks, bf16x8 (&af)[MS]) {
@@ -335,7 +367,7 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
     }
 }
 
-template <int EPI, bool DBG>
+template <int FMT, int EPI, bool DBG>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
     constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
     constexpr int NW = (NMAT == 2) ? 2 : 4;       // 16-col subtiles per wave per matrix
@@ -357,7 +389,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
     const int tid = threadIdx.x;
     const int E = p.n_experts, N = p.rows;
 
-    // bf16 codebook: entry i = 8 values in {-1,0,1} -> 8 bf16 (exact).
+    // grid1: bf16 codebook, entry i = 8 values in {-1,0,1} -> 8 bf16 (exact);
+    // sign1: entry i = the bf16 sign bits (0x8000 where bit j of i is set) of
+    // the 8 weights of sign byte i
+    if constexpr (FMT == kSign1) {
+        if (tid < 256) {
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = (((tid >> (2 * j)) & 1) ? 0x8000u : 0u) | (((tid >> (2 * j + 1)) & 1) ? 0x80000000u : 0u);
+            s_cb[tid] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    } else {
     for (int i = tid; i < kGridEntries; i += kThreads) {
         const uint2 raw = reinterpret_cast<const uint2*>(p.grid)[i];
         uint32_t o[4];
@@ -371,6 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
             o[j] = c0 | (c1 << 16);
         }
         s_cb[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
     }
     // Chunks of up to 64 rows are numbered in expert order; s_cpre[e] is the
     // number of expert e's first chunk (exclusive scan of the chunk counts),
@@ -424,35 +468,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
         }
         __syncthreads();
         switch ((mrows + 15) >> 4) {
-            case 1: gemm_item<EPI, DBG, 1>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
-            case 2: gemm_item<EPI, DBG, 2>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
-            case 3: gemm_item<EPI, DBG, 3>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
-            default: gemm_item<EPI, DBG, 4>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 1: gemm_item<FMT, EPI, DBG, 1>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 2: gemm_item<FMT, EPI, DBG, 2>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
+            case 3: gemm_item<FMT, EPI, DBG, 3>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
+            default: gemm_item<FMT, EPI, DBG, 4>(p, s_a0, s_a1, s_q0, s_q1, s_h0, s_h1, s_cb, s_row, s_asg, e, mrows, nt); break;
         }
         __syncthreads();   // s_row / s_asg / rings are reused by the next item
     }
 }
 
-template <int EPI, bool DBG>
+template <int FMT, int EPI, bool DBG>
 hipError_t launch_one(const ExpertArgs& a, hipStream_t s) {
     // persistent: one workgroup per compute unit, a multiple of 8 (XCDs)
     int grid = cu_count();
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_gemm<EPI, DBG>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<FMT, EPI, DBG>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool gemm_supported(int rows, int cols, int epi) {
+bool gemm_supported(Fmt fmt, int rows, int cols, int epi) {
     if (cols % 256 != 0 || rows < 1) return false;
+    if (fmt == kSign1 && cols % 512 != 0) return false;   // whole 16-byte sub-scale units
+    if (fmt != kGrid1 && fmt != kSign1) return false;
     return epi == kEpiF32 || epi == kEpiSwigluBf16;
 }
 
-hipError_t launch_gemm(Epi epi, const ExpertArgs& a, hipStream_t s) {
-    if (epi == kEpiF32) return a.debug ? launch_one<kEpiF32, true>(a, s) : launch_one<kEpiF32, false>(a, s);
+template <int FMT>
+hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
+    if (epi == kEpiF32) return a.debug ? launch_one<FMT, kEpiF32, true>(a, s) : launch_one<FMT, kEpiF32, false>(a, s);
     if (epi == kEpiSwigluBf16)
-        return a.debug ? launch_one<kEpiSwigluBf16, true>(a, s) : launch_one<kEpiSwigluBf16, false>(a, s);
+        return a.debug ? launch_one<FMT, kEpiSwigluBf16, true>(a, s) : launch_one<FMT, kEpiSwigluBf16, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
+    if (fmt == kSign1) return launch_fmt<kSign1>(epi, a, s);
+    if (fmt == kGrid1) return launch_fmt<kGrid1>(epi, a, s);
     return hipErrorInvalidValue;
 }
 

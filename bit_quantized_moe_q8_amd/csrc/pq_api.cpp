@@ -536,7 +536,7 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w* w, const pq_grid1_w* w_up,
         if (!aligned(w->qs, 16) || !aligned(w->qh, 8) || !aligned(w->d, 2) ||
             !aligned(w->grid, 16))
             return PQ_ERR_ALIGN;
-        if (!pqk::gemm_supported(w->rows, w->cols, epilogue)) return PQ_ERR_UNSUPPORTED;
+        if (!pqk::gemm_supported(pqk::kGrid1, w->rows, w->cols, epilogue)) return PQ_ERR_UNSUPPORTED;
         if (g->n_tokens == 0) return PQ_OK;
         if (!x) return PQ_ERR_NULL;
         if (!aligned(x, 16)) return PQ_ERR_ALIGN;
@@ -555,7 +555,48 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w* w, const pq_grid1_w* w_up,
         a.xb = x;
         a.out0 = out0;
         fill_debug(a, dbg);
-        return from_hip(pqk::launch_gemm(static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
+        return from_hip(pqk::launch_gemm(pqk::kGrid1, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
+    });
+}
+
+pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w* w, const pq_sign1_w* w_up,
+                                         const pq_groups* g, const uint16_t* x, int32_t act_by_token,
+                                         int32_t epilogue, void* out0, const pq_debug* dbg,
+                                         pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->signs || !w->sc || !w->d) return PQ_ERR_NULL;
+        pq_status st = check_groups(g);
+        if (st != PQ_OK) return st;
+        if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
+        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, nullptr, false)) != PQ_OK)
+            return st;
+        if (epilogue == PQ_EPI_SWIGLU_BF16) {
+            if (!w_up->signs || !w_up->sc || !w_up->d) return PQ_ERR_NULL;
+            if (w_up->n_experts != w->n_experts || w_up->rows != w->rows || w_up->cols != w->cols)
+                return PQ_ERR_SHAPE;
+            if (!aligned(w_up->signs, 16) || !aligned(w_up->sc, 16) || !aligned(w_up->d, 2))
+                return PQ_ERR_ALIGN;
+        }
+        if (!aligned(w->signs, 16) || !aligned(w->sc, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+        if (!pqk::gemm_supported(pqk::kSign1, w->rows, w->cols, epilogue)) return PQ_ERR_UNSUPPORTED;
+        if (g->n_tokens == 0) return PQ_OK;
+        if (!x) return PQ_ERR_NULL;
+        if (!aligned(x, 16)) return PQ_ERR_ALIGN;
+        pqk::ExpertArgs a{};
+        a.qs[0] = w->signs;
+        a.sc[0] = w->sc;
+        a.d[0] = w->d;
+        a.qs[1] = w_up ? w_up->signs : nullptr;
+        a.sc[1] = w_up ? w_up->sc : nullptr;
+        a.d[1] = w_up ? w_up->d : nullptr;
+        a.rows = w->rows;
+        a.cols = w->cols;
+        fill_groups(a, g);
+        a.act_by_token = act_by_token ? 1 : 0;
+        a.xb = x;
+        a.out0 = out0;
+        fill_debug(a, dbg);
+        return from_hip(pqk::launch_gemm(pqk::kSign1, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
     });
 }
 

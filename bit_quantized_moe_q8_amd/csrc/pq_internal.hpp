@@ -96,8 +96,8 @@ bool matvec_supported(Fmt fmt, int cols);
 hipError_t launch_tile_q8(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
 bool tile_q8_supported(int cols);
 
-// Prefill dequant-per-tile GEMM (grid1, bf16 MFMA).
-hipError_t launch_gemm(Epi epi, const ExpertArgs& a, hipStream_t s);
-bool gemm_supported(int rows, int cols, int epi);
+// Prefill dequant-per-tile GEMM (grid1 or sign1, bf16 MFMA).
+hipError_t launch_gemm(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
+bool gemm_supported(Fmt fmt, int rows, int cols, int epi);
 
 }  // namespace pqk

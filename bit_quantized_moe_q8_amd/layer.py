@@ -111,7 +111,8 @@ class DecodeLayer:
 
 
 class PrefillLayer:
-    """Buffers and call sequence of one prefill MoE FFN layer (grid1 weights, bf16 x)."""
+    """Buffers and call sequence of one prefill MoE FFN layer (grid1 or sub-scaled
+    sign weights, bf16 x)."""
 
     def __init__(self, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int,
                  device="cuda"):
@@ -136,10 +137,10 @@ class PrefillLayer:
         moe_route_topk(logits, self.k, self.ids, self.w)
         group_tokens_by_expert(self.ids, self.E, self.groups)
 
-    def gate_up(self, x_bf16, gate: Grid1Weights, up: Grid1Weights, dbg=None):
+    def gate_up(self, x_bf16, gate, up, dbg=None):
         moe_gemm_dequant_tile(gate, up, self.groups, x_bf16, True, PQ_EPI_SWIGLU_BF16, self.h, dbg)
 
-    def down(self, down: Grid1Weights, dbg=None):
+    def down(self, down, dbg=None):
         moe_gemm_dequant_tile(down, None, self.groups, self.h, False, PQ_EPI_F32, self.out, dbg)
 
     def combine(self):

@@ -304,6 +304,19 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w *w, const pq_grid1_w *w_up,
                                    const pq_debug *dbg, pq_stream stream);
 
 /*
+ * The same GEMM over sub-scaled sign weights (pq_sign1_w; pxq_llama README,
+ * "What's PXQ?", PXQ1): each weight is decoded on chip to the bf16 of
+ * sign * sc (exact, |w| <= 15) and every 256-column block is scaled by the
+ * row's fp16 anchor in fp32, so out = sum_b d[n] * sum_{k in b} x[k] * sign *
+ * sc, within the fp32 tolerance of the definition.  cols % 512 == 0; signs and
+ * sc 16-byte aligned; otherwise as pq_moe_gemm_dequant_tile.
+ */
+pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
+                                         const pq_groups *g, const uint16_t *x,
+                                         int32_t act_by_token, int32_t epilogue, void *out0,
+                                         const pq_debug *dbg, pq_stream stream);
+
+/*
  * Weighted combine of the per-assignment expert outputs (the scatter of the
  * pxq_llama README, "Run"): y[t][n] = sum_{j<top_k} topk_w[t][j] *
  * out_assign[t*top_k+j][n], summed in slot order j = 0..top_k-1 (deterministic).

@@ -202,3 +202,27 @@ def test_decode1_gate_up_validation(L):
     assert f3(A16, A16, 8, 2, b(pq.Sign1W(A16, A16, A16, 8, 256, 768)), b(pq.Sign1W(A16, A16, A16, 8, 256, 768)),
               *([A16] * 8), A16, S) == pq.PQ_ERR_UNSUPPORTED                    # cols/128 = 6
     assert f3(A16, A16, 8, 9, b(sw), b(sw), *([A16] * 8), A16, S) == pq.PQ_ERR_SHAPE   # top_k > E
+
+
+def test_gemm_validation(L):
+    """The prefill GEMM entry points: grid1 and sub-scaled signs (cols % 512
+    for the latter, sub-scales 16-byte aligned)."""
+    import bit_quantized_moe_q8_amd as pq
+    b = ctypes.byref
+    g = _groups(pq)
+    f = L.pq_moe_gemm_dequant_tile
+    gw = pq.Grid1W(A16, A16, A16, A16, 8, 64, 1024)
+    assert f(b(pq.Grid1W(A16, A16, A16, None, 8, 64, 1024)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_NULL
+    assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 64, 1000)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_SHAPE
+    assert f(b(gw), None, b(g), A1, 1, 0, A16, None, S) == pq.PQ_ERR_ALIGN
+    assert f(b(gw), b(gw), b(g), A16, 1, 1, A16, None, S) == pq.PQ_ERR_UNSUPPORTED   # q8 epilogue
+    f2 = L.pq_moe_gemm_dequant_tile_sign1
+    sw = pq.Sign1W(A16, A16, A16, 8, 64, 1024)
+    assert f2(b(pq.Sign1W(A16, None, A16, 8, 64, 1024)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_NULL
+    assert f2(b(pq.Sign1W(A16, A16, A16, 8, 64, 768)), None, b(g), A16, 1, 0, A16, None, S) \
+        == pq.PQ_ERR_UNSUPPORTED                                                   # cols % 512 != 0
+    assert f2(b(pq.Sign1W(A16, ctypes.c_void_p(0x10008), A16, 8, 64, 1024)), None, b(g), A16, 1, 0, A16,
+              None, S) == pq.PQ_ERR_ALIGN                                          # sc 8-byte aligned only
+    assert f2(b(sw), b(pq.Sign1W(A16, A16, A16, 8, 32, 1024)), b(g), A16, 1, 2, A16, None, S) \
+        == pq.PQ_ERR_SHAPE                                                         # up shape
+    assert f2(b(sw), None, b(_groups(pq, T=0)), None, 1, 0, A16, None, S) == pq.PQ_OK

@@ -26,7 +26,7 @@ def _run(inp, sample=None):
     T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
     A = T * k
     layer = PrefillLayer(T, H, I, E, k, dev())
-    W = {n: weights_to_device("grid1", inp[n], inp["grid"]) for n in ("gate", "up", "down")}
+    W = {n: weights_to_device(cfg["fmt"], inp[n], inp.get("grid")) for n in ("gate", "up", "down")}
     x = to_dev(inp["x_bf16"])
     dbg = {"g": torch.zeros((A, I), device=dev()), "u": torch.zeros((A, I), device=dev()),
            "h": torch.zeros((A, I), device=dev())}
@@ -55,8 +55,9 @@ def _check(inp, gpu, sample=None):
     assert_equal(gpu["ids"], ids, "ids")
     rows = np.arange(A) if sample is None else np.asarray(sample)
     tok = np.arange(A) // k
-    g_ref, tg = moe.grouped_matvec_bf16("grid1", inp["gate"], inp["grid"], ids, inp["x_bf16"], tok, H, rows)
-    u_ref, tu = moe.grouped_matvec_bf16("grid1", inp["up"], inp["grid"], ids, inp["x_bf16"], tok, H, rows)
+    fmt, grid = cfg["fmt"], inp.get("grid")
+    g_ref, tg = moe.grouped_matvec_bf16(fmt, inp["gate"], grid, ids, inp["x_bf16"], tok, H, rows)
+    u_ref, tu = moe.grouped_matvec_bf16(fmt, inp["up"], grid, ids, inp["x_bf16"], tok, H, rows)
     assert_tol(gpu["g"], g_ref[rows], tg[rows], "G")
     assert_tol(gpu["u"], u_ref[rows], tu[rows], "U")
     h_ref = oracle.swiglu(gpu["g"], gpu["u"])
@@ -64,7 +65,7 @@ def _check(inp, gpu, sample=None):
     hb_ref = oracle.float_to_bf16(gpu["h"]).reshape(gpu["h"].shape)
     assert_equal(gpu["hb"], hb_ref, "h (bf16 rounding)")
     assert_equal(gpu["hb_prod"], gpu["hb"], "debug vs production variant")
-    o_ref, to = moe.grouped_matvec_bf16("grid1", inp["down"], inp["grid"], ids, gpu["hb_all"], np.arange(A), I, rows)
+    o_ref, to = moe.grouped_matvec_bf16(fmt, inp["down"], grid, ids, gpu["hb_all"], np.arange(A), I, rows)
     assert_tol(gpu["out"], o_ref[rows], to[rows], "out")
     if sample is None:
         y_ref, ty = oracle.combine(gpu["out_all"], gpu["w"], k)
@@ -78,18 +79,23 @@ def _check(inp, gpu, sample=None):
     (5, 64, 1024, 256, 3, 4),     # most experts empty, single rows
     (130, 1, 512, 256, 1, 5),     # one expert takes every token (3 chunks)
 ])
-def test_prefill_layer_small(T, E, H, I, k, seed):
-    say("prefill small", T, E, H, I, k)
-    inp = wl.make_workload("grid1_moe_prefill_t2048", seed=seed, T=T, E=E, H=H, I=I, top_k=k)
+@pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
+def test_prefill_layer_small(T, E, H, I, k, seed, name):
+    if name.startswith("sign1") and (H % 512 or I % 512):
+        I = 512   # sub-scaled signs need row lengths that are multiples of 512
+        H = max(512, H // 512 * 512)
+    say("prefill small", name, T, E, H, I, k)
+    inp = wl.make_workload(name, seed=seed, T=T, E=E, H=H, I=I, top_k=k)
     gpu = _run(inp)
     _check(inp, gpu)
 
 
-def test_prefill_layer_full_size_sampled():
+@pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
+def test_prefill_layer_full_size_sampled(name):
     """2048 tokens, hidden 4096, intermediate 1536, 256 experts, top-8: all
     experts run on the GPU; 48 assignments (every column) are checked."""
-    say("prefill full size")
-    inp = wl.make_workload("grid1_moe_prefill_t2048")
+    say("prefill full size", name)
+    inp = wl.make_workload(name)
     rng = np.random.default_rng(0)
     A = 2048 * 8
     sample = np.sort(rng.choice(A, size=48, replace=False))
@@ -114,3 +120,60 @@ def test_gemm_partial_column_tiles(N, K, T, E, k):
     A = T * k
     y_ref, t_ref = moe.grouped_matvec_bf16("grid1", planes, grid, ids, x, np.arange(A) // k, K)
     assert_tol(to_host(out), y_ref, t_ref, "out")
+
+
+@pytest.mark.parametrize("N,K,T,E,k", [(100, 512, 40, 3, 2), (300, 1024, 9, 5, 2), (1, 512, 3, 2, 1),
+                                       (64, 4096, 70, 2, 1)])
+def test_gemm_sign1_f32(N, K, T, E, k):
+    """Sub-scaled sign weights through the GEMM (bf16 of sign * sc, the row
+    anchor per block), F32 epilogue, partial column tiles; debug and
+    production launches give the same bits."""
+    say("gemm sign1 f32", N, K, T, E, k)
+    seed = N + K + T
+    planes = wl.stack_experts("sign1", seed, "w", E, N, K)
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = wl.activations_bf16(seed, T, K)
+    g = pq.group_tokens_by_expert(to_dev(ids), E)
+    W = weights_to_device("sign1", planes, None)
+    A = T * k
+    dbg = {"g": torch.zeros((A, N), device=dev())}
+    out = pq.moe_gemm_dequant_tile(W, None, g, to_dev(x), True, pq.PQ_EPI_F32, dbg=dbg)
+    out2 = pq.moe_gemm_dequant_tile(W, None, g, to_dev(x), True, pq.PQ_EPI_F32)
+    torch.cuda.synchronize()
+    y_ref, t_ref = moe.grouped_matvec_bf16("sign1", planes, None, ids, x, np.arange(A) // k, K)
+    assert_tol(to_host(out), y_ref, t_ref, "out")
+    assert_equal(to_host(out2), to_host(out), "debug vs production variant")
+
+
+@pytest.mark.parametrize("I,H,T,E,k", [(96, 1024, 50, 4, 2), (256, 512, 20, 2, 1)])
+def test_gemm_sign1_swiglu(I, H, T, E, k):
+    """Gate/up with the SwiGLU bf16 epilogue over sub-scaled signs: G and U
+    against the oracle, h against the GPU's own G and U, its bf16 rounding
+    bit-exact, production bits equal to the debug launch's."""
+    say("gemm sign1 swiglu", I, H, T, E, k)
+    seed = I + H + T
+    gate = wl.stack_experts("sign1", seed, "gate", E, I, H)
+    up = wl.stack_experts("sign1", seed, "up", E, I, H)
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = wl.activations_bf16(seed, T, H)
+    g = pq.group_tokens_by_expert(to_dev(ids), E)
+    Wg, Wu = weights_to_device("sign1", gate, None), weights_to_device("sign1", up, None)
+    A = T * k
+    dbg = {"g": torch.zeros((A, I), device=dev()), "u": torch.zeros((A, I), device=dev()),
+           "h": torch.zeros((A, I), device=dev())}
+    hb = pq.moe_gemm_dequant_tile(Wg, Wu, g, to_dev(x), True, pq.PQ_EPI_SWIGLU_BF16, dbg=dbg)
+    hb2 = pq.moe_gemm_dequant_tile(Wg, Wu, g, to_dev(x), True, pq.PQ_EPI_SWIGLU_BF16)
+    torch.cuda.synchronize()
+    tok = np.arange(A) // k
+    g_ref, tg = moe.grouped_matvec_bf16("sign1", gate, None, ids, x, tok, H)
+    u_ref, tu = moe.grouped_matvec_bf16("sign1", up, None, ids, x, tok, H)
+    gg, uu, hh = to_host(dbg["g"]), to_host(dbg["u"]), to_host(dbg["h"])
+    assert_tol(gg, g_ref, tg, "G")
+    assert_tol(uu, u_ref, tu, "U")
+    h_ref = oracle.swiglu(gg, uu)
+    assert_tol(hh, h_ref, np.abs(h_ref), "h (fp32)")
+    hb_host = to_host(hb).view(np.uint16) if to_host(hb).dtype != np.uint16 else to_host(hb)
+    assert_equal(hb_host.reshape(hh.shape), oracle.float_to_bf16(hh).reshape(hh.shape), "h (bf16 rounding)")
+    assert_equal(to_host(hb2), to_host(hb), "debug vs production variant")

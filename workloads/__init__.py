@@ -82,6 +82,9 @@ WORKLOADS = {
                                        T=2048, top_k=8, logits="uniform", seed=105),
     "ternary_moe_prefill_q8_t2048": dict(kind="prefill_q8", fmt="ternary", E=256, H=2048, I=768,
                                          T=2048, top_k=8, logits="uniform", seed=106),
+    # sub-scaled signs through the bf16 GEMM at the grid1 prefill shapes
+    "sign1_moe_prefill_t2048": dict(kind="prefill", fmt="sign1", E=256, H=4096, I=1536,
+                                    T=2048, top_k=8, logits="uniform", seed=109),
     # sub-scaled signs through the same tile at the grid1 prefill shapes
     "sign1_moe_prefill_q8_t2048": dict(kind="prefill_q8", fmt="sign1", E=256, H=4096, I=1536,
                                        T=2048, top_k=8, logits="uniform", seed=108),
