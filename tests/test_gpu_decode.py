@@ -383,19 +383,21 @@ def test_decode_layer(name, override, fused):
     _check_layer(inp, gpu)
 
 
-def test_one_token_layer_in_captured_graph():
+@pytest.mark.parametrize("name,override", [("ternary_moe_decode_t1", {}),
+                                           ("sign1_moe_decode_t8", dict(T=1, E=64, H=2048, I=1536, top_k=8))])
+def test_one_token_layer_in_captured_graph(name, override):
     """The one-token layer (two launches: routed gate/up, down with the fused
     combine) captured in a graph and replayed three times, with eager steps
     on other inputs between the replays: routing, q8(h) and y of every replay
     match the oracle (y within tolerance: the fused combine adds the top-k
     terms with atomics, so its last bits can differ between runs)."""
-    say("one-token layer in graph")
-    inp = decode_inputs("ternary_moe_decode_t1")
+    say("one-token layer in graph", name)
+    inp = decode_inputs(name, **override)
     cfg = inp["cfg"]
-    T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
-    layer = DecodeLayer("ternary", T, H, I, E, k, dev())
+    fmt, T, H, I, E, k = cfg["fmt"], cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
+    layer = DecodeLayer(fmt, T, H, I, E, k, dev())
     assert layer.decode1
-    W = {n: weights_to_device("ternary", inp[n]) for n in ("gate", "up", "down")}
+    W = {n: weights_to_device(fmt, inp[n], inp.get("grid")) for n in ("gate", "up", "down")}
     x, logits = to_dev(inp["x"]), to_dev(inp["logits"])
     other_x = to_dev(wl.activations_f32(77, T, H))
     other_lg = to_dev(wl.router_logits(77, T, E, "normal"))
@@ -414,7 +416,7 @@ def test_one_token_layer_in_captured_graph():
         hq, hd = to_host(layer.hq), to_host(layer.hd)
         ok = q8_rows_equal_ignoring_ties(hq, ref["hq"], ref["h"], ref["hd"])
         assert ok.all(), "q8(h) (replay %d)" % rep
-        o_ref, to, _ = moe.grouped_matvec_q8("ternary", inp["down"], None, ref["ids"], hq, hd,
+        o_ref, to, _ = moe.grouped_matvec_q8(fmt, inp["down"], inp.get("grid"), ref["ids"], hq, hd,
                                              np.arange(T * k), I, want_isums=False)
         w = to_host(layer.w)
         y_ref, ty = oracle.combine(o_ref.astype(np.float32), w, k)
