@@ -123,7 +123,8 @@ def test_gemm_partial_column_tiles(N, K, T, E, k):
 
 
 @pytest.mark.parametrize("N,K,T,E,k", [(100, 512, 40, 3, 2), (300, 1024, 9, 5, 2), (1, 512, 3, 2, 1),
-                                       (64, 4096, 70, 2, 1)])
+                                       (64, 4096, 70, 2, 1),
+                                       (48, 512, 100, 1024, 8)])   # 1024 experts, most empty or single rows
 def test_gemm_sign1_f32(N, K, T, E, k):
     """Sub-scaled sign weights through the GEMM (bf16 of sign * sc, the row
     anchor per block), F32 epilogue, partial column tiles; debug and
