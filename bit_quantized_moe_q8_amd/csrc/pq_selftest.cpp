@@ -199,6 +199,34 @@ pq_status run(hipStream_t s) {
     pq_ok(pq_moe_matvec_sign1(&sw, nullptr, &g, dxq.as<int8_t>(), dxd.as<float>(), 1, PQ_EPI_F32,
                               dout.p, nullptr, nullptr, st));
     check_out();
+    // ---- sub-scaled signs in the prefill GEMM (hidden 512: whole 16-byte
+    // sub-scale units), bf16 activations that are small integers (exact)
+    {
+        constexpr int kH2 = 512;
+        std::vector<uint16_t> xb2(kT * kH2);
+        double s2[kT] = {0.0, 0.0};
+        for (int t = 0; t < kT; ++t)
+            for (int c = 0; c < kH2; ++c) {
+                const float v = static_cast<float>((t * 7 + c * 3) % 17 - 8);
+                uint32_t u;
+                std::memcpy(&u, &v, 4);
+                xb2[t * kH2 + c] = static_cast<uint16_t>(u >> 16);
+                s2[t] += v;
+            }
+        std::vector<uint8_t> sg2(static_cast<size_t>(kE) * kRows * kH2 / 8, 0);
+        std::vector<uint8_t> sc2(static_cast<size_t>(kE) * kRows * kH2 / 32, 0x11);
+        DevBuf dxb2, dsg2, dsc2;
+        ok(dxb2.put(xb2) && dsg2.put(sg2) && dsc2.put(sc2));
+        const pq_sign1_w sw2{dsg2.as<uint8_t>(), dsc2.as<uint8_t>(), dsanc.as<uint16_t>(), kE, kRows, kH2};
+        hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
+        pq_ok(pq_moe_gemm_dequant_tile_sign1(&sw2, nullptr, &g, dxb2.as<uint16_t>(), 1, PQ_EPI_F32, dout.p,
+                                             nullptr, st));
+        hip_ok(hipStreamSynchronize(s));
+        std::vector<float> out(kA * kRows);
+        ok(dout.get(out));
+        for (int a = 0; a < kA; ++a)
+            for (int n = 0; n < kRows; ++n) ok(out[a * kRows + n] == static_cast<float>(s2[a / kK]));
+    }
     // ---- the int8-MFMA tile in all three formats (same answers)
     hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
     pq_ok(pq_moe_tile_q8_ternary(&tw, nullptr, &g, dxq.as<int8_t>(), dxd.as<float>(), 1, PQ_EPI_F32,

@@ -379,8 +379,9 @@ pq_status pq_validate_ternary(const pq_ternary_w *w, int32_t *n_bad, pq_stream s
  * in closed form: q8 blocks with max|x| = 127 (scale exactly 1), routing of
  * increasing logits, grouping of a fixed id list, the ternary, grid1 and
  * sub-scaled sign mat-vecs, the int8-MFMA tile in all three formats and the
- * prefill GEMM with all-(+1) weights and unit scales (each output is the
- * exact sum of its activations), the fused prep and combine.  Unlike
+ * prefill GEMM (grid1 and sub-scaled signs) with all-(+1) weights and unit
+ * scales (each output is the exact sum of its activations), the fused prep
+ * and combine.  Unlike
  * every other entry point it allocates device memory and synchronizes
  * `stream`; not for the hot path.  PQ_OK, PQ_ERR_SELFTEST on a wrong answer,
  * PQ_ERR_HIP on a runtime failure.
