@@ -126,8 +126,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    per_matrix = wl.packed_bytes_per_matrix(fmt, I, H)      # gate, up and down have equal size
-    per_expert = 3 * per_matrix
+    per_matrix = wl.packed_bytes_per_matrix(fmt, I, H)      # gate or up ([I][H])
+    # down is [H][I]: the same size for per-256 scales, larger by its extra
+    # rows' anchors for the sub-scaled signs (one anchor per row)
+    per_expert = 2 * per_matrix + wl.packed_bytes_per_matrix(fmt, H, I)
     expect_touched = min(E, T * k)
     touched_est = expect_touched * per_expert
     M = max(1, args.graph_steps)
