@@ -362,6 +362,23 @@ def test_matvec_bf16_vs_numpy():
     assert np.allclose(t, tref, rtol=1e-12)
 
 
+def test_sign1_matvec_bf16_vs_numpy_dequant():
+    """The bf16 prefill oracle path on sub-scaled signs (the reference of the
+    sign1 GEMM): grouped_matvec_bf16 against sign * sc * anchor @ x in fp64,
+    and its term sums against |w| @ |x|."""
+    K, N = 1024, 24
+    planes = wl.stack_experts("sign1", 33, "w", 3, N, K)
+    xb = wl.activations_bf16(33, 2, K)
+    ids = np.array([[2, 0]], np.int32)
+    y, t = moe.grouped_matvec_bf16("sign1", planes, None, ids, xb, np.array([0, 1]), K)
+    for a, e in enumerate(ids.ravel()):
+        W = oracle.unpack_sign1(planes["signs"][e], planes["sc"][e], K).astype(np.float64)
+        Wd = W * planes["d"][e].view(np.float16).astype(np.float64)[:, None]
+        xf = (xb[a].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.all(np.abs(y[a] - Wd @ xf) <= 1e-12 * t[a] + 1e-300)
+        assert np.allclose(t[a], np.abs(Wd) @ np.abs(xf), rtol=1e-12)
+
+
 def test_matvec_thread_count_determinism():
     K = 2048
     qs, d = wl.ternary_expert(17, "w", 0, 768, K)
