@@ -1,10 +1,11 @@
 """Python binding of libpq (include/pq.h): packed 1-bit-class MoE expert kernels for MI355X.
 
-Argument marshalling only: each function checks tensor dtypes, devices and
-contiguity, then calls the C entry point of the same name on torch's current
-HIP stream.  Every step of the computation runs in the library's HIP kernels;
+Argument marshalling only: each function checks tensor dtypes, sizes,
+devices and contiguity on the host (an undersized buffer raises ValueError
+before anything is launched), then calls the C entry point of the same name on
+torch's current HIP stream.  Every step of the computation runs in the library's HIP kernels;
 there is no host fallback, and importing this module fails if libpq.so has not
-been built (``python -m bit_quantized_moe_q8_amd._build``).
+been built (``python bit_quantized_moe_q8_amd/_build.py``).
 """
 from __future__ import annotations
 
@@ -19,6 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libpq.so")
 
 PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE, PQ_ERR_ALIGN, PQ_ERR_UNSUPPORTED, PQ_ERR_HIP, PQ_ERR_SELFTEST = range(7)
 PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 3
+PQ_FMT = {"ternary": 0, "grid1": 1, "sign1": 2}
+PQ_CALL_MATVEC, PQ_CALL_TILE_Q8, PQ_CALL_GEMM, PQ_CALL_DECODE1_GATE_UP = 0, 1, 2, 3
+(PQ_PLAN_MATVEC, PQ_PLAN_MATVEC_PAIRS, PQ_PLAN_MATVEC_TOK1, PQ_PLAN_TILE_Q8, PQ_PLAN_GEMM,
+ PQ_PLAN_DECODE1_ROUTED, PQ_PLAN_DEBUG) = 1, 2, 4, 8, 16, 32, 64
 
 EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",
@@ -27,7 +32,7 @@ EXPORTS = (
     "pq_moe_gemm_dequant_tile", "pq_moe_gemm_dequant_tile_sign1",
     "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1",
     "pq_moe_decode1_gate_up_sign1", "pq_validate_ternary",
-    "pq_selftest", "pq_status_str", "pq_abi_version",
+    "pq_selftest", "pq_plan", "pq_status_str", "pq_abi_version",
 )
 
 
@@ -67,7 +72,7 @@ class Debug(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libpq.so is not built; run: python -m bit_quantized_moe_q8_amd._build")
+        raise ImportError("libpq.so is not built; run: python bit_quantized_moe_q8_amd/_build.py")
     L = ctypes.CDLL(LIB_PATH)
     p, i32 = ctypes.c_void_p, ctypes.c_int32
     sig = {
@@ -113,6 +118,8 @@ def _load():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    L.pq_plan.argtypes = [i32] * 9
+    L.pq_plan.restype = i32
     L.pq_status_str.argtypes = [ctypes.c_int]
     L.pq_status_str.restype = ctypes.c_char_p
     L.pq_abi_version.restype = ctypes.c_int32
@@ -166,6 +173,54 @@ def _dt(t, *dtypes):
         raise TypeError("expected dtype in %s, got %s" % (dtypes, t.dtype))
 
 
+def _need(t, what: str, numel: int, *dtypes):
+    """Host-side check of a buffer the kernels will index: dtype, and at
+    least `numel` elements (an undersized buffer would be read or written
+    out of bounds on the device)."""
+    if t is None:
+        return
+    if dtypes:
+        _dt(t, *dtypes)
+    if t.numel() < numel:
+        raise ValueError("%s holds %d elements, the call needs %d" % (what, t.numel(), numel))
+
+
+_F32 = (torch.float32,)
+_I8 = (torch.int8,)
+_I32 = (torch.int32,)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _need_plane(t, what, shape, *dtypes):
+    _dt(t, *dtypes)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (what, tuple(t.shape), tuple(shape)))
+
+
+def _check_groups(groups, n_tokens=None, top_k=None, n_experts=None):
+    g = groups
+    for v, want, what in ((n_tokens, g.n_tokens, "n_tokens"), (top_k, g.top_k, "top_k"),
+                          (n_experts, g.n_experts, "n_experts")):
+        if v is not None and v != want:
+            raise ValueError("groups were built for %s = %d, the call has %d" % (what, want, v))
+    _need(g.expert_offsets, "expert_offsets", g.n_experts + 1, *_I32)
+    _need(g.sorted_assign, "sorted_assign", g.n_tokens * g.top_k, *_I32)
+    _need(g.active_experts, "active_experts", g.n_experts, *_I32)
+    _need(g.n_active, "n_active", 1, *_I32)
+
+
+def _check_debug(dbg, A, rows, cols, two):
+    if not dbg:
+        return
+    _need(dbg.get("isums"), "dbg isums", A * rows * (cols // 32), *_I32)
+    if two:
+        _need(dbg.get("isums_up"), "dbg isums_up", A * rows * (cols // 32), *_I32)
+    elif dbg.get("isums_up") is not None:
+        raise ValueError("dbg isums_up needs w_up")
+    for f in ("g", "u", "h"):
+        _need(dbg.get(f), "dbg " + f, A * rows, *_F32)
+
+
 @dataclass
 class TernaryWeights:
     """Packed ternary expert tensor: qs uint8 [E][rows][cols/4], d fp16 bits [E][rows][cols/256]."""
@@ -179,8 +234,10 @@ class TernaryWeights:
 
     def cstruct(self) -> TernaryW:
         _dt(self.qs, torch.uint8)
-        _dt(self.d, torch.int16, torch.float16, torch.uint16)
+        if self.qs.dim() != 3:
+            raise ValueError("qs must be [E][rows][cols/4]")
         E, rows, cols = self.shape
+        _need_plane(self.d, "d", (E, rows, cols // 256), torch.int16, torch.float16, torch.uint16)
         return TernaryW(_ptr(self.qs), _ptr(self.d), E, rows, cols)
 
 
@@ -199,9 +256,11 @@ class Sign1Weights:
 
     def cstruct(self) -> Sign1W:
         _dt(self.signs, torch.uint8)
-        _dt(self.sc, torch.uint8)
-        _dt(self.d, torch.int16, torch.float16, torch.uint16)
+        if self.signs.dim() != 3:
+            raise ValueError("signs must be [E][rows][cols/8]")
         E, rows, cols = self.shape
+        _need_plane(self.sc, "sc", (E, rows, cols // 32), torch.uint8)
+        _need_plane(self.d, "d", (E, rows), torch.int16, torch.float16, torch.uint16)
         return Sign1W(_ptr(self.signs), _ptr(self.sc), _ptr(self.d), E, rows, cols)
 
 
@@ -221,10 +280,12 @@ class Grid1Weights:
 
     def cstruct(self) -> Grid1W:
         _dt(self.qs, torch.uint8)
-        _dt(self.qh, torch.int16, torch.uint16)
-        _dt(self.d, torch.int16, torch.float16, torch.uint16)
-        _dt(self.grid, torch.int8)
+        if self.qs.dim() != 3:
+            raise ValueError("qs must be [E][rows][cols/8]")
         E, rows, cols = self.shape
+        _need_plane(self.qh, "qh", (E, rows, cols // 32), torch.int16, torch.uint16)
+        _need_plane(self.d, "d", (E, rows, cols // 256), torch.int16, torch.float16, torch.uint16)
+        _need(self.grid, "grid", 2048 * 8, torch.int8)
         return Grid1W(_ptr(self.qs), _ptr(self.qh), _ptr(self.d), _ptr(self.grid), E, rows, cols)
 
 
@@ -262,10 +323,20 @@ def _debug_struct(dbg):
 
 # ------------------------------------------------------------------ entry points
 
+def plan(call: int, fmt: str, n_tokens: int, top_k: int, n_experts: int, rows: int, cols: int,
+         epilogue: int = PQ_EPI_F32, debug: bool = False) -> int:
+    """pq_plan: the PQ_PLAN_* flags of the kernels an entry point of family
+    `call` launches for these sizes (host only; negative: -status)."""
+    return int(_lib.pq_plan(int(call), PQ_FMT[fmt], int(n_tokens), int(top_k), int(n_experts),
+                            int(rows), int(cols), int(epilogue), int(bool(debug))))
+
+
 def quantize_act_q8(x: torch.Tensor, xq: torch.Tensor = None, xd: torch.Tensor = None):
     """pq_quantize_act_q8: x float32 [rows][cols] -> (xq int8 [rows][cols], xd float32 [rows][cols/32])."""
     _dt(x, torch.float32)
     rows, cols = x.shape
+    _need(xq, "xq", rows * cols, *_I8)
+    _need(xd, "xd", rows * (cols // 32), *_F32)
     if xq is None:
         xq = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
     if xd is None:
@@ -278,6 +349,8 @@ def moe_route_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor = None, w
     """pq_moe_route_topk: logits float32 [T][E] -> (ids int32 [T][k], w float32 [T][k])."""
     _dt(logits, torch.float32)
     T, E = logits.shape
+    _need(ids, "ids", T * top_k, *_I32)
+    _need(w, "w", T * top_k, *_F32)
     if ids is None:
         ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
     if w is None:
@@ -292,6 +365,7 @@ def group_tokens_by_expert(ids: torch.Tensor, n_experts: int, groups: GroupBuffe
     T, k = ids.shape
     if groups is None:
         groups = GroupBuffers.empty(T, k, n_experts, ids.device)
+    _check_groups(groups, T, k, n_experts)
     g = groups
     _check("pq_group_tokens_by_expert", _lib.pq_group_tokens_by_expert(
         _ptr(ids), T, k, n_experts, _ptr(g.expert_offsets), _ptr(g.sorted_assign),
@@ -307,6 +381,14 @@ def decode_prep(x: torch.Tensor, logits: torch.Tensor, top_k: int, xq, xd, ids, 
     _dt(logits, torch.float32)
     T, H = x.shape
     E = logits.shape[1]
+    if logits.shape[0] != T:
+        raise ValueError("logits rows %d != tokens %d" % (logits.shape[0], T))
+    _need(xq, "xq", T * H, *_I8)
+    _need(xd, "xd", T * (H // 32), *_F32)
+    _need(ids, "ids", T * top_k, *_I32)
+    _need(w, "w", T * top_k, *_F32)
+    _need(y_zero, "y_zero", T * H, *_F32)
+    _check_groups(groups, T, top_k, E)
     g = groups
     _check("pq_moe_decode_prep", _lib.pq_moe_decode_prep(
         _ptr(x), _ptr(logits), T, H, E, top_k, _ptr(xq), _ptr(xd), _ptr(ids), _ptr(w),
@@ -319,11 +401,34 @@ def decode_prep_supported(n_tokens: int, n_experts: int, top_k: int) -> bool:
     return 1 <= n_tokens <= 16 and n_experts <= 1024 and n_tokens * top_k <= 256 and top_k <= 16
 
 
+def _check_up(w, w_up):
+    if w_up is None:
+        return
+    if type(w_up) is not type(w) or tuple(w_up.shape) != tuple(w.shape):
+        raise ValueError("w_up must be the same format and shape as w")
+
+
 def _matvec(fn_name, w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg):
     _dt(xq, torch.int8)
     _dt(xd, torch.float32)
     E, rows, cols = w.shape
+    _check_up(w, w_up)
+    _check_groups(groups, n_experts=E)
     A = groups.n_tokens * groups.top_k
+    n_act = groups.n_tokens if act_by_token else A
+    _need(xq, "xq", n_act * cols)
+    _need(xd, "xd", n_act * (cols // 32))
+    if epilogue == PQ_EPI_F32:
+        _need(out0, "out0", A * rows, *_F32)
+    elif epilogue == PQ_EPI_SWIGLU_Q8:
+        _need(out0, "out0 (hq)", A * rows, *_I8)
+        _need(out1, "out1 (hd)", A * (rows // 32), *_F32)
+    elif epilogue == PQ_EPI_F32_COMBINE:
+        if out0 is None or out1 is None:
+            raise ValueError("PQ_EPI_F32_COMBINE needs out0 (y) and out1 (topk_w)")
+        _need(out0, "out0 (y)", groups.n_tokens * rows, *_F32)
+        _need(out1, "out1 (topk_w)", A, *_F32)
+    _check_debug(dbg, A, rows, cols, w_up is not None)
     dev = xq.device
     if out0 is None:
         if epilogue == PQ_EPI_F32:
@@ -382,9 +487,18 @@ def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: t
                           act_by_token: bool, epilogue: int = PQ_EPI_F32, out0=None, dbg: dict = None):
     """pq_moe_gemm_dequant_tile (grid1) or pq_moe_gemm_dequant_tile_sign1 (Sign1Weights):
     x bf16 (torch.bfloat16 or int16 bits)."""
-    _dt(x_bf16, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(x_bf16, *_BF16)
     E, rows, cols = w.shape
+    _check_up(w, w_up)
+    _check_groups(groups, n_experts=E)
     A = groups.n_tokens * groups.top_k
+    n_act = groups.n_tokens if act_by_token else A
+    _need(x_bf16, "x", n_act * cols)
+    if epilogue == PQ_EPI_F32:
+        _need(out0, "out0", A * rows, *_F32)
+    else:
+        _need(out0, "out0 (h)", A * rows, *_BF16)
+    _check_debug(dbg, A, rows, cols, w_up is not None)
     if out0 is None:
         dt = torch.float32 if epilogue == PQ_EPI_F32 else torch.bfloat16
         out0 = torch.empty((A, rows), dtype=dt, device=x_bf16.device)
@@ -402,9 +516,12 @@ def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: t
 def moe_combine(out_assign: torch.Tensor, topk_w: torch.Tensor, top_k: int, y: torch.Tensor = None):
     """pq_moe_combine: out_assign float32 [T*k][rows], topk_w float32 [T][k] -> y float32 [T][rows]."""
     _dt(out_assign, torch.float32)
-    _dt(topk_w, torch.float32)
     A, rows = out_assign.shape
+    if A % top_k:
+        raise ValueError("out_assign rows %d are not a multiple of top_k %d" % (A, top_k))
     T = A // top_k
+    _need(topk_w, "topk_w", A, *_F32)
+    _need(y, "y", T * rows, *_F32)
     if y is None:
         y = torch.empty((T, rows), dtype=torch.float32, device=out_assign.device)
     _check("pq_moe_combine", _lib.pq_moe_combine(_ptr(out_assign), _ptr(topk_w), T, top_k, rows, _ptr(y), _stream()))
@@ -413,9 +530,9 @@ def moe_combine(out_assign: torch.Tensor, topk_w: torch.Tensor, top_k: int, y: t
 
 def validate_ternary(w: "TernaryWeights", n_bad: torch.Tensor = None) -> torch.Tensor:
     """pq_validate_ternary: device int32 [1] holding the number of code-3 fields in w.qs."""
+    _need(n_bad, "n_bad", 1, *_I32)
     if n_bad is None:
         n_bad = torch.empty(1, dtype=torch.int32, device=w.qs.device)
-    _dt(n_bad, torch.int32)
     cw = w.cstruct()
     _check("pq_validate_ternary", _lib.pq_validate_ternary(ctypes.byref(cw), _ptr(n_bad), _stream()))
     return n_bad
@@ -435,6 +552,19 @@ def moe_decode1_gate_up(gate, up, x: torch.Tensor, logits: torch.Tensor, top_k: 
     _dt(x, torch.float32)
     _dt(logits, torch.float32)
     E = logits.shape[-1]
+    Eg, I, H = gate.shape
+    _check_up(gate, up)
+    if Eg != E:
+        raise ValueError("logits cover %d experts, the weights %d" % (E, Eg))
+    if x.numel() != H or logits.numel() != E:
+        raise ValueError("one token: x must hold %d values and logits %d" % (H, E))
+    for t, what, n, dts in ((ids, "ids", top_k, _I32), (w, "w", top_k, _F32), (hq, "hq", top_k * I, _I8),
+                            (hd, "hd", top_k * (I // 32), _F32)):
+        if t is None:
+            raise ValueError("%s is required" % what)
+        _need(t, what, n, *dts)
+    _need(y_zero, "y_zero", H, *_F32)
+    _check_groups(groups, 1, top_k, E)
     fn = ("pq_moe_decode1_gate_up_ternary" if isinstance(gate, TernaryWeights)
           else "pq_moe_decode1_gate_up_sign1" if isinstance(gate, Sign1Weights)
           else "pq_moe_decode1_gate_up_grid1")

@@ -27,8 +27,20 @@ FLAGS = [
 FILE_FLAGS = {"k_tile_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """The object is older than its source or any header of csrc/include."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".hpp")]
+    deps.append(os.path.join(os.path.dirname(HERE), "include", "pq.h"))
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -36,11 +48,12 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpq.so (always rebuilds)."""
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source and link libpq.so (always rebuilds, unless
+    `incremental`: then only sources older than their objects' inputs)."""
     os.makedirs(OBJDIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, incremental), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,4 +66,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)

@@ -70,9 +70,6 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kTileRows = 32;      // q8 block of the SwiGLU epilogue; tiles are 1, 2 or 4 of these
 constexpr int kMaxTileShift = 2;
 constexpr int kDepth = 4;          // row iterations of weight loads in flight per wave
-// Assignments from which an expert goes to the int8-MFMA tile kernel
-// (measured on the skewed 64-token decode: 6 and 8 best, 4 and 16 slower).
-constexpr int kHeavyMin = 8;
 
 template <int FMT>
 struct FmtInfo;
@@ -562,32 +559,32 @@ hipError_t launch_epi(Epi epi, const ExpertArgs& a, hipStream_t s) {
 }
 
 template <int FMT, int LPR>
-hipError_t launch_mt(Epi epi, const ExpertArgs& a, hipStream_t s) {
+hipError_t launch_mt(Epi epi, const ExpertArgs& a, bool pairs, hipStream_t s) {
     // One token: every expert sees one activation row.  Up to one assignment
     // per expert on average: pairs (single rows for grid1 and sign1, whose
     // table lookups already hold more registers), passes repeated for the rare
-    // heavier expert.  Otherwise pairs of assignments, each its own work item
-    // (measured faster than groups of four or eight on the skewed 64-token
-    // decode: fewer idle dot products for the many one-assignment experts).
-    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    // heavier expert.  Otherwise (`pairs`, PQ_PLAN_MATVEC_PAIRS) pairs of
+    // assignments, each its own work item (measured faster than groups of
+    // four or eight on the skewed 64-token decode: fewer idle dot products
+    // for the many one-assignment experts).
     if (a.n_tokens <= 1) return launch_epi<FMT, LPR, 1, false>(epi, a, s);
     constexpr int kMtPair = (FMT == kTernary) ? 2 : 1;
-    if (A <= a.n_experts) return launch_epi<FMT, LPR, kMtPair, false>(epi, a, s);
+    if (!pairs) return launch_epi<FMT, LPR, kMtPair, false>(epi, a, s);
     return launch_epi<FMT, LPR, 2, true>(epi, a, s);
 }
 
 template <int FMT>
-hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
+hipError_t launch_fmt(Epi epi, const ExpertArgs& a, bool pairs, hipStream_t s) {
     switch (a.cols / FmtInfo<FMT>::kChunkWeights) {
-        case 2: return launch_mt<FMT, 2>(epi, a, s);
-        case 4: return launch_mt<FMT, 4>(epi, a, s);
-        case 8: return launch_mt<FMT, 8>(epi, a, s);
-        case 12: return launch_mt<FMT, 12>(epi, a, s);
-        case 16: return launch_mt<FMT, 16>(epi, a, s);
-        case 24: return launch_mt<FMT, 24>(epi, a, s);
-        case 32: return launch_mt<FMT, 32>(epi, a, s);
-        case 48: return launch_mt<FMT, 48>(epi, a, s);
-        case 64: return launch_mt<FMT, 64>(epi, a, s);
+        case 2: return launch_mt<FMT, 2>(epi, a, pairs, s);
+        case 4: return launch_mt<FMT, 4>(epi, a, pairs, s);
+        case 8: return launch_mt<FMT, 8>(epi, a, pairs, s);
+        case 12: return launch_mt<FMT, 12>(epi, a, pairs, s);
+        case 16: return launch_mt<FMT, 16>(epi, a, pairs, s);
+        case 24: return launch_mt<FMT, 24>(epi, a, pairs, s);
+        case 32: return launch_mt<FMT, 32>(epi, a, pairs, s);
+        case 48: return launch_mt<FMT, 48>(epi, a, pairs, s);
+        case 64: return launch_mt<FMT, 64>(epi, a, pairs, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -607,17 +604,18 @@ hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
     // Per-expert choice by load: with more assignments than experts (the
     // split grouping) an expert holding at least kHeavyMin of them runs on
     // the int8-MFMA tile kernel, the rest on the mat-vec.
-    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    const int plan = plan_matvec(a.n_tokens, a.top_k, a.n_experts, a.cols, a.debug);
     ExpertArgs m = a;
     m.heavy_min = 0;
-    if (a.n_tokens >= kHeavyMin && A > a.n_experts && tile_q8_supported(a.cols)) {
+    if (plan & PQ_PLAN_TILE_Q8) {
         m.heavy_min = kHeavyMin;
         const hipError_t err = launch_tile_q8(fmt, epi, m, s);
         if (err != hipSuccess) return err;
     }
-    if (fmt == kTernary) return launch_fmt<kTernary>(epi, m, s);
-    if (fmt == kSign1) return launch_fmt<kSign1>(epi, m, s);
-    return launch_fmt<kGrid1>(epi, m, s);
+    const bool pairs = (plan & PQ_PLAN_MATVEC_PAIRS) != 0;
+    if (fmt == kTernary) return launch_fmt<kTernary>(epi, m, pairs, s);
+    if (fmt == kSign1) return launch_fmt<kSign1>(epi, m, pairs, s);
+    return launch_fmt<kGrid1>(epi, m, pairs, s);
 }
 
 }  // namespace pqk

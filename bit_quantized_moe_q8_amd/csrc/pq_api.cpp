@@ -30,6 +30,21 @@ int cu_count() {
     return v;
 }
 
+int plan_matvec(int n_tokens, int top_k, int n_experts, int cols, bool debug) {
+    if (n_tokens <= 0) return 0;
+    const int dbg = debug ? PQ_PLAN_DEBUG : 0;
+    // one token: the one-token kernel (its debug outputs come from the
+    // grouped kernel, one assignment group per expert)
+    if (n_tokens == 1) return (debug ? PQ_PLAN_MATVEC : PQ_PLAN_MATVEC_TOK1) | dbg;
+    const int64_t A = int64_t(n_tokens) * top_k;
+    if (A <= n_experts) return PQ_PLAN_MATVEC | dbg;
+    // more assignments than experts: pairs of assignments per work item, and
+    // in a batch of kHeavyMin+ tokens the experts holding kHeavyMin+
+    // assignments on the int8-MFMA tile
+    const bool heavy = n_tokens >= kHeavyMin && tile_q8_supported(cols);
+    return PQ_PLAN_MATVEC_PAIRS | (heavy ? PQ_PLAN_TILE_Q8 : 0) | dbg;
+}
+
 }  // namespace pqk
 
 namespace {
@@ -328,7 +343,8 @@ pq_status sign1_args(const pq_sign1_w* w, const pq_sign1_w* w_up, const pq_group
 
 pq_status launch_matvec_any(pqk::Fmt fmt, int32_t epilogue, const pqk::ExpertArgs& a,
                             const pq_debug* dbg, pq_stream stream) {
-    if (a.n_tokens == 1 && !dbg)
+    const int plan = pqk::plan_matvec(a.n_tokens, a.top_k, a.n_experts, a.cols, dbg != nullptr);
+    if (plan & PQ_PLAN_MATVEC_TOK1)
         return from_hip(pqk::launch_matvec_tok1(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
     return from_hip(pqk::launch_matvec(fmt, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
 }
@@ -650,6 +666,38 @@ pq_status pq_moe_decode1_gate_up_sign1(const float* x, const float* logits, int3
                                expert_offsets, sorted_assign, active_experts, n_active, hq, hd,
                                y_zero, stream);
     });
+}
+
+int32_t pq_plan(int32_t call, int32_t fmt, int32_t n_tokens, int32_t top_k, int32_t n_experts,
+                int32_t rows, int32_t cols, int32_t epilogue, int32_t debug) {
+    try {
+        if (fmt < PQ_FMT_TERNARY || fmt > PQ_FMT_SIGN1) return -PQ_ERR_UNSUPPORTED;
+        const pqk::Fmt f = static_cast<pqk::Fmt>(fmt);
+        if (n_tokens < 0 || n_experts < 1 || n_experts > kMaxExperts) return -PQ_ERR_SHAPE;
+        if (top_k < 1 || top_k > kMaxTopK || top_k > n_experts) return -PQ_ERR_SHAPE;
+        if (int64_t(n_tokens) * top_k > kMaxAssign) return -PQ_ERR_SHAPE;
+        if (rows < 1 || cols < 256 || cols % 256 != 0) return -PQ_ERR_SHAPE;
+        const int dbg = debug ? PQ_PLAN_DEBUG : 0;
+        switch (call) {
+            case PQ_CALL_MATVEC:
+                if (!pqk::matvec_supported(f, cols)) return -PQ_ERR_UNSUPPORTED;
+                return pqk::plan_matvec(n_tokens, top_k, n_experts, cols, debug != 0);
+            case PQ_CALL_TILE_Q8:
+                if (!pqk::tile_q8_supported(cols)) return -PQ_ERR_UNSUPPORTED;
+                return n_tokens ? (PQ_PLAN_TILE_Q8 | dbg) : 0;
+            case PQ_CALL_GEMM:
+                if (!pqk::gemm_supported(f, rows, cols, epilogue)) return -PQ_ERR_UNSUPPORTED;
+                return n_tokens ? (PQ_PLAN_GEMM | dbg) : 0;
+            case PQ_CALL_DECODE1_GATE_UP:
+                if (debug) return -PQ_ERR_UNSUPPORTED;
+                if (!pqk::matvec_supported(f, cols) || rows % 32 != 0) return -PQ_ERR_UNSUPPORTED;
+                return PQ_PLAN_DECODE1_ROUTED;
+            default:
+                return -PQ_ERR_UNSUPPORTED;
+        }
+    } catch (...) {
+        return -PQ_ERR_HIP;
+    }
 }
 
 pq_status pq_validate_ternary(const pq_ternary_w* w, int32_t* n_bad, pq_stream stream) {

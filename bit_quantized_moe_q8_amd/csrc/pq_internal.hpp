@@ -5,10 +5,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/pq.h"
+
 namespace pqk {
 
 constexpr int kGridEntries = 2048;  // grid1 codebook entries of 8 int8 values
 constexpr int kMaxExperts = 1024;   // experts per layer accepted by every entry point
+// Assignments from which an expert of a large decode batch goes to the
+// int8-MFMA tile kernel (measured on the skewed 64-token decode: 6 and 8
+// best, 4 and 16 slower); also the least token count for that split.
+constexpr int kHeavyMin = 8;
 
 // Number of compute units of the current device (cached per device).
 int cu_count();
@@ -65,6 +71,11 @@ struct ExpertArgs {
     // tile kernel (which takes exactly those); 0: the mat-vec takes all.
     int heavy_min;
 };
+
+// Kernels (PQ_PLAN_* flags) of a q8 expert call of the mat-vec family on
+// argument sizes the entry point has accepted: the one decision every
+// launcher of that family and pq_plan share.
+int plan_matvec(int n_tokens, int top_k, int n_experts, int cols, bool debug);
 
 // Decode mat-vec; returns hipErrorInvalidValue when no kernel matches cols.
 hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);

@@ -80,6 +80,28 @@ enum {
     PQ_EPI_F32_COMBINE = 3  /* out0 = float y [n_tokens][rows] (+=), out1 = float topk_w */
 };
 
+/* Weight formats (pq_plan). */
+enum { PQ_FMT_TERNARY = 0, PQ_FMT_GRID1 = 1, PQ_FMT_SIGN1 = 2 };
+
+/* Entry-point families (pq_plan). */
+enum {
+    PQ_CALL_MATVEC = 0,          /* pq_moe_matvec_{ternary,grid1,sign1} */
+    PQ_CALL_TILE_Q8 = 1,         /* pq_moe_tile_q8_{ternary,grid1,sign1} */
+    PQ_CALL_GEMM = 2,            /* pq_moe_gemm_dequant_tile{,_sign1} */
+    PQ_CALL_DECODE1_GATE_UP = 3  /* pq_moe_decode1_gate_up_{ternary,grid1,sign1} */
+};
+
+/* Kernels a call launches (bit flags returned by pq_plan). */
+enum {
+    PQ_PLAN_MATVEC = 1,          /* grouped mat-vec, all of an expert's assignments per work item */
+    PQ_PLAN_MATVEC_PAIRS = 2,    /* grouped mat-vec, pairs of an expert's assignments per work item */
+    PQ_PLAN_MATVEC_TOK1 = 4,     /* one-token mat-vec (one workgroup per slot and 32-row tile) */
+    PQ_PLAN_TILE_Q8 = 8,         /* int8-MFMA tile (every expert, or with MATVEC_PAIRS those of 8+ assignments) */
+    PQ_PLAN_GEMM = 16,           /* bf16 dequant-per-tile MFMA GEMM */
+    PQ_PLAN_DECODE1_ROUTED = 32, /* one-token gate/up that routes and quantizes itself */
+    PQ_PLAN_DEBUG = 64           /* the kernels' debug variants (dbg != NULL) */
+};
+
 /* hipStream_t, passed as an opaque pointer; NULL = null stream. */
 typedef void *pq_stream;
 
@@ -370,13 +392,18 @@ pq_status pq_moe_decode1_gate_up_sign1(const float *x, const float *logits, int3
  * number of 2-bit codes equal to 3 in w->qs (an invalid code: the format has
  * 0 -> 0, 1 -> +1, 2 -> -1 only, and the kernels' output on code 3 is
  * unspecified).  One workgroup streams the whole plane (meant for load time,
- * not the hot path); qs 16-byte aligned.
+ * not the hot path); qs 16-byte aligned.  A check of packed codes before the
+ * fused path trusts them, as the pxq_llama README ("Updates - 2026-07-30")
+ * does with its one-shot self-check of the 1-bit sign book.
  */
 pq_status pq_validate_ternary(const pq_ternary_w *w, int32_t *n_bad, pq_stream stream);
 
 /*
- * Known-answer self test of every kernel on tiny inputs whose results follow
- * in closed form: q8 blocks with max|x| = 127 (scale exactly 1), routing of
+ * Known-answer self test of every kernel (the runtime self test the Parallax
+ * 8B kappa article runs after building its runtime, "Which runtime is
+ * needed"; the one-shot self-check the pxq_llama README, "Updates -
+ * 2026-07-30", runs before trusting its fused 1-bit path) on tiny inputs
+ * whose results follow in closed form: q8 blocks with max|x| = 127 (scale exactly 1), routing of
  * increasing logits, grouping of a fixed id list, the ternary, grid1 and
  * sub-scaled sign mat-vecs, the int8-MFMA tile in all three formats and the
  * prefill GEMM (grid1 and sub-scaled signs) with all-(+1) weights and unit
@@ -387,6 +414,21 @@ pq_status pq_validate_ternary(const pq_ternary_w *w, int32_t *n_bad, pq_stream s
  * PQ_ERR_HIP on a runtime failure.
  */
 pq_status pq_selftest(pq_stream stream);
+
+/*
+ * Which kernels an entry point of family `call` (PQ_CALL_*) launches for
+ * weights of format `fmt` (PQ_FMT_*) with these sizes, as PQ_PLAN_* flags: the
+ * same decision the entry point itself takes (the pages choose between a
+ * mat-vec and a tiled kernel by batch size: Parakon Runtime README, "How it
+ * works"; the pxq_llama README, "Updates - 2026-07-28", reports a decode
+ * kernel that silently never ran at a large batch, which a test of the
+ * dispatch catches).  `debug` != 0 plans a call with dbg != NULL.  Host only:
+ * no HIP call, nothing enqueued.  Returns 0 when the call launches nothing
+ * (n_tokens == 0) and -PQ_ERR_SHAPE / -PQ_ERR_UNSUPPORTED for arguments the
+ * entry point rejects for their sizes alone.
+ */
+int32_t pq_plan(int32_t call, int32_t fmt, int32_t n_tokens, int32_t top_k, int32_t n_experts,
+                int32_t rows, int32_t cols, int32_t epilogue, int32_t debug);
 
 /* Human-readable name of a status code (static storage). */
 const char *pq_status_str(pq_status status);

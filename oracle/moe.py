@@ -140,10 +140,11 @@ def tol_ok(got, ref, tsum, rel=1e-5, abs_=1e-6):
 
 
 def prefill_ffn(inp: dict, assign_subset=None) -> dict:
-    """Free-running oracle chain of one prefill MoE FFN layer (grid1 weights, bf16 x).
+    """Free-running oracle chain of one prefill MoE FFN layer (grid1 or
+    sub-scaled sign weights, bf16 x), ending in the weighted combine y.
 
     assign_subset restricts the expert work to those assignments (the other
-    rows of g, u, h, out stay NaN)."""
+    rows of g, u, h, out stay NaN) and skips the combine (y is None)."""
     cfg = inp["cfg"]
     fmt, k, H, I, E = cfg["fmt"], cfg["top_k"], cfg["H"], cfg["I"], cfg["E"]
     grid = inp.get("grid")
@@ -162,4 +163,8 @@ def prefill_ffn(inp: dict, assign_subset=None) -> dict:
     hb[rows] = float_to_bf16(h[rows].astype(np.float32)).reshape(len(rows), I)
     r["h_bf16"] = hb
     r["out"], r["tout"] = grouped_matvec_bf16(fmt, inp["down"], grid, r["ids"], hb, np.arange(A), I, assign_subset)
+    if assign_subset is None:
+        r["y"], r["ty"] = combine(r["out"].astype(np.float32), r["w"].astype(np.float32), k)
+    else:
+        r["y"], r["ty"] = None, None
     return r

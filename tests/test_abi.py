@@ -226,3 +226,128 @@ def test_gemm_validation(L):
     assert f2(b(sw), b(pq.Sign1W(A16, A16, A16, 8, 32, 1024)), b(g), A16, 1, 2, A16, None, S) \
         == pq.PQ_ERR_SHAPE                                                         # up shape
     assert f2(b(sw), None, b(_groups(pq, T=0)), None, 1, 0, A16, None, S) == pq.PQ_OK
+
+
+# ------------------------------------------------------- dispatch plan (host only)
+
+def test_plan_of_each_workload():
+    """Which kernels each entry point launches at the workload shapes: the
+    routed one-token gate/up at one token, the one-token mat-vec for its down
+    projection, the grouped mat-vec at 8 tokens, the tile for the heavy experts
+    of the skewed 64-token batch, the GEMM for prefill, every expert on the tile
+    at 2048 tokens with q8 activations."""
+    import bit_quantized_moe_q8_amd as pq
+    P = pq
+    # one token, ternary: gate/up routed launch, down one-token mat-vec
+    assert pq.plan(P.PQ_CALL_DECODE1_GATE_UP, "ternary", 1, 8, 128, 768, 2048, P.PQ_EPI_SWIGLU_Q8) == P.PQ_PLAN_DECODE1_ROUTED
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 1, 8, 128, 2048, 768, P.PQ_EPI_F32_COMBINE) == P.PQ_PLAN_MATVEC_TOK1
+    # the debug outputs of a one-token call come from the grouped kernel
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 1, 8, 128, 768, 2048, P.PQ_EPI_SWIGLU_Q8, True) == \
+        P.PQ_PLAN_MATVEC | P.PQ_PLAN_DEBUG
+    # 8 tokens over 256 grid1 experts: 64 assignments <= 256 experts
+    for fmt in ("grid1", "sign1"):
+        assert pq.plan(P.PQ_CALL_MATVEC, fmt, 8, 8, 256, 1536, 4096, P.PQ_EPI_SWIGLU_Q8) == P.PQ_PLAN_MATVEC
+    # 64 skewed tokens: pairs of assignments, heavy experts on the tile
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 64, 8, 256, 768, 2048, P.PQ_EPI_SWIGLU_Q8) == \
+        P.PQ_PLAN_MATVEC_PAIRS | P.PQ_PLAN_TILE_Q8
+    # fewer than 8 tokens but more assignments than experts: pairs, no tile
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 4, 2, 3, 256, 512) == P.PQ_PLAN_MATVEC_PAIRS
+    # 2048 tokens with q8 activations: the mat-vec entry hands every expert
+    # with 8+ assignments to the tile (all of them at this load)
+    assert pq.plan(P.PQ_CALL_MATVEC, "grid1", 2048, 8, 256, 1536, 4096, P.PQ_EPI_SWIGLU_Q8) & P.PQ_PLAN_TILE_Q8
+    assert pq.plan(P.PQ_CALL_TILE_Q8, "grid1", 2048, 8, 256, 1536, 4096, P.PQ_EPI_SWIGLU_Q8) == P.PQ_PLAN_TILE_Q8
+    # prefill GEMM, both formats
+    assert pq.plan(P.PQ_CALL_GEMM, "grid1", 2048, 8, 256, 1536, 4096, P.PQ_EPI_SWIGLU_BF16) == P.PQ_PLAN_GEMM
+    assert pq.plan(P.PQ_CALL_GEMM, "sign1", 2048, 8, 256, 4096, 1536, P.PQ_EPI_F32) == P.PQ_PLAN_GEMM
+    # sub-scaled signs on the GEMM need rows of a multiple of 512 weights
+    assert pq.plan(P.PQ_CALL_GEMM, "sign1", 2048, 8, 256, 4096, 768, P.PQ_EPI_F32) == -P.PQ_ERR_UNSUPPORTED
+    assert pq.plan(P.PQ_CALL_GEMM, "ternary", 2048, 8, 256, 1536, 4096, P.PQ_EPI_F32) == -P.PQ_ERR_UNSUPPORTED
+    # the single 1024 x 1024 matrix: E = T = k = 1 takes the one-token kernel
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 1, 1, 1, 1024, 1024) == P.PQ_PLAN_MATVEC_TOK1
+    # nothing to do, invalid sizes
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 0, 8, 128, 768, 2048) == 0
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 1, 9, 8, 768, 2048) == -P.PQ_ERR_SHAPE
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 1, 8, 128, 768, 2000) == -P.PQ_ERR_SHAPE
+    assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 1, 8, 128, 768, 8192) == -P.PQ_ERR_UNSUPPORTED
+    assert pq.plan(P.PQ_CALL_DECODE1_GATE_UP, "grid1", 1, 8, 128, 768, 2048, P.PQ_EPI_SWIGLU_Q8, True) == \
+        -P.PQ_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------ binding: sizes checked on the host
+
+def _cpu_ternary(E, N, K):
+    import torch
+    import bit_quantized_moe_q8_amd as pq
+    return pq.TernaryWeights(torch.zeros((E, N, K // 4), dtype=torch.uint8),
+                             torch.zeros((E, N, K // 256), dtype=torch.int16))
+
+
+def test_binding_rejects_undersized_buffers():
+    """Every wrapper checks dtype and size of each buffer before the C call;
+    host tensors of the wrong size raise ValueError/TypeError before the
+    device check (so nothing here needs a GPU)."""
+    import torch
+    import bit_quantized_moe_q8_amd as pq
+    f32, i8, i32 = torch.float32, torch.int8, torch.int32
+    x = torch.zeros((2, 64), dtype=f32)
+    with pytest.raises(ValueError, match="xq"):
+        pq.quantize_act_q8(x, torch.zeros(127, dtype=i8), torch.zeros(4, dtype=f32))
+    with pytest.raises(ValueError, match="xd"):
+        pq.quantize_act_q8(x, torch.zeros(128, dtype=i8), torch.zeros(3, dtype=f32))
+    with pytest.raises(TypeError):
+        pq.quantize_act_q8(x, torch.zeros(128, dtype=i32), torch.zeros(4, dtype=f32))
+    lg = torch.zeros((3, 16), dtype=f32)
+    with pytest.raises(ValueError, match="ids"):
+        pq.moe_route_topk(lg, 4, torch.zeros(11, dtype=i32), torch.zeros(12, dtype=f32))
+    ids = torch.zeros((3, 4), dtype=i32)
+    g = pq.GroupBuffers(torch.zeros(16, dtype=i32), torch.zeros(12, dtype=i32), torch.zeros(16, dtype=i32),
+                        torch.zeros(1, dtype=i32), 3, 4, 16)
+    with pytest.raises(ValueError, match="expert_offsets"):
+        pq.group_tokens_by_expert(ids, 16, g)
+    g = pq.GroupBuffers.empty(3, 4, 16, "cpu")
+    with pytest.raises(ValueError, match="n_experts"):
+        pq.group_tokens_by_expert(ids, 8, g)
+    # mat-vec: activations, outputs, weights, debug
+    W = _cpu_ternary(16, 64, 256)
+    xq, xd = torch.zeros((3, 256), dtype=i8), torch.zeros((3, 8), dtype=f32)
+    with pytest.raises(ValueError, match="xq"):
+        pq.moe_matvec_ternary(W, None, g, xq, xd, False)      # by assignment: 12 rows needed
+    xq12, xd12 = torch.zeros((12, 256), dtype=i8), torch.zeros((12, 8), dtype=f32)
+    with pytest.raises(ValueError, match="out0"):
+        pq.moe_matvec_ternary(W, None, g, xq12, xd12, False, pq.PQ_EPI_F32, torch.zeros((12, 63), dtype=f32))
+    with pytest.raises(ValueError, match="hd"):
+        pq.moe_matvec_ternary(W, W, g, xq, xd, True, pq.PQ_EPI_SWIGLU_Q8, torch.zeros((12, 64), dtype=i8),
+                              torch.zeros((12, 1), dtype=f32))
+    with pytest.raises(ValueError, match="topk_w"):
+        pq.moe_matvec_ternary(W, None, g, xq12, xd12, False, pq.PQ_EPI_F32_COMBINE,
+                              torch.zeros((3, 64), dtype=f32), torch.zeros(11, dtype=f32))
+    with pytest.raises(ValueError, match="w_up"):
+        pq.moe_matvec_ternary(W, _cpu_ternary(16, 32, 256), g, xq, xd, True, pq.PQ_EPI_SWIGLU_Q8)
+    with pytest.raises(ValueError, match="dbg isums"):
+        pq.moe_matvec_ternary(W, None, g, xq12, xd12, False, dbg={"isums": torch.zeros(10, dtype=i32)})
+    bad_d = pq.TernaryWeights(W.qs, torch.zeros((16, 64, 2), dtype=torch.int16))
+    with pytest.raises(ValueError, match="d has shape"):
+        pq.moe_matvec_ternary(bad_d, None, g, xq12, xd12, False, pq.PQ_EPI_F32, torch.zeros((12, 64), dtype=f32))
+    # GEMM and combine
+    Wg = pq.Grid1Weights(torch.zeros((16, 64, 32), dtype=torch.uint8), torch.zeros((16, 64, 8), dtype=torch.int16),
+                         torch.zeros((16, 64, 1), dtype=torch.int16), torch.zeros((2048, 8), dtype=i8))
+    with pytest.raises(ValueError, match="x holds"):
+        pq.moe_gemm_dequant_tile(Wg, None, g, torch.zeros((3, 256), dtype=torch.bfloat16), False)
+    with pytest.raises(ValueError, match="grid"):
+        pq.moe_gemm_dequant_tile(pq.Grid1Weights(Wg.qs, Wg.qh, Wg.d, torch.zeros(100, dtype=i8)), None, g,
+                                 torch.zeros((12, 256), dtype=torch.bfloat16), False, pq.PQ_EPI_F32,
+                                 torch.zeros((12, 64), dtype=f32))
+    with pytest.raises(ValueError, match="topk_w"):
+        pq.moe_combine(torch.zeros((12, 64), dtype=f32), torch.zeros(11, dtype=f32), 4)
+    with pytest.raises(ValueError, match="multiple of top_k"):
+        pq.moe_combine(torch.zeros((10, 64), dtype=f32), torch.zeros(12, dtype=f32), 4)
+    # one-token gate/up
+    g1 = pq.GroupBuffers.empty(1, 4, 16, "cpu")
+    with pytest.raises(ValueError, match="hq"):
+        pq.moe_decode1_gate_up(W, W, torch.zeros((1, 256), dtype=f32), torch.zeros((1, 16), dtype=f32), 4,
+                               torch.zeros(4, dtype=i32), torch.zeros(4, dtype=f32), g1,
+                               torch.zeros((4, 63), dtype=i8), torch.zeros((4, 2), dtype=f32))
+    with pytest.raises(ValueError, match="experts"):
+        pq.moe_decode1_gate_up(W, W, torch.zeros((1, 256), dtype=f32), torch.zeros((1, 8), dtype=f32), 4,
+                               torch.zeros(4, dtype=i32), torch.zeros(4, dtype=f32), g1,
+                               torch.zeros((4, 64), dtype=i8), torch.zeros((4, 2), dtype=f32))

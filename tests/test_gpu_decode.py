@@ -18,8 +18,8 @@ import oracle
 from oracle import moe
 import workloads as wl
 
-from gpu_util import (assert_equal, assert_tol, dev, decode_inputs, q8_rows_equal_ignoring_ties, say,
-                      to_dev, to_host)
+from gpu_util import (assert_equal, assert_plan, assert_tol, dev, decode_inputs, q8h_check, say, to_dev,
+                      to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -161,6 +161,8 @@ def test_ternary_matvec_1024_single_matrix():
     g = pq.group_tokens_by_expert(to_dev(np.zeros((1, 1), np.int32)), 1)
     isums = torch.zeros((1, 1024, 32), dtype=torch.int32, device=dev())
     W = weights_to_device("ternary", planes)
+    assert_plan(pq.PQ_PLAN_MATVEC | pq.PQ_PLAN_DEBUG, pq.PQ_CALL_MATVEC, "ternary", 1, 1, 1, 1024, 1024, debug=True)
+    assert_plan(pq.PQ_PLAN_MATVEC_TOK1, pq.PQ_CALL_MATVEC, "ternary", 1, 1, 1, 1024, 1024)
     out, _ = pq.moe_matvec_ternary(W, None, g, xq_d, xd_d, True, pq.PQ_EPI_F32, dbg={"isums": isums})
     w = oracle.unpack_ternary(planes["qs"][0], 1024)
     y_ref, t_ref, i_ref = oracle.matvec_q8(w, planes["d"][0], xq[0], xd[0])
@@ -226,6 +228,7 @@ def test_matvec_one_expert_many_tokens():
 def test_matvec_one_token(fmt, K, k, abt):
     """The one-token production kernel (no debug outputs), ragged row tiles."""
     say("matvec one token", fmt, K, k, abt)
+    assert_plan(pq.PQ_PLAN_MATVEC_TOK1, pq.PQ_CALL_MATVEC, fmt, 1, k, 16, 72, K)
     _single(fmt, 16, 72, K, 1, k, abt, seed=K + k, want_dbg=False)
 
 
@@ -249,11 +252,8 @@ def test_matvec_one_token_repeated_ids(fmt):
     tok = np.zeros(k, np.int64)
     g_ref, tg, _ = moe.grouped_matvec_q8(fmt, gate, grid, ids, xq, xd, tok, K, False)
     u_ref, tu, _ = moe.grouped_matvec_q8(fmt, up, grid, ids, xq, xd, tok, K, False)
-    h_ref = oracle.swiglu(g_ref.astype(np.float32), u_ref.astype(np.float32))
-    hq_ref, hd_ref = oracle.quantize_q8(h_ref.astype(np.float32))
     hq_g, hd_g = to_host(hq), to_host(hd)
-    assert q8_rows_equal_ignoring_ties(hq_g, hq_ref, h_ref, hd_ref).all()
-    assert_tol(hd_g, hd_ref, hd_ref, "hd", rtol=1e-4)
+    q8h_check(hq_g, hd_g, g_ref, u_ref, tg, tu)
     # the repeated assignments (slots 0, 1, 4 of expert 5) are identical
     assert_equal(hq_g[1], hq_g[0], "repeat hq")
     assert_equal(hq_g[4], hq_g[0], "repeat hq")
@@ -278,6 +278,16 @@ def _run_layer(name, fused=False, **override):
     A = T * k
     layer = DecodeLayer(fmt, T, H, I, E, k, dev(), fused=fused, fused_combine=fused)
     assert layer.fused == fused and layer.fused_combine == fused
+    # the staged check runs the debug variants; the production run after it
+    # (whose hq and y must repeat) takes the production kernels
+    for debug in (True, False):
+        gu = pq.plan(pq.PQ_CALL_MATVEC, fmt, T, k, E, I, H, pq.PQ_EPI_SWIGLU_Q8, debug)
+        dn = pq.plan(pq.PQ_CALL_MATVEC, fmt, T, k, E, H, I, pq.PQ_EPI_F32, debug)
+        assert gu > 0 and dn > 0 and bool(gu & pq.PQ_PLAN_DEBUG) == debug
+        if T == 1 and not debug:
+            assert dn == pq.PQ_PLAN_MATVEC_TOK1
+    if layer.decode1:
+        assert_plan(pq.PQ_PLAN_DECODE1_ROUTED, pq.PQ_CALL_DECODE1_GATE_UP, fmt, T, k, E, I, H, pq.PQ_EPI_SWIGLU_Q8)
     grid = inp.get("grid")
     W = {n: weights_to_device(fmt, inp[n], grid) for n in ("gate", "up", "down")}
     x, logits = to_dev(inp["x"]), to_dev(inp["logits"])
@@ -353,12 +363,12 @@ def _check_layer(inp, gpu):
         # repeat run is bitwise identical
         assert_equal(gpu["hq2"], gpu["hq"], "hq repeat")
         assert_equal(gpu["y2"], gpu["y"], "y repeat")
-    # free-running oracle chain: tokens whose q8 h rows all agree must match y
+    # free-running oracle chain: q8(h) within the bound derived from the
+    # tolerance of g and u; tokens whose q8 h rows all agree must match y
     ref = moe.decode_ffn(inp, want_isums=False)
     same = (ref["hq"] == gpu["hq"]).reshape(T, k, I).all(axis=(1, 2))
-    flips = int((ref["hq"] != gpu["hq"]).sum())
-    say("  free-running q8(h) flips: %d of %d" % (flips, ref["hq"].size))
-    assert flips <= max(2, ref["hq"].size // 10000)
+    flips = q8h_check(gpu["hq"], gpu["hd"], ref["g"], ref["u"], ref["tg"], ref["tu"], "free-running q8(h)")
+    say("  free-running q8(h) flips at rounding boundaries: %d of %d" % (flips, ref["hq"].size))
     ty_free = np.einsum("tj,tjn->tn", np.abs(ref["w"]), ref["tout"].reshape(T, k, H))
     assert_tol(gpu["y"][same], ref["y"][same], ty_free[same], "y (free-running)")
 
@@ -414,8 +424,7 @@ def test_one_token_layer_in_captured_graph(name, override):
         torch.cuda.synchronize()
         assert_equal(to_host(layer.ids), ref["ids"], "ids (replay %d)" % rep)
         hq, hd = to_host(layer.hq), to_host(layer.hd)
-        ok = q8_rows_equal_ignoring_ties(hq, ref["hq"], ref["h"], ref["hd"])
-        assert ok.all(), "q8(h) (replay %d)" % rep
+        q8h_check(hq, hd, ref["g"], ref["u"], ref["tg"], ref["tu"], "q8(h) (replay %d)" % rep)
         o_ref, to, _ = moe.grouped_matvec_q8(fmt, inp["down"], inp.get("grid"), ref["ids"], hq, hd,
                                              np.arange(T * k), I, want_isums=False)
         w = to_host(layer.w)
@@ -510,6 +519,7 @@ def test_decode1_gate_up(fmt, E, H, I, k, kind):
     """The routed one-token gate/up against the oracle, and bit for bit
     against the staged prep + gate/up mat-vec on the same inputs."""
     say("decode1 gate/up", fmt, E, H, I, k, kind)
+    assert_plan(pq.PQ_PLAN_DECODE1_ROUTED, pq.PQ_CALL_DECODE1_GATE_UP, fmt, 1, k, E, I, H, pq.PQ_EPI_SWIGLU_Q8)
     seed = E + H + k
     x = wl.activations_f32(seed, 1, H)
     if kind == "ties":
@@ -559,12 +569,9 @@ def test_decode1_gate_up(fmt, E, H, I, k, kind):
     assert_equal(to_host(g.active_experts)[:k], act, "active")
     xq, xs = oracle.quantize_q8(x)
     tok = np.zeros(k, np.int64)
-    g_ref, _, _ = moe.grouped_matvec_q8(fmt, gate, grid, ids_ref, xq, xs, tok, H, False)
-    u_ref, _, _ = moe.grouped_matvec_q8(fmt, up, grid, ids_ref, xq, xs, tok, H, False)
-    h_ref = oracle.swiglu(g_ref.astype(np.float32), u_ref.astype(np.float32))
-    hq_ref, hd_ref = oracle.quantize_q8(h_ref.astype(np.float32))
-    assert q8_rows_equal_ignoring_ties(to_host(hq), hq_ref, h_ref, hd_ref).all()
-    assert_tol(to_host(hd), hd_ref, hd_ref, "hd", rtol=1e-4)
+    g_ref, tg, _ = moe.grouped_matvec_q8(fmt, gate, grid, ids_ref, xq, xs, tok, H, False)
+    u_ref, tu, _ = moe.grouped_matvec_q8(fmt, up, grid, ids_ref, xq, xs, tok, H, False)
+    q8h_check(to_host(hq), to_host(hd), g_ref, u_ref, tg, tu)
 
 
 # ------------------------------------------------------- load-time helpers

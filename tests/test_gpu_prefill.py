@@ -90,15 +90,32 @@ def test_prefill_layer_small(T, E, H, I, k, seed, name):
     _check(inp, gpu)
 
 
+def _every_expert_sample(inp):
+    """Assignments that cover every expert with rows: the first row of its
+    last 64-row chunk (the GEMM's work unit), its last row, and one row drawn
+    at random from its group; sorted, unique."""
+    cfg = inp["cfg"]
+    ids, _ = oracle.route_topk(inp["logits"], cfg["top_k"])
+    off, srt, act = oracle.group(ids, cfg["E"])
+    rng = np.random.default_rng(0)
+    pick = []
+    for e in act:
+        b, n = int(off[e]), int(off[e + 1] - off[e])
+        pick += [srt[b + (n - 1) // 64 * 64], srt[b + n - 1], srt[b + int(rng.integers(n))]]
+    return np.unique(np.asarray(pick)), act
+
+
 @pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
 def test_prefill_layer_full_size_sampled(name):
     """2048 tokens, hidden 4096, intermediate 1536, 256 experts, top-8: all
-    experts run on the GPU; 48 assignments (every column) are checked."""
+    experts run on the GPU; for every expert the first row of its last 64-row
+    chunk, its last row and a random row are checked in every column (G, U,
+    h, out), so an expert-index or chunk-offset error anywhere shows."""
     say("prefill full size", name)
     inp = wl.make_workload(name)
-    rng = np.random.default_rng(0)
-    A = 2048 * 8
-    sample = np.sort(rng.choice(A, size=48, replace=False))
+    sample, act = _every_expert_sample(inp)
+    assert act.size == inp["cfg"]["E"]
+    say("  %d assignments over %d experts" % (sample.size, act.size))
     gpu = _run(inp, sample)
     _check(inp, gpu, sample)
 

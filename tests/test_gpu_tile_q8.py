@@ -18,7 +18,7 @@ import oracle
 from oracle import moe
 import workloads as wl
 
-from gpu_util import assert_equal, assert_tol, dev, say, to_dev, to_host
+from gpu_util import assert_equal, assert_plan, assert_tol, dev, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -152,7 +152,9 @@ def test_tile_q8_combine(fmt, E, H, I, T, k):
     o_ref, to, _ = moe.grouped_matvec_q8(fmt, down, grid, ids, hq, hd, np.arange(A), I, want_isums=False)
     y_ref = np.einsum("tj,tjn->tn", w.astype(np.float64), o_ref.reshape(T, k, H))
     ty = np.einsum("tj,tjn->tn", np.abs(w.astype(np.float64)), to.reshape(T, k, H))
-    assert_tol(to_host(y), y_ref, ty + np.abs(y_ref) * 1e-6, "y")
+    # the fused combine rounds each w * out product and each of the k atomic
+    # adds in fp32: (k + 1) * 2^-24 * sum|w * out|, far inside 1e-5 * ty
+    assert_tol(to_host(y), y_ref, ty, "y")
 
 
 @pytest.mark.parametrize("fmt,K,E,T", [("ternary", 768, 16, 40), ("grid1", 1024, 16, 40), ("ternary", 512, 1024, 600),
@@ -166,6 +168,7 @@ def test_matvec_hands_heavy_experts_to_tile(fmt, K, E, T):
     say("matvec dispatch", fmt, K, E, T)
     N, k = 96, 2
     assert T * k > E
+    assert_plan(pq.PQ_PLAN_MATVEC_PAIRS | pq.PQ_PLAN_TILE_Q8, pq.PQ_CALL_MATVEC, fmt, T, k, E, N, K)
     seed = _seed("dispatch", fmt, K, E)
     rng = np.random.default_rng(seed)
     ids = np.stack([np.zeros(T, np.int32), rng.integers(1, E, size=T).astype(np.int32)], axis=1)
@@ -214,7 +217,7 @@ def test_q8_prefill_full_size_sampled(name):
     checked: routing exactly, q8(h) against the free-running oracle (up to
     rounding ties), the down outputs on the GPU's own q8(h), and y."""
     from bit_quantized_moe_q8_amd.layer import DecodeLayer
-    from gpu_util import q8_rows_equal_ignoring_ties
+    from gpu_util import q8h_check
     say("q8 prefill full size", name)
     inp = wl.make_workload(name)
     cfg = inp["cfg"]
@@ -230,8 +233,7 @@ def test_q8_prefill_full_size_sampled(name):
     ref = moe.decode_ffn(inp, want_isums=False, assign_subset=sub)
     assert_equal(to_host(layer.ids), ref["ids"], "ids")
     hq, hd = to_host(layer.hq), to_host(layer.hd)
-    ok = q8_rows_equal_ignoring_ties(hq[sub], ref["hq"][sub], ref["h"][sub], ref["hd"][sub])
-    assert ok.all(), "q8(h): %d of %d codes differ beyond rounding ties" % ((~ok).sum(), ok.size)
+    q8h_check(hq[sub], hd[sub], ref["g"][sub], ref["u"][sub], ref["tg"][sub], ref["tu"][sub])
     o_ref, to, _ = moe.grouped_matvec_q8(fmt, inp["down"], grid, ref["ids"], hq, hd, np.arange(T * k), I,
                                          want_isums=False, assign_subset=sub)
     out = to_host(layer.out)

@@ -284,6 +284,35 @@ def test_matvec_q8_vs_numpy_dequant(K):
     assert np.all(np.abs(y - ref) <= 1e-12 * t + 1e-300)
     # tsum is at least |y| and equals it when all terms have one sign
     assert np.all(t >= np.abs(y) * (1 - 1e-12))
+    # tsum exactly: the sum of |d_w * xd * isum| over the 32-weight blocks,
+    # with the block sums from a numpy brute force (an over-estimate such as
+    # |.| inside the block sum, or a dropped scale, fails here)
+    assert np.allclose(t, _numpy_term_sums(w, d, xq[0], xd[0]), rtol=1e-12, atol=0)
+
+
+def _numpy_term_sums(w_int8, d16, xq, xd):
+    K = w_int8.shape[1]
+    isum = (w_int8.astype(np.int64).reshape(w_int8.shape[0], K // 32, 32) *
+            xq.astype(np.int64).reshape(1, K // 32, 32)).sum(-1)
+    dw = np.repeat(np.asarray(d16, np.uint16).view(np.float16).astype(np.float64), 8, axis=-1)
+    return np.abs(dw * xd.astype(np.float64)[None, :] * isum).sum(-1)
+
+
+def test_matvec_q8_term_sums_distinguish_overestimates():
+    """A case where |isum| < sum|w*q| inside a block: the pinned term sum
+    is the smaller value, so the tolerance is not silently loosened."""
+    K = 256
+    w = np.zeros((1, K), np.int8)
+    w[0, :2] = [1, -1]
+    xq = np.zeros(K, np.int8)
+    xq[:2] = [5, 5]                        # isum of block 0 = 0, sum|w*q| = 10
+    xq[32:34] = [3, 4]
+    w[0, 32:34] = [1, 1]                   # isum of block 1 = 7
+    xd = np.full(K // 32, 0.5, np.float32)
+    d16 = np.full((1, 1), 0x4000, np.uint16)   # 2.0
+    y, t, isums = oracle.matvec_q8(w, d16, xq, xd)
+    assert isums[0, 0] == 0 and isums[0, 1] == 7
+    assert y[0] == 7.0 and t[0] == 7.0
 
 
 def test_isums_three_formulas_and_brute_force():
@@ -465,6 +494,13 @@ def test_combine_vs_numpy():
     ref = np.einsum("tj,tjn->tn", w.astype(np.float64), out.reshape(5, 4, 33).astype(np.float64))
     assert np.allclose(y, ref, rtol=1e-14, atol=1e-15)
     assert np.all(ty >= np.abs(y) - 1e-12)
+    # ty exactly: sum over the slots of |w * out| (numpy)
+    tref = np.einsum("tj,tjn->tn", np.abs(w.astype(np.float64)),
+                     np.abs(out.reshape(5, 4, 33).astype(np.float64)))
+    assert np.allclose(ty, tref, rtol=1e-14, atol=0)
+    # opposite signs cancel in y but not in ty
+    y2, ty2 = oracle.combine(np.float32([[2.0], [-2.0]]), np.float32([[0.5, 0.5]]), 2)
+    assert y2[0, 0] == 0.0 and ty2[0, 0] == 2.0
 
 
 # ------------------------------------------------------------------- MoE
@@ -502,3 +538,67 @@ def test_moe_weights_sum_and_slot_order():
     W = oracle.unpack_ternary(inp["down"]["qs"][e], 256)
     y, _, _ = oracle.matvec_q8(W, inp["down"]["d"][e], r["hq"][a], r["hd"][a])
     assert np.array_equal(y, r["out"][a])
+
+
+def _bf16_float(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _torch_bf16_bits(x32):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
+def test_prefill_topk1_single_expert_is_dense_bf16_swiglu_mlp(name):
+    """E = 1, k = 1: the prefill layer is a dense SwiGLU MLP through one
+    expert, computed here with numpy matmuls on the dequantized weights and
+    torch's bf16 rounding of h (a library routine), independently of the
+    oracle's own unpack-free arithmetic."""
+    H, I, T = 512, 512, 6
+    inp = wl.make_workload(name, E=1, H=H, I=I, T=T, top_k=1)
+    r = moe.prefill_ffn(inp)
+    fmt, grid = inp["cfg"]["fmt"], inp.get("grid")
+    assert np.all(r["ids"] == 0) and np.all(r["w"] == 1.0)
+
+    def deq(planes, K):
+        W = moe.unpack_expert(fmt, planes, 0, K, grid).astype(np.float64)
+        if fmt == "sign1":
+            return W * planes["d"][0].view(np.float16).astype(np.float64)[:, None]
+        return W * _deq_scales(planes["d"][0], K)
+
+    xf = _bf16_float(inp["x_bf16"])
+    G, U = xf @ deq(inp["gate"], H).T, xf @ deq(inp["up"], H).T
+    assert np.allclose(r["g"], G, rtol=1e-12, atol=1e-12)
+    assert np.allclose(r["u"], U, rtol=1e-12, atol=1e-12)
+    g32, u32 = G.astype(np.float32), U.astype(np.float32)
+    h = g32.astype(np.float64) * scipy.special.expit(g32.astype(np.float64)) * u32.astype(np.float64)
+    hb = _torch_bf16_bits(h.astype(np.float32))
+    assert np.array_equal(r["h_bf16"], hb)
+    out = _bf16_float(hb) @ deq(inp["down"], I).T
+    assert np.allclose(r["out"], out, rtol=1e-12, atol=1e-12)
+    # one slot of weight 1: y is out rounded to fp32 and summed once
+    assert np.array_equal(r["y"], r["out"].astype(np.float32).astype(np.float64))
+
+
+def test_prefill_layer_vs_numpy_per_assignment():
+    """Several experts, top-2: every assignment's output is the dense MLP of
+    its own expert on its token's row, and y the weighted sum of a token's two
+    slots (numpy einsum); the term sums are |x| @ |W| products."""
+    H, I, T, E, k = 256, 256, 10, 4, 2
+    inp = wl.make_workload("grid1_moe_prefill_t2048", E=E, H=H, I=I, T=T, top_k=k)
+    r = moe.prefill_ffn(inp)
+    grid = inp["grid"]
+    ids = r["ids"].ravel()
+    xf = _bf16_float(inp["x_bf16"])
+    for a in range(T * k):
+        e, t = int(ids[a]), a // k
+        Wg = oracle.unpack_grid1(inp["gate"]["qs"][e], inp["gate"]["qh"][e], grid, H) * _deq_scales(inp["gate"]["d"][e], H)
+        Wd = oracle.unpack_grid1(inp["down"]["qs"][e], inp["down"]["qh"][e], grid, I) * _deq_scales(inp["down"]["d"][e], I)
+        assert np.allclose(r["g"][a], Wg @ xf[t], rtol=1e-12, atol=1e-12)
+        assert np.allclose(r["tg"][a], np.abs(Wg) @ np.abs(xf[t]), rtol=1e-12, atol=0)
+        assert np.allclose(r["out"][a], Wd @ _bf16_float(r["h_bf16"][a]), rtol=1e-12, atol=1e-12)
+    y = np.einsum("tj,tjn->tn", r["w"].astype(np.float32).astype(np.float64),
+                  r["out"].astype(np.float32).astype(np.float64).reshape(T, k, H))
+    assert np.allclose(r["y"], y, rtol=1e-14, atol=1e-15)
