@@ -32,7 +32,7 @@ EXPORTS = (
     "pq_moe_gemm_dequant_tile", "pq_moe_gemm_dequant_tile_sign1",
     "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1",
     "pq_moe_decode1_gate_up_sign1", "pq_validate_ternary",
-    "pq_selftest", "pq_plan", "pq_status_str", "pq_abi_version",
+    "pq_selftest", "pq_plan", "pq_peak_read", "pq_peak_mfma_bf16", "pq_status_str", "pq_abi_version",
 )
 
 
@@ -113,6 +113,8 @@ def _load():
                                          ctypes.POINTER(Grid1W)] + [p] * 10,
         "pq_validate_ternary": [ctypes.POINTER(TernaryW), p, p],
         "pq_selftest": [p],
+        "pq_peak_read": [p, ctypes.c_int64, p, p],
+        "pq_peak_mfma_bf16": [i32, i32, p, p, p, p],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -574,3 +576,20 @@ def moe_decode1_gate_up(gate, up, x: torch.Tensor, logits: torch.Tensor, top_k: 
                            _ptr(groups.active_experts), _ptr(groups.n_active), _ptr(hq), _ptr(hd),
                            _ptr(y_zero), _stream())
     _check(fn, rc)
+
+
+def peak_read(buf: torch.Tensor, sink: torch.Tensor):
+    """pq_peak_read over every byte of `buf` (a measurement aid)."""
+    _need(sink, "sink", 1024, torch.int32)
+    n = buf.numel() * buf.element_size()
+    _check("pq_peak_read", _lib.pq_peak_read(_ptr(buf), n - n % 16, _ptr(sink), _stream()))
+    return n - n % 16
+
+
+def peak_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor) -> float:
+    """pq_peak_mfma_bf16 (a measurement aid); returns the flops it issues."""
+    _need(sink, "sink", 1024, torch.float32)
+    wpw, ch = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("pq_peak_mfma_bf16", _lib.pq_peak_mfma_bf16(int(workgroups), int(iters), _ptr(sink),
+                                                       ctypes.byref(wpw), ctypes.byref(ch), _stream()))
+    return float(workgroups) * wpw.value * iters * ch.value * 16 * 16 * 32 * 2

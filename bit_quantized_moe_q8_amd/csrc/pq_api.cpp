@@ -700,6 +700,27 @@ int32_t pq_plan(int32_t call, int32_t fmt, int32_t n_tokens, int32_t top_k, int3
     }
 }
 
+pq_status pq_peak_read(const void* buf, int64_t bytes, uint32_t* sink, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (bytes < 16 || bytes % 16 != 0) return PQ_ERR_SHAPE;
+        if (!buf || !sink) return PQ_ERR_NULL;
+        if (!aligned(buf, 16) || !aligned(sink, 4)) return PQ_ERR_ALIGN;
+        return from_hip(pqk::launch_peak_read(buf, bytes, sink, as_stream(stream)));
+    });
+}
+
+pq_status pq_peak_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, int32_t* waves_per_workgroup,
+                            int32_t* chains, pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (workgroups < 1 || iters < 1) return PQ_ERR_SHAPE;
+        if (!sink) return PQ_ERR_NULL;
+        if (!aligned(sink, 4)) return PQ_ERR_ALIGN;
+        if (waves_per_workgroup) *waves_per_workgroup = pqk::peak_mfma_waves_per_workgroup();
+        if (chains) *chains = pqk::peak_mfma_chains();
+        return from_hip(pqk::launch_peak_mfma(workgroups, iters, sink, as_stream(stream)));
+    });
+}
+
 pq_status pq_validate_ternary(const pq_ternary_w* w, int32_t* n_bad, pq_stream stream) {
     return guarded([&]() -> pq_status {
         if (!w || !w->qs || !n_bad) return PQ_ERR_NULL;

@@ -111,4 +111,12 @@ bool tile_q8_supported(int cols);
 hipError_t launch_gemm(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
 bool gemm_supported(Fmt fmt, int rows, int cols, int epi);
 
+// Measurement aids (k_peak.hip): a read stream over `bytes` of device memory,
+// and `workgroups` x peak_mfma_waves_per_workgroup() waves each issuing
+// iters x peak_mfma_chains() bf16 16x16x32 MFMAs.
+hipError_t launch_peak_read(const void* p, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_peak_mfma(int workgroups, int iters, float* sink, hipStream_t s);
+int peak_mfma_waves_per_workgroup();
+int peak_mfma_chains();
+
 }  // namespace pqk

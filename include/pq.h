@@ -430,6 +430,24 @@ pq_status pq_selftest(pq_stream stream);
 int32_t pq_plan(int32_t call, int32_t fmt, int32_t n_tokens, int32_t top_k, int32_t n_experts,
                 int32_t rows, int32_t cols, int32_t epilogue, int32_t debug);
 
+/*
+ * Measurement aids, not on the hot path: the achievable rates of the device,
+ * used as second denominators next to the nominal 8 TB/s HBM and 2.5 PFLOP/s
+ * dense bf16 peaks when expert-kernel rates are quoted as roofline fractions.
+ *
+ * pq_peak_read: streams `bytes` (a multiple of 16, buf 16-byte aligned) of
+ * device memory with 16-byte loads and discards them; `sink` is a device
+ * uint32 [1024] the kernel may write (it never does for real data).
+ *
+ * pq_peak_mfma_bf16: `workgroups` workgroups of *waves_per_workgroup waves,
+ * each wave issuing iters * (*chains) v_mfma_f32_16x16x32_bf16 on register
+ * operands (16*16*32*2 flops each) and nothing else; `sink` is a device float
+ * [1024] as above.  waves_per_workgroup and chains may be NULL.
+ */
+pq_status pq_peak_read(const void *buf, int64_t bytes, uint32_t *sink, pq_stream stream);
+pq_status pq_peak_mfma_bf16(int32_t workgroups, int32_t iters, float *sink, int32_t *waves_per_workgroup,
+                            int32_t *chains, pq_stream stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *pq_status_str(pq_status status);
 
