@@ -102,11 +102,24 @@ constexpr int kSignPatterns = 256;
 // activations (every workgroup the same, so no earlier launch is waited for);
 // workgroup (0, 0) also writes the routing, the grouping the down projection
 // reads, and zeros the output row for its fused combine.
-template <int FMT, int LPR, int EPI, bool ABT, bool ROUTE, int NK = 1>
-__global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArgs ra) {
+//
+// KS > 1 (K split): the workgroup is KS groups of four waves, group s taking
+// chunks [s*LPR/KS, (s+1)*LPR/KS) of every row of the tile, so a tile's rows
+// stream with KS times the waves and a quarter (or half) of the dependent
+// work per wave.  Each group's row sums go through LDS and are added in the
+// pairwise order ((S0 + S1) + (S2 + S3)) that the single-group lane tree
+// (seg_sum over the whole row) uses for the same chunks, so the totals are
+// bit-identical to KS = 1 and to the grouped mat-vec.
+template <int FMT, int LPR, int EPI, bool ABT, bool ROUTE, int NK = 1, int KS = 1>
+__global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, RouteArgs ra) {
     using CK = Chunk<FMT>;
-    constexpr int LS = (LPR <= 2) ? 2 : (LPR <= 4) ? 4 : (LPR <= 8) ? 8 : (LPR <= 16) ? 16
-                     : (LPR <= 32) ? 32 : 64;         // lanes per row slot
+    constexpr int NT = kThreads * KS;                 // threads of the workgroup
+    static_assert(KS == 1 || KS == 2 || KS == 4, "K slices");
+    static_assert(LPR % KS == 0 && (KS == 1 || (LPR / KS) % 4 == 0), "whole, pairwise-summed slices");
+    constexpr int LPS = LPR / KS;                     // chunks of a row in one K slice
+    constexpr int LS = (LPS <= 2) ? 2 : (LPS <= 4) ? 4 : (LPS <= 8) ? 8 : (LPS <= 16) ? 16
+                     : (LPS <= 32) ? 32 : 64;         // lanes per row slot
+    static_assert(KS == 1 || LS == LPS, "a split row fills its lane slots");
     constexpr int RPW = kWave / LS;                   // row slots per wave
     constexpr int ROWS_IT = kWaves * RPW;             // rows per iteration
     constexpr int NMAT = (EPI == kEpiSwigluQ8) ? 2 : 1;
@@ -120,6 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
     // grid1: the codebook; sign1: the 256 byte patterns of +-1
     __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : (FMT == kSign1) ? kSignPatterns : 1];
     __shared__ float s_gu[NMAT][kTile];
+    __shared__ float s_kp[KS > 1 ? KS : 1][KS > 1 ? kTile * NMAT : 1];   // K-slice row sums
     __shared__ uint64_t s_key64[(ROUTE && NK <= 4) ? 4 * kWave : 1];
     __shared__ int s_part[(ROUTE && NK <= 4) ? 2 : 1][(ROUTE && NK <= 4) ? 2 * kWave : 1];
     __shared__ float s_tv[ROUTE ? 16 : 1];
@@ -128,10 +142,12 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
     __shared__ float s_xd[ROUTE ? kMaxCols / 32 : 1];
 
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int kslice = wave_all / kWaves;               // K slice of this wave
+    const int wave = wave_all % kWaves;                 // wave within the slice
     const int slot_row = lane / LS, chunk = lane % LS;
-    const bool lane_on = chunk < LPR;
-    const uint32_t cc = static_cast<uint32_t>(lane_on ? chunk : LPR - 1);
+    const bool lane_on = chunk < LPS;
+    const uint32_t cc = static_cast<uint32_t>(kslice * LPS + (lane_on ? chunk : LPS - 1));
     const int slot = blockIdx.y;
     const int n0 = blockIdx.x * kTile;
     const int rows = p.rows, cols = p.cols;
@@ -142,9 +158,9 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
         const uint4* src = reinterpret_cast<const uint4*>(p.grid);
         uint4* dst = reinterpret_cast<uint4*>(s_grid);
 #pragma unroll
-        for (int k = 0; k < kGridEntries / 2 / kThreads; ++k)
-            __builtin_amdgcn_global_load_lds(src + k * kThreads + tid,
-                                             (lds_void*)(dst + k * kThreads + wave * kWave), 16, 0, 0);
+        for (int k = 0; k < kGridEntries / 2 / NT; ++k)
+            __builtin_amdgcn_global_load_lds(src + k * NT + tid,
+                                             (lds_void*)(dst + k * NT + wave_all * kWave), 16, 0, 0);
     }
     if constexpr (FMT == kSign1) {
         // pattern i: byte j is -1 where bit j of i is set, else +1
@@ -172,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
         for (int s = 0; s < SUBS; ++s) xs[s] = xdp[s];
     };
     int n_active, e, a0;
-    constexpr int kXP = ROUTE ? kMaxCols / 4 / kThreads : 1;   // float4 passes of the q8
+    constexpr int kXP = ROUTE ? (kMaxCols / 4 + NT - 1) / NT : 1;   // float4 passes of the q8
     float4 xv[kXP];
     if constexpr (ROUTE) {
         // ---- the fp32 activations (kept for the q8 below) and the logits:
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
         const int n4 = cols / 4;
 #pragma unroll
         for (int u = 0; u < kXP; ++u) {
-            const int i = u * kThreads + tid;
+            const int i = u * NT + tid;
             xv[u] = i < n4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         const int E = p.n_experts, k = p.top_k;
@@ -194,15 +210,17 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
             // threads share a logit, each counting half of the keys
             // (keys past E are 0, below every real key, so every thread
             // scans a fixed 64-key range with all its LDS reads in flight)
+            // (the first 256 threads rank; with a K split the others wait)
+            const bool rk = tid < 4 * kWave;
             const float lt = tid < E ? ra.logits[tid] : 0.0f;
-            s_key64[tid] = tid < E ? route_key(lt == 0.0f ? 0.0f : lt, tid) : 0ull;   // -0 -> +0
+            if (rk) s_key64[tid] = tid < E ? route_key(lt == 0.0f ? 0.0f : lt, tid) : 0ull;   // -0 -> +0
             __syncthreads();
             const bool split = E <= 2 * kWave;
             const int i = split ? (tid & (2 * kWave - 1)) : tid;
-            const int j0 = split ? (tid >> 7) * kWave : 0;
+            const int j0 = split ? ((tid >> 7) & 1) * kWave : 0;
             const int nch = split ? 1 : (E + kWave - 1) / kWave;   // 64-key chunks
             int cnt = 0;
-            if (i < E) {
+            if (rk && i < E) {
                 const uint64_t ki = s_key64[i];
                 const uint4* k4 = reinterpret_cast<const uint4*>(s_key64 + j0);
                 for (int c = 0; c < nch; ++c) {
@@ -222,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
                 }
             }
             if (split) {
-                if (i < E) s_part[tid >> 7][i] = cnt;
+                if (rk && i < E) s_part[(tid >> 7) & 1][i] = cnt;
                 __syncthreads();
                 if (tid < E) cnt = s_part[0][tid] + s_part[1][tid];
             }
@@ -264,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
                 for (int i = 0; i < NK; ++i)
                     if (i * kWave + lane == win) kv[i] = 0u;
                 if (r == slot) e = win;
-                if (lists && wave == 0) {
+                if (lists && wave_all == 0) {
                     // the winner's logit as given (not the folded key)
                     float wv = 0.0f;
 #pragma unroll
@@ -333,10 +351,10 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
         const int n4 = cols / 4;
 #pragma unroll
         for (int u = 0; u < kXP; ++u) {
-            if (u * kThreads * 4 < cols) {   // uniform; 8-lane groups are whole (cols % 32 == 0)
+            if (u * NT * 4 < cols) {   // uniform; 8-lane groups are whole (cols % 32 == 0)
                 float d;
                 const uint32_t q = q8_pack4_dpp(xv[u], d);
-                const int i = u * kThreads + tid;
+                const int i = u * NT + tid;
                 if (i < n4) {
                     reinterpret_cast<uint32_t*>(s_xq)[i] = q;
                     if ((i & 7) == 0) s_xd[i >> 3] = d;
@@ -458,8 +476,34 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
 
     // outputs of assignment a (the row sums sit in each slot's last lane)
     auto store = [&](int a, float wsel) {
+        if constexpr (KS > 1) {
+            // the K slices' row sums, added in the lane tree's pairwise order
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                const int pr = it * ROWS_IT + wrow0 + slot_row;
+                if (pr < P && chunk == LS - 1) s_kp[kslice][pr] = part[it];
+            }
+            __syncthreads();
+            if (tid < P) {
+                float t;
+                if constexpr (KS == 2) t = s_kp[0][tid] + s_kp[1][tid];
+                else t = (s_kp[0][tid] + s_kp[1][tid]) + (s_kp[2][tid] + s_kp[3][tid]);
+                const int n = n0 + (tid & (kTile - 1));
+                if constexpr (EPI == kEpiF32) {
+                    if (n < rows) static_cast<float*>(p.out0)[static_cast<int64_t>(a) * rows + n] = t;
+                } else if constexpr (EPI == kEpiF32Combine) {
+                    if (n < rows)
+                        atomicAdd(static_cast<float*>(p.out0) + static_cast<int64_t>(a / p.top_k) * rows + n,
+                                  wsel * t);
+                } else {
+                    s_gu[tid / kTile][tid & (kTile - 1)] = t;
+                }
+            }
+            if constexpr (EPI != kEpiSwigluQ8) __syncthreads();   // s_kp is reused by a repeated expert
+        }
 #pragma unroll
         for (int it = 0; it < ITERS; ++it) {
+            if constexpr (KS > 1) break;
             const int pr0 = it * ROWS_IT + wrow0;
             const int pr = pr0 + slot_row;
             const int n = n0 + (pr & (kTile - 1));
@@ -477,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
         if constexpr (EPI == kEpiSwigluQ8) {
             // h = silu(g) * u and its q8 block: wave 0, one lane per output
             __syncthreads();
-            if (wave == 0) {
+            if (wave_all == 0) {
                 const int i = lane & 31;
                 const bool valid = lane < 32 && n0 + i < rows;
                 const float gg = s_gu[0][i], uu = s_gu[1][i];
@@ -514,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
         // experts (active list and sorted assignments in expert order,
         // offsets), and the zeroed output row
         const int k = p.top_k;
-        if (wave == 0) route_softmax_store(s_tv, s_ti, k, lane, ra.ids, ra.w);
+        if (wave_all == 0) route_softmax_store(s_tv, s_ti, k, lane, ra.ids, ra.w);
         if (tid < k) {
             const int et = s_ti[tid];
             int pos = 0;
@@ -522,25 +566,35 @@ __global__ __launch_bounds__(kThreads) void k_matvec_tok1(ExpertArgs p, RouteArg
             ra.active[pos] = et;
             ra.sorted[pos] = tid;
         }
-        for (int ee = tid; ee <= p.n_experts; ee += kThreads) {
+        for (int ee = tid; ee <= p.n_experts; ee += NT) {
             int below = 0;
             for (int q = 0; q < k; ++q) below += (s_ti[q] < ee) ? 1 : 0;
             ra.offsets[ee] = below;
         }
         if (tid == 0) *ra.n_active = k;
         if (ra.y)
-            for (int i = tid; i < cols; i += kThreads) ra.y[i] = 0.0f;
+            for (int i = tid; i < cols; i += NT) ra.y[i] = 0.0f;
     }
+}
+
+// K slices per workgroup for rows of LPR chunks: rows of 16 chunks and more
+// (gate/up rows of 2048 ternary or 4096 grid1 weights) split in two or four,
+// so a one-token launch (a few hundred workgroups) holds two to four waves
+// per SIMD; narrower rows stay whole.
+template <int LPR>
+constexpr int tok1_kslices() {
+    return (LPR == 16) ? 2 : (LPR == 32 || LPR == 64) ? 4 : 1;
 }
 
 template <int FMT, int LPR, int EPI, bool ABT>
 hipError_t launch_one(const ExpertArgs& a, hipStream_t s) {
     const RouteArgs none{};
+    constexpr int KS = tok1_kslices<LPR>();
     const unsigned tiles = static_cast<unsigned>((a.rows + kTile - 1) / kTile);
     // slots: at most top_k experts are active at one token
     const unsigned slots = static_cast<unsigned>(a.top_k < a.n_experts ? a.top_k : a.n_experts);
-    hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, EPI, ABT, false>), dim3(tiles, slots), dim3(kThreads), 0, s,
-                       a, none);
+    hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, EPI, ABT, false, 1, KS>), dim3(tiles, slots),
+                       dim3(kThreads * KS), 0, s, a, none);
     return hipGetLastError();
 }
 
@@ -575,15 +629,18 @@ hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
 
 template <int FMT, int LPR>
 hipError_t launch_route_one(const ExpertArgs& a, const RouteArgs& r, hipStream_t s) {
+    constexpr int KS = tok1_kslices<LPR>();   // as the unrouted kernel: the same sums
     const unsigned tiles = static_cast<unsigned>((a.rows + kTile - 1) / kTile);
     const dim3 grid(tiles, a.top_k);
     if (a.n_experts <= 2 * kWave)
-        hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, kEpiSwigluQ8, true, true, 2>), grid, dim3(kThreads), 0, s, a, r);
+        hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, kEpiSwigluQ8, true, true, 2, KS>), grid, dim3(kThreads * KS), 0,
+                           s, a, r);
     else if (a.n_experts <= 4 * kWave)
-        hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, kEpiSwigluQ8, true, true, 4>), grid, dim3(kThreads), 0, s, a, r);
+        hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, kEpiSwigluQ8, true, true, 4, KS>), grid, dim3(kThreads * KS), 0,
+                           s, a, r);
     else
-        hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, kEpiSwigluQ8, true, true, kMaxExperts / kWave>), grid,
-                           dim3(kThreads), 0, s, a, r);
+        hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, kEpiSwigluQ8, true, true, kMaxExperts / kWave, KS>), grid,
+                           dim3(kThreads * KS), 0, s, a, r);
     return hipGetLastError();
 }
 

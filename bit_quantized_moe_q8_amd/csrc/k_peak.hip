@@ -43,7 +43,7 @@ constexpr int kChains = 8;   // independent accumulators per wave
 // operands (16 * 16 * 32 * 2 flops each); the operands come from the lane id
 // so the compiler cannot fold them, and the sum decides a store that does not
 // happen (so no product is dropped).
-__global__ __launch_bounds__(kMfmaThreads) void k_peak_mfma(int iters, float* __restrict__ sink) {
+__global__ void k_peak_mfma(int iters, float* __restrict__ sink) {
     const uint32_t l = threadIdx.x;
     const uint32_t ha = 0x3F80u | (l & 7u), hb = 0x3F80u | ((l >> 3) & 7u);   // bf16 1.0 .. 1.05
     const uint32_t wa = ha | (ha << 16), wb = hb | (hb << 16);
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_peak_mfma(int iters, float* __
     }
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][3];
     if (s == -1.0f) sink[blockIdx.x & 1023] = s;
 }
 
