@@ -114,6 +114,7 @@ hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, i
 constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * 64;
 constexpr int kGroupMaxExperts = 1024;
+constexpr int kGroupBatch = 8;   // rows of 64 ids loaded per round trip
 
 __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ ids, int A,
                                                          int E, int32_t* __restrict__ offsets,
@@ -129,7 +130,20 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
     __syncthreads();
     const int chunk = (A + kGroupWaves - 1) / kGroupWaves;
     const int beg = min(wave * chunk, A), end = min(beg + chunk, A);
-    for (int a = beg + lane; a < end; a += 64) atomicAdd(&hist[wave * E + ids[a]], 1);
+    // kGroupBatch rows of 64 ids are loaded together (independent loads in
+    // flight) before they are counted, so a long range costs a few memory
+    // round trips instead of one per 64 ids
+    for (int a0 = beg; a0 < end; a0 += 64 * kGroupBatch) {
+        int key[kGroupBatch];
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int a = a0 + 64 * u + lane;
+            key[u] = a < end ? ids[a] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u)
+            if (key[u] >= 0) atomicAdd(&hist[wave * E + key[u]], 1);
+    }
     __syncthreads();
 
     // Experts e = tid + 512*half, processed in two halves to cover E <= 1024.
@@ -168,22 +182,33 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = beg; base < end; base += 64) {
-        const int a = base + lane;
-        const bool ok = a < end;
-        const int key = ok ? ids[a] : 0;
-        uint64_t m = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (key >> b) & 1;
-            const uint64_t bb = __ballot(ok && bit);
-            m &= bit ? bb : ~bb;
+    for (int a0 = beg; a0 < end; a0 += 64 * kGroupBatch) {
+        int keys[kGroupBatch];
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int a = a0 + 64 * u + lane;
+            keys[u] = a < end ? ids[a] : 0;
         }
-        if (ok) {
-            const int rank = __popcll(m & below);
-            const int pos = hist[wave * E + key] + rank;
-            sorted[pos] = a;
-            const int leader = 63 - __clzll(m);
-            if (leader == lane) hist[wave * E + key] += __popcll(m);
+        // rows of 64 in assignment order (the ranks below rely on it)
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int a = a0 + 64 * u + lane;
+            const bool ok = a < end;
+            const int key = keys[u];
+            uint64_t m = __ballot(ok);
+            if (m == 0) break;   // uniform: the range ended
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = (key >> b) & 1;
+                const uint64_t bb = __ballot(ok && bit);
+                m &= bit ? bb : ~bb;
+            }
+            if (ok) {
+                const int rank = __popcll(m & below);
+                const int pos = hist[wave * E + key] + rank;
+                sorted[pos] = a;
+                const int leader = 63 - __clzll(m);
+                if (leader == lane) hist[wave * E + key] += __popcll(m);
+            }
         }
     }
 }
@@ -413,23 +438,59 @@ hipError_t launch_validate_ternary(const uint8_t* qs, int64_t n_bytes, int32_t* 
 // ---------------------------------------------------------------------------
 // Weighted combine in slot order: y[t][n] = sum_j w[t][j] * out[t*k+j][n].
 // ---------------------------------------------------------------------------
+// Tokens on blockIdx.y (grid-stride past the y limit; a token's k weights
+// are wave-uniform scalar loads), V consecutive outputs per thread (V = 4:
+// 16-byte loads and stores when rows is a multiple of 4 and both arrays are
+// 16-byte aligned); the sum runs in slot order j = 0 .. k-1 for every output,
+// whatever V.
+constexpr int kCombineMaxGridY = 32768;
+
+template <int V>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ out,
                                                  const float* __restrict__ w, int T, int k,
                                                  int rows, float* __restrict__ y) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= static_cast<int64_t>(T) * rows) return;
-    const int64_t t = i / rows, n = i % rows;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) acc += w[t * k + j] * out[(t * k + j) * rows + n];
-    y[i] = acc;
+    const int64_t n = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * V;
+    if (n >= rows) return;
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        const float* wt = w + static_cast<int64_t>(t) * k;
+        const float* o = out + static_cast<int64_t>(t) * k * rows + n;
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const float wj = load_uniform(wt + j);
+            if constexpr (V == 4) {
+                const float4 x = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(j) * rows);
+                acc[0] += wj * x.x;
+                acc[1] += wj * x.y;
+                acc[2] += wj * x.z;
+                acc[3] += wj * x.w;
+            } else {
+                acc[0] += wj * o[static_cast<int64_t>(j) * rows];
+            }
+        }
+        float* yt = y + static_cast<int64_t>(t) * rows + n;
+        if constexpr (V == 4) {
+            *reinterpret_cast<float4*>(yt) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+            yt[0] = acc[0];
+        }
+    }
 }
 
 hipError_t launch_combine(const float* out, const float* w, int n_tokens, int top_k, int rows,
                           float* y, hipStream_t s) {
-    const int64_t n = static_cast<int64_t>(n_tokens) * rows;
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                       out, w, n_tokens, top_k, rows, y);
+    if (n_tokens == 0) return hipSuccess;
+    const bool vec = rows % 4 == 0 && (reinterpret_cast<uintptr_t>(out) % 16) == 0 &&
+                     (reinterpret_cast<uintptr_t>(y) % 16) == 0;
+    const unsigned gy = static_cast<unsigned>(n_tokens < kCombineMaxGridY ? n_tokens : kCombineMaxGridY);
+    if (vec) {
+        const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(rows / 4) + 255) / 256), gy);
+        hipLaunchKernelGGL(k_combine<4>, grid, dim3(256), 0, s, out, w, n_tokens, top_k, rows, y);
+    } else {
+        const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(rows) + 255) / 256), gy);
+        hipLaunchKernelGGL(k_combine<1>, grid, dim3(256), 0, s, out, w, n_tokens, top_k, rows, y);
+    }
     return hipGetLastError();
 }
 

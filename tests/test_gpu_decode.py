@@ -491,13 +491,20 @@ def test_decode_prep_rejects_large():
     assert st == pq.PQ_ERR_UNSUPPORTED
 
 
-def test_combine():
-    say("combine")
-    rng = np.random.default_rng(5)
-    out = rng.standard_normal((7 * 3, 100)).astype(np.float32)
-    w = rng.random((7, 3)).astype(np.float32)
-    y = pq.moe_combine(to_dev(out), to_dev(w), 3)
-    y_ref, ty = oracle.combine(out, w, 3)
+@pytest.mark.parametrize("T,k,rows,offset", [
+    (7, 3, 100, 0),       # rows % 4 == 0: 16-byte path
+    (7, 3, 101, 0),       # ragged rows: one output per thread
+    (5, 2, 100, 1),       # out not 16-byte aligned: one output per thread
+    (33000, 2, 12, 0),    # more tokens than one grid column holds
+])
+def test_combine(T, k, rows, offset):
+    say("combine", T, k, rows, offset)
+    rng = np.random.default_rng(5 + rows + T)
+    out = rng.standard_normal((T * k, rows)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    out_d = to_dev(np.concatenate([np.zeros(offset, np.float32), out.ravel()]))[offset:]
+    y = pq.moe_combine(out_d.view(T * k, rows), to_dev(w), k)
+    y_ref, ty = oracle.combine(out, w, k)
     assert_tol(to_host(y), y_ref, ty, "y")
 
 
