@@ -257,7 +257,10 @@ def measure_peaks():
 
 # ------------------------------------------------------------------ workloads
 
-def make_pool(fmt, E, rows_cols, L, seed, dev, grid_seed):
+def make_pool(fmt, E, rows_cols, L, seed, dev, grid_seed, tiled=False):
+    """L layers of random packed weights on the device; `tiled`: code planes in
+    the tile layout of the prefill GEMM (built on the device, outside any
+    timed region, as a model loader would)."""
     import torch
     import bit_quantized_moe_q8_amd as pq
     import workloads as wl
@@ -269,13 +272,31 @@ def make_pool(fmt, E, rows_cols, L, seed, dev, grid_seed):
         lay = {}
         for name, (n, kk) in rows_cols.items():
             if fmt == "ternary":
-                lay[name] = pq.TernaryWeights(**wl.torch_ternary_planes(gen, E, n, kk, dev))
+                w = pq.TernaryWeights(**wl.torch_ternary_planes(gen, E, n, kk, dev))
             elif fmt == "sign1":
-                lay[name] = pq.Sign1Weights(**wl.torch_sign1_planes(gen, E, n, kk, dev))
+                w = pq.Sign1Weights(**wl.torch_sign1_planes(gen, E, n, kk, dev))
             else:
-                lay[name] = pq.Grid1Weights(grid=grid, **wl.torch_grid1_planes(gen, E, n, kk, dev))
+                w = pq.Grid1Weights(grid=grid, **wl.torch_grid1_planes(gen, E, n, kk, dev))
+            lay[name] = pq.tile_layout(w) if tiled else w
+            del w
         layers.append(lay)
     return layers
+
+
+# the tile layout's (rows per group, 16-byte..32-byte unit, 256-column blocks
+# per unit) of each code plane
+TILE_PLANES = {"qs": (4, 32, 1), "signs": (4, 32, 1), "qh": (8, 16, 1), "sc": (8, 16, 2)}
+
+
+def untile(a, f):
+    """Host copy of a tile-layout plane [E][rows][bytes per row] back in row order."""
+    import numpy as np
+    R, unit, per = TILE_PLANES[f]
+    E, N = a.shape[0], a.shape[1]
+    b = np.ascontiguousarray(a).view(np.uint8).reshape(E, N, -1)
+    nb = b.shape[2] // unit
+    out = b.reshape(E, N // R, nb, R, unit).transpose(0, 1, 3, 2, 4).reshape(E, N, nb * unit)
+    return np.ascontiguousarray(out).view(a.dtype).reshape(a.shape)
 
 
 def bench_layer_workload(name, args, peaks):
@@ -304,7 +325,7 @@ def bench_layer_workload(name, args, peaks):
     log("workload %s: %d layers in the pool (%.2f GB packed), %d steps per graph" % (
         name, L, L * E * per_expert / 1e9, M))
 
-    layers = make_pool(fmt, E, {"gate": (I, H), "up": (I, H), "down": (H, I)}, L, seed, dev, seed)
+    layers = make_pool(fmt, E, {"gate": (I, H), "up": (I, H), "down": (H, I)}, L, seed, dev, seed, tiled=prefill)
     xs, lg = [], []
     for l in range(L):
         if prefill:
@@ -550,7 +571,7 @@ def cpu_baseline_layers(args, cfg, layers, xs, lg, n_active, per_expert, L, pref
                 src = getattr(Wt, f)
                 host = np.zeros(tuple(src.shape), dtype=np.uint8 if f in ("qs", "signs", "sc") else np.uint16)
                 host[touched] = src.index_select(0, sel).cpu().numpy().view(host.dtype)
-                planes[f] = host
+                planes[f] = untile(host, f) if getattr(Wt, "tiled", False) and f in TILE_PLANES else host
             inp[name] = planes
             if fmt == "grid1":
                 inp["grid"] = Wt.grid.cpu().numpy()

@@ -33,6 +33,7 @@ EXPORTS = (
     "pq_moe_combine", "pq_moe_decode1_gate_up_ternary", "pq_moe_decode1_gate_up_grid1",
     "pq_moe_decode1_gate_up_sign1", "pq_validate_ternary",
     "pq_selftest", "pq_plan", "pq_peak_read", "pq_peak_mfma_bf16", "pq_status_str", "pq_abi_version",
+    "pq_tile_layout_grid1", "pq_tile_layout_sign1",
 )
 
 
@@ -115,6 +116,8 @@ def _load():
         "pq_selftest": [p],
         "pq_peak_read": [p, ctypes.c_int64, p, p],
         "pq_peak_mfma_bf16": [i32, i32, p, p, p, p],
+        "pq_tile_layout_grid1": [ctypes.POINTER(Grid1W), p, p, p],
+        "pq_tile_layout_sign1": [ctypes.POINTER(Sign1W), p, p, p],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -250,6 +253,7 @@ class Sign1Weights:
     signs: torch.Tensor
     sc: torch.Tensor
     d: torch.Tensor
+    tiled: bool = False   # signs and sc in the tile layout (tile_layout), for the prefill GEMM only
 
     @property
     def shape(self):
@@ -274,6 +278,7 @@ class Grid1Weights:
     qh: torch.Tensor
     d: torch.Tensor
     grid: torch.Tensor
+    tiled: bool = False   # qs and qh in the tile layout (tile_layout), for the prefill GEMM only
 
     @property
     def shape(self):
@@ -411,6 +416,8 @@ def _check_up(w, w_up):
 
 
 def _matvec(fn_name, w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg):
+    _need_layout(w, False, fn_name)
+    _need_layout(w_up, False, fn_name)
     _dt(xq, torch.int8)
     _dt(xd, torch.float32)
     E, rows, cols = w.shape
@@ -485,10 +492,32 @@ def moe_tile_q8_sign1(w: Sign1Weights, w_up, groups: GroupBuffers, xq, xd, act_b
     return _matvec("pq_moe_tile_q8_sign1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
 
 
+def _need_layout(w, tiled: bool, what: str):
+    if w is not None and bool(getattr(w, "tiled", False)) != tiled:
+        raise ValueError("%s takes weights %s the tile layout" % (what, "in" if tiled else "not in"))
+
+
+def tile_layout(w):
+    """pq_tile_layout_grid1 / pq_tile_layout_sign1: a copy of w (Grid1Weights or
+    Sign1Weights) with its code planes in the tile layout the prefill GEMM
+    reads; d (and the grid) are shared with w."""
+    _need_layout(w, False, "tile_layout")
+    cw = w.cstruct()
+    if isinstance(w, Sign1Weights):
+        signs, sc = torch.empty_like(w.signs), torch.empty_like(w.sc)
+        _check("pq_tile_layout_sign1", _lib.pq_tile_layout_sign1(ctypes.byref(cw), _ptr(signs), _ptr(sc), _stream()))
+        return Sign1Weights(signs=signs, sc=sc, d=w.d, tiled=True)
+    qs, qh = torch.empty_like(w.qs), torch.empty_like(w.qh)
+    _check("pq_tile_layout_grid1", _lib.pq_tile_layout_grid1(ctypes.byref(cw), _ptr(qs), _ptr(qh), _stream()))
+    return Grid1Weights(qs=qs, qh=qh, d=w.d, grid=w.grid, tiled=True)
+
+
 def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: torch.Tensor,
                           act_by_token: bool, epilogue: int = PQ_EPI_F32, out0=None, dbg: dict = None):
     """pq_moe_gemm_dequant_tile (grid1) or pq_moe_gemm_dequant_tile_sign1 (Sign1Weights):
-    x bf16 (torch.bfloat16 or int16 bits)."""
+    weights in the tile layout (tile_layout), x bf16 (torch.bfloat16 or int16 bits)."""
+    _need_layout(w, True, "moe_gemm_dequant_tile")
+    _need_layout(w_up, True, "moe_gemm_dequant_tile")
     _dt(x_bf16, *_BF16)
     E, rows, cols = w.shape
     _check_up(w, w_up)
@@ -551,6 +580,8 @@ def moe_decode1_gate_up(gate, up, x: torch.Tensor, logits: torch.Tensor, top_k: 
     (SwiGLU + q8) in one launch.  x float32 [1][H], logits float32 [1][E];
     writes ids int32 [1][k], w float32 [1][k], groups (GroupBuffers), hq int8
     [k][I], hd float32 [k][I/32], and zeros y_zero float32 [1][H] if given."""
+    _need_layout(gate, False, "moe_decode1_gate_up")
+    _need_layout(up, False, "moe_decode1_gate_up")
     _dt(x, torch.float32)
     _dt(logits, torch.float32)
     E = logits.shape[-1]

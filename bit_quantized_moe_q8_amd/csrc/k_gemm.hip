@@ -22,6 +22,12 @@
 //    instruction, one block ahead of the MFMAs; 16-byte slots are
 //    XOR-swizzled by row so every fragment read (16 rows x one 16-byte
 //    column) is conflict-free.
+//  - The weight planes come in the tile layout (rows grouped so that one K
+//    block of a group is one 128-byte line: 4 rows of 32 index bytes, 8 rows
+//    of 16 high-bit bytes, 8 rows of 16 sub-scale bytes per block pair), so
+//    every copy into the ring moves whole lines; with rows kept whole, a line
+//    would serve four to eight blocks and leave the L2 before the later
+//    blocks read it.
 //  - B (weights) is decoded on chip only: lane l of a wave takes column
 //    l % 16 and, in K step ks, the grid group 8*(l/16) + ks of the block; its
 //    11-bit index selects a 16-byte bf16 row of the codebook in LDS, which is
@@ -93,6 +99,18 @@ __device__ __forceinline__ void order_block() {
         order_block<KS + 1, NC, NV, NM>();
     }
 }
+// The same with the step's ND LDS reads (NQ more with the first step: the
+// block's group indices) issued together between the copy and the MFMAs, so
+// a wave waits once per step instead of once per fragment.
+template <int KS, int NC, int NV, int NM, int ND, int NQ>
+__device__ __forceinline__ void order_block_lds() {
+    if constexpr (KS < kKs) {
+        __builtin_amdgcn_sched_group_barrier(0x0020, (KS == 0 ? NV : 0) + (KS < NC ? 1 : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x0100, ND + (KS == 0 ? NQ : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x0008, NM, 0);
+        order_block_lds<KS + 1, NC, NV, NM, ND, NQ>();
+    }
+}
 
 template <int NMAT, int NW>
 struct BCur {
@@ -124,7 +142,7 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
     const int N = p.rows, K = p.cols, KB = K / 256;
     // grid1: qh uint16 per 32 weights and one scale per 256; sign1: one
     // sub-scale byte per 32 weights and one anchor per row
-    const int qs_row = K / 8, qh_row = K / 32, d_row = (FMT == kSign1) ? 1 : K / 256;
+    const int d_row = (FMT == kSign1) ? 1 : K / 256;
 
     // activation row of each A copy this lane issues (fixed for the item)
     constexpr int ACOPIES = MS * 8 / kWaves;   // A copies per wave per block
@@ -167,7 +185,11 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
         int n = ntt * TILE_N + (pi % TILE_N);
         n = n < N ? n : N - 1;
         const uint8_t* base = (NMAT == 1 || m == 0) ? p.qs[0] : p.qs[1];
-        copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qs_row + kb * 32 + half * 16, dq + u0);
+        // tile layout: block kb of rows 4g..4g+3 is the 128 bytes at group
+        // line (g, kb), row n at 32 * (n % 4) in it
+        copy16_to_lds(base + ((static_cast<int64_t>(ee) * (N / 4) + n / 4) * KB + kb) * 128 + (n % 4) * 32 +
+                          half * 16,
+                      dq + u0);
     };
     auto issue_qh = [&](int r, int kb, uint4* dh, int ee, int ntt) {
         const int u0 = (wave * kQhCopies + r) * 64;   // uniform
@@ -175,12 +197,18 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
         const int pi = u0 + lane;
         int n = ntt * TILE_N + (pi % TILE_N);
         n = n < N ? n : N - 1;
+        // tile layout, groups of 8 rows: the 16 bytes of row n sit at
+        // 16 * (n % 8) of group line (g, kb) (high bits) or (g, kb / 2)
+        // (sub-scales of a block pair)
         if constexpr (FMT == kSign1) {
             const uint8_t* base = (NMAT == 1 || m == 0) ? p.sc[0] : p.sc[1];
-            copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qh_row + 8 * (kb & ~1), dh + u0);
+            copy16_to_lds(base + ((static_cast<int64_t>(ee) * (N / 8) + n / 8) * (KB / 2) + kb / 2) * 128 +
+                              (n % 8) * 16,
+                          dh + u0);
         } else {
-            const uint16_t* base = (NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1];
-            copy16_to_lds(base + (static_cast<int64_t>(ee) * N + n) * qh_row + kb * 8, dh + u0);
+            const uint8_t* base = reinterpret_cast<const uint8_t*>((NMAT == 1 || m == 0) ? p.qh[0] : p.qh[1]);
+            copy16_to_lds(base + ((static_cast<int64_t>(ee) * (N / 8) + n / 8) * KB + kb) * 128 + (n % 8) * 16,
+                          dh + u0);
         }
     };
     auto issue_b = [&](int kb, uint4* dq, uint4* dh) {
@@ -308,7 +336,10 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
         // Instruction order of the block: the scale loads and the first copy,
         // then one K step of MFMAs, one more copy, and so on (the scheduler
         // would otherwise sink all copies to the end of the block).
-        order_block<0, NCOPIES, NMAT * NW, MS * NMAT * NW>();
+        if constexpr (NMAT == 2)
+            order_block_lds<0, NCOPIES, NMAT * NW, MS * NMAT * NW, MS + NMAT * NW, 2 * NMAT * NW>();
+        else
+            order_block<0, NCOPIES, NMAT * NW, MS * NMAT * NW>();
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -489,7 +520,7 @@ hipError_t launch_one(const ExpertArgs& a, hipStream_t s) {
 }  // namespace
 
 bool gemm_supported(Fmt fmt, int rows, int cols, int epi) {
-    if (cols % 256 != 0 || rows < 1) return false;
+    if (cols % 256 != 0 || rows < 1 || rows % kTileRows != 0) return false;
     if (fmt == kSign1 && cols % 512 != 0) return false;   // whole 16-byte sub-scale units
     if (fmt != kGrid1 && fmt != kSign1) return false;
     return epi == kEpiF32 || epi == kEpiSwigluBf16;

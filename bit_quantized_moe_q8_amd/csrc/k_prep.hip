@@ -436,6 +436,38 @@ hipError_t launch_validate_ternary(const uint8_t* qs, int64_t n_bytes, int32_t* 
 }
 
 // ---------------------------------------------------------------------------
+// Tile layout of a packed plane (the layout the prefill GEMM copies from):
+// rows in groups of R, and per K unit the R rows' bytes back to back, one
+// 128-byte line per (group, unit).  A permutation of 16-byte pieces: thread
+// u writes destination piece u.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_tile_layout(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                     int64_t n16, int nb, int R, int u16) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; u < n16; u += stride) {
+        const int j = static_cast<int>(u % u16);
+        int64_t t = u / u16;
+        const int rr = static_cast<int>(t % R);
+        t /= R;
+        const int b = static_cast<int>(t % nb);
+        const int64_t g = t / nb;
+        dst[u] = src[((g * R + rr) * nb + b) * u16 + j];
+    }
+}
+
+hipError_t launch_tile_layout(const void* src, void* dst, int64_t rows, int nb, int unit, hipStream_t s) {
+    const int R = 128 / unit, u16 = unit / 16;
+    const int64_t n16 = rows * nb * u16;
+    if (n16 == 0) return hipSuccess;
+    int64_t grid = (n16 + 255) / 256;
+    const int64_t cap = static_cast<int64_t>(cu_count()) * 16;
+    if (grid > cap) grid = cap;
+    hipLaunchKernelGGL(k_tile_layout, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                       static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16, nb, R, u16);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Weighted combine in slot order: y[t][n] = sum_j w[t][j] * out[t*k+j][n].
 // ---------------------------------------------------------------------------
 // Tokens on blockIdx.y (grid-stride past the y limit; a token's k weights

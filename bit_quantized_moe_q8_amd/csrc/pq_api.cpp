@@ -552,6 +552,7 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w* w, const pq_grid1_w* w_up,
         if (!aligned(w->qs, 16) || !aligned(w->qh, 8) || !aligned(w->d, 2) ||
             !aligned(w->grid, 16))
             return PQ_ERR_ALIGN;
+        if (w->rows % pqk::kTileRows != 0) return PQ_ERR_SHAPE;
         if (!pqk::gemm_supported(pqk::kGrid1, w->rows, w->cols, epilogue)) return PQ_ERR_UNSUPPORTED;
         if (g->n_tokens == 0) return PQ_OK;
         if (!x) return PQ_ERR_NULL;
@@ -594,6 +595,7 @@ pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w* w, const pq_sign1_w* 
                 return PQ_ERR_ALIGN;
         }
         if (!aligned(w->signs, 16) || !aligned(w->sc, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+        if (w->rows % pqk::kTileRows != 0) return PQ_ERR_SHAPE;
         if (!pqk::gemm_supported(pqk::kSign1, w->rows, w->cols, epilogue)) return PQ_ERR_UNSUPPORTED;
         if (g->n_tokens == 0) return PQ_OK;
         if (!x) return PQ_ERR_NULL;
@@ -613,6 +615,65 @@ pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w* w, const pq_sign1_w* 
         a.out0 = out0;
         fill_debug(a, dbg);
         return from_hip(pqk::launch_gemm(pqk::kSign1, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
+    });
+}
+
+namespace {
+
+// [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
+// no destination plane shares a byte with any plane of the call
+bool planes_overlap(const void* s0, int64_t n0, const void* s1, int64_t n1, const void* d0, const void* d1) {
+    return overlap(d0, n0, s0, n0) || overlap(d0, n0, s1, n1) || overlap(d1, n1, s0, n0) ||
+           overlap(d1, n1, s1, n1) || overlap(d0, n0, d1, n1);
+}
+
+pq_status check_tile_dims(int32_t n_experts, int32_t rows, int32_t cols, int32_t col_mult) {
+    if (n_experts < 1 || n_experts > kMaxExperts) return PQ_ERR_SHAPE;
+    if (rows < 1 || rows % pqk::kTileRows != 0) return PQ_ERR_SHAPE;
+    if (cols < col_mult || cols % col_mult != 0) return PQ_ERR_SHAPE;
+    if (int64_t(rows) * cols > (int64_t(1) << 31)) return PQ_ERR_SHAPE;
+    return PQ_OK;
+}
+
+}  // namespace
+
+pq_status pq_tile_layout_grid1(const pq_grid1_w* w, uint8_t* qs_tiled, uint16_t* qh_tiled,
+                               pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->qs || !w->qh || !qs_tiled || !qh_tiled) return PQ_ERR_NULL;
+        pq_status st = check_tile_dims(w->n_experts, w->rows, w->cols, 256);
+        if (st != PQ_OK) return st;
+        if (!aligned(w->qs, 16) || !aligned(w->qh, 16) || !aligned(qs_tiled, 16) || !aligned(qh_tiled, 16))
+            return PQ_ERR_ALIGN;
+        const int64_t rows = int64_t(w->n_experts) * w->rows;
+        const int64_t qs_bytes = rows * (w->cols / 8), qh_bytes = rows * (w->cols / 32) * 2;
+        if (planes_overlap(w->qs, qs_bytes, w->qh, qh_bytes, qs_tiled, qh_tiled)) return PQ_ERR_SHAPE;
+        const int nb = w->cols / 256;
+        hipError_t e = pqk::launch_tile_layout(w->qs, qs_tiled, rows, nb, 32, as_stream(stream));
+        if (e == hipSuccess) e = pqk::launch_tile_layout(w->qh, qh_tiled, rows, nb, 16, as_stream(stream));
+        return from_hip(e);
+    });
+}
+
+pq_status pq_tile_layout_sign1(const pq_sign1_w* w, uint8_t* signs_tiled, uint8_t* sc_tiled,
+                               pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->signs || !w->sc || !signs_tiled || !sc_tiled) return PQ_ERR_NULL;
+        pq_status st = check_tile_dims(w->n_experts, w->rows, w->cols, 512);
+        if (st != PQ_OK) return st;
+        if (!aligned(w->signs, 16) || !aligned(w->sc, 16) || !aligned(signs_tiled, 16) || !aligned(sc_tiled, 16))
+            return PQ_ERR_ALIGN;
+        const int64_t rows = int64_t(w->n_experts) * w->rows;
+        const int64_t s_bytes = rows * (w->cols / 8), c_bytes = rows * (w->cols / 32);
+        if (planes_overlap(w->signs, s_bytes, w->sc, c_bytes, signs_tiled, sc_tiled)) return PQ_ERR_SHAPE;
+        hipError_t e = pqk::launch_tile_layout(w->signs, signs_tiled, rows, w->cols / 256, 32, as_stream(stream));
+        if (e == hipSuccess) e = pqk::launch_tile_layout(w->sc, sc_tiled, rows, w->cols / 512, 16, as_stream(stream));
+        return from_hip(e);
     });
 }
 

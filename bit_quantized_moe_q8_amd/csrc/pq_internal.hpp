@@ -11,6 +11,7 @@ namespace pqk {
 
 constexpr int kGridEntries = 2048;  // grid1 codebook entries of 8 int8 values
 constexpr int kMaxExperts = 1024;   // experts per layer accepted by every entry point
+constexpr int kTileRows = 8;        // rows of the tile layout's largest row group
 // Assignments from which an expert of a large decode batch goes to the
 // int8-MFMA tile kernel (measured on the skewed 64-token decode: 6 and 8
 // best, 4 and 16 slower); also the least token count for that split.
@@ -109,6 +110,11 @@ bool tile_q8_supported(int cols);
 
 // Prefill dequant-per-tile GEMM (grid1 or sign1, bf16 MFMA).
 hipError_t launch_gemm(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
+
+// Tile layout of one packed plane: src [rows][nb][unit] bytes ->
+// dst [rows / R][nb][R][unit] with R = 128 / unit (unit 16 or 32 bytes,
+// rows % R == 0, both 16-byte aligned, no overlap).
+hipError_t launch_tile_layout(const void* src, void* dst, int64_t rows, int nb, int unit, hipStream_t s);
 bool gemm_supported(Fmt fmt, int rows, int cols, int epi);
 
 // Measurement aids (k_peak.hip): a read stream over `bytes` of device memory,

@@ -24,7 +24,8 @@ import torch
 from . import (PQ_EPI_F32, PQ_EPI_F32_COMBINE, PQ_EPI_SWIGLU_BF16, PQ_EPI_SWIGLU_Q8,
                GroupBuffers, Grid1Weights, Sign1Weights, TernaryWeights, decode_prep, decode_prep_supported,
                group_tokens_by_expert, moe_combine, moe_decode1_gate_up, moe_gemm_dequant_tile,
-               moe_matvec_grid1, moe_matvec_sign1, moe_matvec_ternary, moe_route_topk, quantize_act_q8)
+               moe_matvec_grid1, moe_matvec_sign1, moe_matvec_ternary, moe_route_topk, quantize_act_q8,
+               tile_layout)
 
 # When the decode layer fuses the prep kernels (tokens x experts up to one
 # key per thread of the fused kernel), and the combine into the down mat-vec
@@ -112,7 +113,7 @@ class DecodeLayer:
 
 class PrefillLayer:
     """Buffers and call sequence of one prefill MoE FFN layer (grid1 or sub-scaled
-    sign weights, bf16 x)."""
+    sign weights in the tile layout, bf16 x)."""
 
     def __init__(self, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int,
                  device="cuda"):
@@ -154,8 +155,9 @@ class PrefillLayer:
         return self.y
 
 
-def weights_to_device(fmt: str, planes: dict, grid=None, device="cuda"):
-    """Host numpy planes (workloads module layout) -> device weight container."""
+def weights_to_device(fmt: str, planes: dict, grid=None, device="cuda", tiled: bool = False):
+    """Host numpy planes (workloads module layout) -> device weight container;
+    `tiled`: code planes in the tile layout of the prefill GEMM (grid1, sign1)."""
     import numpy as np
 
     def t(a):
@@ -165,7 +167,11 @@ def weights_to_device(fmt: str, planes: dict, grid=None, device="cuda"):
         return torch.from_numpy(a).to(device)
 
     if fmt == "ternary":
+        if tiled:
+            raise ValueError("ternary weights have no tile layout")
         return TernaryWeights(t(planes["qs"]), t(planes["d"]))
     if fmt == "sign1":
-        return Sign1Weights(t(planes["signs"]), t(planes["sc"]), t(planes["d"]))
-    return Grid1Weights(t(planes["qs"]), t(planes["qh"]), t(planes["d"]), t(grid))
+        w = Sign1Weights(t(planes["signs"]), t(planes["sc"]), t(planes["d"]))
+    else:
+        w = Grid1Weights(t(planes["qs"]), t(planes["qh"]), t(planes["d"]), t(grid))
+    return tile_layout(w) if tiled else w

@@ -309,11 +309,38 @@ pq_status pq_moe_tile_q8_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                                void *out1, const pq_debug *dbg, pq_stream stream);
 
 /*
+ * Tile layout of the packed planes that the prefill GEMM reads (the same
+ * bytes, reordered; Parakon Runtime README, "How it works": the packed blocks
+ * are consumed tile by tile and never expanded).  Rows are taken in groups,
+ * and for every 256-column block (every 512-column pair for sub-scales) the
+ * group's bytes of that block lie back to back as one 128-byte line:
+ *   grid1 qs     [E][rows/4][cols/256][4][32]  bytes
+ *   grid1 qh     [E][rows/8][cols/256][8][8]   uint16
+ *   sign1 signs  [E][rows/4][cols/256][4][32]  bytes
+ *   sign1 sc     [E][rows/8][cols/512][8][16]  bytes
+ * (row n of a group sits at its position n % 4 or n % 8 in the line).  The d
+ * planes and the grid keep their own layout.
+ *
+ * pq_tile_layout_grid1 writes w's qs and qh in the tile layout to qs_tiled
+ * (same size as w->qs) and qh_tiled (same size as w->qh);
+ * pq_tile_layout_sign1 does the same for signs and sc.  rows % 8 == 0, cols
+ * % 256 == 0 (grid1) or % 512 == 0 (sign1); every plane 16-byte aligned; no
+ * output may overlap an input or the other output (PQ_ERR_SHAPE).  The
+ * caller owns all buffers; the call only enqueues kernels on `stream`.
+ */
+pq_status pq_tile_layout_grid1(const pq_grid1_w *w, uint8_t *qs_tiled, uint16_t *qh_tiled,
+                               pq_stream stream);
+pq_status pq_tile_layout_sign1(const pq_sign1_w *w, uint8_t *signs_tiled, uint8_t *sc_tiled,
+                               pq_stream stream);
+
+/*
  * Prefill: grouped dequant-per-tile GEMM over grid1 weights with bf16
  * activations on MFMA (Parakon Runtime README, "How it works": prompt
  * processing at large batch sizes uses a dequant-per-tile GEMM path).  Packed
  * blocks are decoded to bf16 {-1,0,+1} on chip only; each 256-column block is
  * accumulated in fp32 and scaled by its fp16 scale in fp32.
+ *   w, w_up: qs and qh in the tile layout (pq_tile_layout_grid1), d and grid
+ *            as in pq_grid1_w.  rows % 8 == 0 (PQ_ERR_SHAPE otherwise).
  *   x: bf16 bits, [n_tokens][cols] if act_by_token else [A][cols]; 16-byte aligned.
  *   PQ_EPI_F32:         out0 float [A][rows].
  *   PQ_EPI_SWIGLU_BF16: needs w_up; out0 bf16 bits [A][rows] of
@@ -330,8 +357,9 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w *w, const pq_grid1_w *w_up,
  * "What's PXQ?", PXQ1): each weight is decoded on chip to the bf16 of
  * sign * sc (exact, |w| <= 15) and every 256-column block is scaled by the
  * row's fp16 anchor in fp32, so out = sum_b d[n] * sum_{k in b} x[k] * sign *
- * sc, within the fp32 tolerance of the definition.  cols % 512 == 0; signs and
- * sc 16-byte aligned; otherwise as pq_moe_gemm_dequant_tile.
+ * sc, within the fp32 tolerance of the definition.  signs and sc in the tile
+ * layout (pq_tile_layout_sign1), d as in pq_sign1_w.  cols % 512 == 0; signs
+ * and sc 16-byte aligned; otherwise as pq_moe_gemm_dequant_tile.
  */
 pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                                          const pq_groups *g, const uint16_t *x,

@@ -216,6 +216,8 @@ def test_gemm_validation(L):
     assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 64, 1000)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_SHAPE
     assert f(b(gw), None, b(g), A1, 1, 0, A16, None, S) == pq.PQ_ERR_ALIGN
     assert f(b(gw), b(gw), b(g), A16, 1, 1, A16, None, S) == pq.PQ_ERR_UNSUPPORTED   # q8 epilogue
+    assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 60, 1024)), None, b(g), A16, 1, 0, A16, None, S) \
+        == pq.PQ_ERR_SHAPE                                                         # rows % 8 != 0
     f2 = L.pq_moe_gemm_dequant_tile_sign1
     sw = pq.Sign1W(A16, A16, A16, 8, 64, 1024)
     assert f2(b(pq.Sign1W(A16, None, A16, 8, 64, 1024)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_NULL
@@ -226,6 +228,33 @@ def test_gemm_validation(L):
     assert f2(b(sw), b(pq.Sign1W(A16, A16, A16, 8, 32, 1024)), b(g), A16, 1, 2, A16, None, S) \
         == pq.PQ_ERR_SHAPE                                                         # up shape
     assert f2(b(sw), None, b(_groups(pq, T=0)), None, 1, 0, A16, None, S) == pq.PQ_OK
+    assert f2(b(pq.Sign1W(A16, A16, A16, 8, 36, 1024)), None, b(g), A16, 1, 0, A16, None, S) \
+        == pq.PQ_ERR_SHAPE                                                         # rows % 8 != 0
+
+
+def test_tile_layout_validation(L):
+    """pq_tile_layout_{grid1,sign1}: every check returns before a HIP call."""
+    import bit_quantized_moe_q8_amd as pq
+    b = ctypes.byref
+    B, C, D = ctypes.c_void_p(0x200000), ctypes.c_void_p(0x400000), ctypes.c_void_p(0x600000)
+    f = L.pq_tile_layout_grid1
+    gw = pq.Grid1W(A16, ctypes.c_void_p(0x100000), A16, A16, 4, 64, 1024)   # qs 32 KB, qh 8 KB
+    assert f(None, B, C, S) == pq.PQ_ERR_NULL
+    assert f(b(gw), None, C, S) == pq.PQ_ERR_NULL
+    assert f(b(pq.Grid1W(A16, A16, A16, A16, 4, 60, 1024)), B, C, S) == pq.PQ_ERR_SHAPE    # rows % 8
+    assert f(b(pq.Grid1W(A16, A16, A16, A16, 4, 64, 1000)), B, C, S) == pq.PQ_ERR_SHAPE    # cols % 256
+    assert f(b(pq.Grid1W(A16, A16, A16, A16, 0, 64, 1024)), B, C, S) == pq.PQ_ERR_SHAPE    # no experts
+    assert f(b(gw), ctypes.c_void_p(0x200008), C, S) == pq.PQ_ERR_ALIGN
+    assert f(b(gw), A16, C, S) == pq.PQ_ERR_SHAPE                  # output over the input qs
+    assert f(b(gw), B, ctypes.c_void_p(0x201000), S) == pq.PQ_ERR_SHAPE   # the two outputs overlap
+    assert f(b(gw), B, ctypes.c_void_p(0x100000 + 4096), S) == pq.PQ_ERR_SHAPE   # qh output over qh
+    f2 = L.pq_tile_layout_sign1
+    sw = pq.Sign1W(A16, ctypes.c_void_p(0x100000), A16, 4, 64, 1024)
+    assert f2(b(sw), None, C, S) == pq.PQ_ERR_NULL
+    assert f2(b(pq.Sign1W(A16, ctypes.c_void_p(0x100000), A16, 4, 64, 768)), B, C, S) == pq.PQ_ERR_SHAPE
+    assert f2(b(pq.Sign1W(A16, ctypes.c_void_p(0x100000), A16, 4, 12, 1024)), B, C, S) == pq.PQ_ERR_SHAPE
+    assert f2(b(sw), B, ctypes.c_void_p(0x400004), S) == pq.PQ_ERR_ALIGN
+    assert f2(b(sw), D, D, S) == pq.PQ_ERR_SHAPE
 
 
 # ------------------------------------------------------- dispatch plan (host only)
@@ -330,13 +359,20 @@ def test_binding_rejects_undersized_buffers():
         pq.moe_matvec_ternary(bad_d, None, g, xq12, xd12, False, pq.PQ_EPI_F32, torch.zeros((12, 64), dtype=f32))
     # GEMM and combine
     Wg = pq.Grid1Weights(torch.zeros((16, 64, 32), dtype=torch.uint8), torch.zeros((16, 64, 8), dtype=torch.int16),
-                         torch.zeros((16, 64, 1), dtype=torch.int16), torch.zeros((2048, 8), dtype=i8))
+                         torch.zeros((16, 64, 1), dtype=torch.int16), torch.zeros((2048, 8), dtype=i8), tiled=True)
     with pytest.raises(ValueError, match="x holds"):
         pq.moe_gemm_dequant_tile(Wg, None, g, torch.zeros((3, 256), dtype=torch.bfloat16), False)
     with pytest.raises(ValueError, match="grid"):
-        pq.moe_gemm_dequant_tile(pq.Grid1Weights(Wg.qs, Wg.qh, Wg.d, torch.zeros(100, dtype=i8)), None, g,
-                                 torch.zeros((12, 256), dtype=torch.bfloat16), False, pq.PQ_EPI_F32,
+        pq.moe_gemm_dequant_tile(pq.Grid1Weights(Wg.qs, Wg.qh, Wg.d, torch.zeros(100, dtype=i8), tiled=True), None,
+                                 g, torch.zeros((12, 256), dtype=torch.bfloat16), False, pq.PQ_EPI_F32,
                                  torch.zeros((12, 64), dtype=f32))
+    with pytest.raises(ValueError, match="tile layout"):   # the GEMM reads only the tile layout
+        pq.moe_gemm_dequant_tile(pq.Grid1Weights(Wg.qs, Wg.qh, Wg.d, Wg.grid), None, g,
+                                 torch.zeros((12, 256), dtype=torch.bfloat16), False)
+    with pytest.raises(ValueError, match="tile layout"):   # and the mat-vec never does
+        pq.moe_matvec_grid1(Wg, None, g, torch.zeros((12, 256), dtype=i8), torch.zeros((12, 8), dtype=f32), False)
+    with pytest.raises(ValueError, match="tile layout"):
+        pq.tile_layout(Wg)
     with pytest.raises(ValueError, match="topk_w"):
         pq.moe_combine(torch.zeros((12, 64), dtype=f32), torch.zeros(11, dtype=f32), 4)
     with pytest.raises(ValueError, match="multiple of top_k"):

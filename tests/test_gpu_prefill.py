@@ -26,7 +26,7 @@ def _run(inp, sample=None):
     T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
     A = T * k
     layer = PrefillLayer(T, H, I, E, k, dev())
-    W = {n: weights_to_device(cfg["fmt"], inp[n], inp.get("grid")) for n in ("gate", "up", "down")}
+    W = {n: weights_to_device(cfg["fmt"], inp[n], inp.get("grid"), tiled=True) for n in ("gate", "up", "down")}
     x = to_dev(inp["x_bf16"])
     dbg = {"g": torch.zeros((A, I), device=dev()), "u": torch.zeros((A, I), device=dev()),
            "h": torch.zeros((A, I), device=dev())}
@@ -120,9 +120,10 @@ def test_prefill_layer_full_size_sampled(name):
     _check(inp, gpu, sample)
 
 
-@pytest.mark.parametrize("N,K,T,E,k", [(100, 256, 40, 3, 2), (300, 512, 9, 5, 2), (1, 256, 3, 2, 1)])
+@pytest.mark.parametrize("N,K,T,E,k", [(104, 256, 40, 3, 2), (296, 512, 9, 5, 2), (8, 256, 3, 2, 1)])
 def test_gemm_partial_column_tiles(N, K, T, E, k):
-    """F32 epilogue with N not a multiple of the 256-column tile (tail columns dropped)."""
+    """F32 epilogue with N not a multiple of the 256-column tile (tail columns
+    dropped; N a multiple of the tile layout's 8-row groups)."""
     say("gemm partial tiles", N, K, T, E, k)
     seed = 11
     planes = wl.stack_experts("grid1", seed, "w", E, N, K)
@@ -131,7 +132,7 @@ def test_gemm_partial_column_tiles(N, K, T, E, k):
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     x = wl.activations_bf16(seed, T, K)
     g = pq.group_tokens_by_expert(to_dev(ids), E)
-    W = weights_to_device("grid1", planes, grid)
+    W = weights_to_device("grid1", planes, grid, tiled=True)
     out = pq.moe_gemm_dequant_tile(W, None, g, to_dev(x), True, pq.PQ_EPI_F32)
     torch.cuda.synchronize()
     A = T * k
@@ -139,7 +140,7 @@ def test_gemm_partial_column_tiles(N, K, T, E, k):
     assert_tol(to_host(out), y_ref, t_ref, "out")
 
 
-@pytest.mark.parametrize("N,K,T,E,k", [(100, 512, 40, 3, 2), (300, 1024, 9, 5, 2), (1, 512, 3, 2, 1),
+@pytest.mark.parametrize("N,K,T,E,k", [(104, 512, 40, 3, 2), (296, 1024, 9, 5, 2), (8, 512, 3, 2, 1),
                                        (64, 4096, 70, 2, 1),
                                        (48, 512, 100, 1024, 8)])   # 1024 experts, most empty or single rows
 def test_gemm_sign1_f32(N, K, T, E, k):
@@ -153,7 +154,7 @@ def test_gemm_sign1_f32(N, K, T, E, k):
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     x = wl.activations_bf16(seed, T, K)
     g = pq.group_tokens_by_expert(to_dev(ids), E)
-    W = weights_to_device("sign1", planes, None)
+    W = weights_to_device("sign1", planes, None, tiled=True)
     A = T * k
     dbg = {"g": torch.zeros((A, N), device=dev())}
     out = pq.moe_gemm_dequant_tile(W, None, g, to_dev(x), True, pq.PQ_EPI_F32, dbg=dbg)
@@ -177,7 +178,7 @@ def test_gemm_sign1_swiglu(I, H, T, E, k):
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     x = wl.activations_bf16(seed, T, H)
     g = pq.group_tokens_by_expert(to_dev(ids), E)
-    Wg, Wu = weights_to_device("sign1", gate, None), weights_to_device("sign1", up, None)
+    Wg, Wu = weights_to_device("sign1", gate, None, tiled=True), weights_to_device("sign1", up, None, tiled=True)
     A = T * k
     dbg = {"g": torch.zeros((A, I), device=dev()), "u": torch.zeros((A, I), device=dev()),
            "h": torch.zeros((A, I), device=dev())}
@@ -195,3 +196,33 @@ def test_gemm_sign1_swiglu(I, H, T, E, k):
     hb_host = to_host(hb).view(np.uint16) if to_host(hb).dtype != np.uint16 else to_host(hb)
     assert_equal(hb_host.reshape(hh.shape), oracle.float_to_bf16(hh).reshape(hh.shape), "h (bf16 rounding)")
     assert_equal(to_host(hb2), to_host(hb), "debug vs production variant")
+
+
+@pytest.mark.parametrize("fmt,E,N,K", [("grid1", 3, 24, 1024), ("grid1", 1, 8, 256), ("sign1", 2, 40, 1536),
+                                       ("sign1", 1, 8, 512)])
+def test_tile_layout_is_the_stated_permutation(fmt, E, N, K):
+    """pq_tile_layout_{grid1,sign1} against the layout written out with numpy
+    reshapes (groups of 4 rows x 32 bytes per block for qs/signs, 8 rows x 16
+    bytes per block for qh and per block pair for sc): bit-exact; d and the
+    grid are shared, not copied."""
+    say("tile layout", fmt, E, N, K)
+    planes = wl.stack_experts(fmt, 3 + N, "w", E, N, K)
+    grid = wl.codebook(3) if fmt == "grid1" else None
+    W = weights_to_device(fmt, planes, grid)
+    T = pq.tile_layout(W)
+    torch.cuda.synchronize()
+    KB = K // 256
+
+    def regroup(a, R, nb, unit):
+        b = np.ascontiguousarray(a).view(np.uint8).reshape(E, N // R, R, nb, unit)
+        return b.transpose(0, 1, 3, 2, 4).reshape(-1)
+
+    if fmt == "grid1":
+        pairs = [(T.qs, regroup(planes["qs"], 4, KB, 32)), (T.qh, regroup(planes["qh"], 8, KB, 16))]
+        assert T.d.data_ptr() == W.d.data_ptr() and T.grid.data_ptr() == W.grid.data_ptr()
+    else:
+        pairs = [(T.signs, regroup(planes["signs"], 4, KB, 32)), (T.sc, regroup(planes["sc"], 8, KB // 2, 16))]
+        assert T.d.data_ptr() == W.d.data_ptr()
+    for got, want in pairs:
+        assert_equal(to_host(got).view(np.uint8).reshape(-1), want, "tile layout")
+    assert T.tiled and not W.tiled
