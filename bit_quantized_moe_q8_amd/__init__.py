@@ -100,10 +100,10 @@ def _load():
                                  ctypes.POINTER(Groups), p, p, i32, i32, p, p,
                                  ctypes.POINTER(Debug), p],
         "pq_moe_gemm_dequant_tile": [ctypes.POINTER(Grid1W), ctypes.POINTER(Grid1W),
-                                     ctypes.POINTER(Groups), p, i32, i32, p,
+                                     ctypes.POINTER(Groups), p, i32, i32, p, p,
                                      ctypes.POINTER(Debug), p],
         "pq_moe_gemm_dequant_tile_sign1": [ctypes.POINTER(Sign1W), ctypes.POINTER(Sign1W),
-                                           ctypes.POINTER(Groups), p, i32, i32, p,
+                                           ctypes.POINTER(Groups), p, i32, i32, p, p,
                                            ctypes.POINTER(Debug), p],
         "pq_moe_combine": [p, p, i32, i32, i32, p, p],
         "pq_moe_decode1_gate_up_ternary": [p, p, i32, i32, ctypes.POINTER(TernaryW),
@@ -513,9 +513,12 @@ def tile_layout(w):
 
 
 def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: torch.Tensor,
-                          act_by_token: bool, epilogue: int = PQ_EPI_F32, out0=None, dbg: dict = None):
+                          act_by_token: bool, epilogue: int = PQ_EPI_F32, out0=None, dbg: dict = None,
+                          out1=None):
     """pq_moe_gemm_dequant_tile (grid1) or pq_moe_gemm_dequant_tile_sign1 (Sign1Weights):
-    weights in the tile layout (tile_layout), x bf16 (torch.bfloat16 or int16 bits)."""
+    weights in the tile layout (tile_layout), x bf16 (torch.bfloat16 or int16 bits).
+    PQ_EPI_F32_COMBINE: out0 = y float32 [T][rows] (accumulated into; zero it
+    first), out1 = topk_w float32 [T][k]."""
     _need_layout(w, True, "moe_gemm_dequant_tile")
     _need_layout(w_up, True, "moe_gemm_dequant_tile")
     _dt(x_bf16, *_BF16)
@@ -527,6 +530,11 @@ def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: t
     _need(x_bf16, "x", n_act * cols)
     if epilogue == PQ_EPI_F32:
         _need(out0, "out0", A * rows, *_F32)
+    elif epilogue == PQ_EPI_F32_COMBINE:
+        if out0 is None or out1 is None:
+            raise ValueError("the fused combine needs y (out0) and topk_w (out1)")
+        _need(out0, "y", groups.n_tokens * rows, *_F32)
+        _need(out1, "topk_w", A, *_F32)
     else:
         _need(out0, "out0 (h)", A * rows, *_BF16)
     _check_debug(dbg, A, rows, cols, w_up is not None)
@@ -539,7 +547,7 @@ def moe_gemm_dequant_tile(w: Grid1Weights, w_up, groups: GroupBuffers, x_bf16: t
     fn = "pq_moe_gemm_dequant_tile_sign1" if isinstance(w, Sign1Weights) else "pq_moe_gemm_dequant_tile"
     rc = getattr(_lib, fn)(ctypes.byref(ws), ctypes.byref(wu) if wu is not None else None,
                            ctypes.byref(gs), _ptr(x_bf16), int(act_by_token), int(epilogue),
-                           _ptr(out0), _debug_struct(dbg), _stream())
+                           _ptr(out0), _ptr(out1), _debug_struct(dbg), _stream())
     _check(fn, rc)
     return out0
 

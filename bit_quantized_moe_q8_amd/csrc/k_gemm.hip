@@ -132,7 +132,7 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
                                           uint4* __restrict__ h1, const uint4* __restrict__ s_cb,
                                           const int* __restrict__ s_row,
                                           const int* __restrict__ s_asg, int e, int mrows, int nt) {
-    constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
+    constexpr int NMAT = (EPI == kEpiSwigluBf16) ? 2 : 1;
     constexpr int NW = (NMAT == 2) ? 2 : 4;
     constexpr int TILE_N = kWaves * NW * 16;
     static_assert(NMAT * TILE_N == kPairs, "tile / ring size mismatch");
@@ -383,6 +383,15 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
                     if constexpr (DBG) {
                         if (p.dbg_g) p.dbg_g[o] = tot[ms][0][w][i];
                     }
+                } else if constexpr (EPI == kEpiF32Combine) {
+                    // weighted combine: y[token][n] += topk_w[a] * out[a][n]
+                    const int a = s_asg[r];
+                    const float wa = static_cast<const float*>(p.out1)[a];
+                    atomicAdd(static_cast<float*>(p.out0) + static_cast<int64_t>(a / p.top_k) * N + n,
+                              wa * tot[ms][0][w][i]);
+                    if constexpr (DBG) {
+                        if (p.dbg_g) p.dbg_g[o] = tot[ms][0][w][i];
+                    }
                 } else {
                     const float g = tot[ms][0][w][i], u = tot[ms][1][w][i];
                     const float h = g / (1.0f + expf(-g)) * u;
@@ -400,7 +409,7 @@ __device__ __forceinline__ void gemm_item(const ExpertArgs& p, uint4* __restrict
 
 template <int FMT, int EPI, bool DBG>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(ExpertArgs p) {
-    constexpr int NMAT = (EPI == kEpiF32) ? 1 : 2;
+    constexpr int NMAT = (EPI == kEpiSwigluBf16) ? 2 : 1;
     constexpr int NW = (NMAT == 2) ? 2 : 4;       // 16-col subtiles per wave per matrix
     constexpr int TILE_N = kWaves * NW * 16;      // 256 (gate/up) or 512 (down)
 
@@ -523,7 +532,7 @@ bool gemm_supported(Fmt fmt, int rows, int cols, int epi) {
     if (cols % 256 != 0 || rows < 1 || rows % kTileRows != 0) return false;
     if (fmt == kSign1 && cols % 512 != 0) return false;   // whole 16-byte sub-scale units
     if (fmt != kGrid1 && fmt != kSign1) return false;
-    return epi == kEpiF32 || epi == kEpiSwigluBf16;
+    return epi == kEpiF32 || epi == kEpiSwigluBf16 || epi == kEpiF32Combine;
 }
 
 template <int FMT>
@@ -531,6 +540,8 @@ hipError_t launch_fmt(Epi epi, const ExpertArgs& a, hipStream_t s) {
     if (epi == kEpiF32) return a.debug ? launch_one<FMT, kEpiF32, true>(a, s) : launch_one<FMT, kEpiF32, false>(a, s);
     if (epi == kEpiSwigluBf16)
         return a.debug ? launch_one<FMT, kEpiSwigluBf16, true>(a, s) : launch_one<FMT, kEpiSwigluBf16, false>(a, s);
+    if (epi == kEpiF32Combine)
+        return a.debug ? launch_one<FMT, kEpiF32Combine, true>(a, s) : launch_one<FMT, kEpiF32Combine, false>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -102,7 +102,6 @@ pq_status check_epilogue_outputs(int epilogue, const void* up, int rows, void* o
         return PQ_OK;
     }
     if (epilogue == PQ_EPI_F32_COMBINE) {
-        if (!decode) return PQ_ERR_UNSUPPORTED;
         if (!out1) return PQ_ERR_NULL;
         if (!aligned(out0, 4) || !aligned(out1, 4)) return PQ_ERR_ALIGN;
         return PQ_OK;
@@ -533,14 +532,14 @@ pq_status pq_moe_tile_q8_sign1(const pq_sign1_w* w, const pq_sign1_w* w_up, cons
 
 pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w* w, const pq_grid1_w* w_up,
                                    const pq_groups* g, const uint16_t* x, int32_t act_by_token,
-                                   int32_t epilogue, void* out0, const pq_debug* dbg,
+                                   int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
                                    pq_stream stream) {
     return guarded([&]() -> pq_status {
         if (!w || !w->qs || !w->qh || !w->d || !w->grid) return PQ_ERR_NULL;
         pq_status st = check_groups(g);
         if (st != PQ_OK) return st;
         if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
-        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, nullptr, false)) != PQ_OK)
+        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, false)) != PQ_OK)
             return st;
         if (epilogue == PQ_EPI_SWIGLU_BF16) {
             if (!w_up->qs || !w_up->qh || !w_up->d) return PQ_ERR_NULL;
@@ -571,6 +570,7 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w* w, const pq_grid1_w* w_up,
         a.act_by_token = act_by_token ? 1 : 0;
         a.xb = x;
         a.out0 = out0;
+        a.out1 = out1;
         fill_debug(a, dbg);
         return from_hip(pqk::launch_gemm(pqk::kGrid1, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
     });
@@ -578,14 +578,14 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w* w, const pq_grid1_w* w_up,
 
 pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w* w, const pq_sign1_w* w_up,
                                          const pq_groups* g, const uint16_t* x, int32_t act_by_token,
-                                         int32_t epilogue, void* out0, const pq_debug* dbg,
+                                         int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
                                          pq_stream stream) {
     return guarded([&]() -> pq_status {
         if (!w || !w->signs || !w->sc || !w->d) return PQ_ERR_NULL;
         pq_status st = check_groups(g);
         if (st != PQ_OK) return st;
         if ((st = check_dims(w->n_experts, w->rows, w->cols, g)) != PQ_OK) return st;
-        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, nullptr, false)) != PQ_OK)
+        if ((st = check_epilogue_outputs(epilogue, w_up, w->rows, out0, out1, false)) != PQ_OK)
             return st;
         if (epilogue == PQ_EPI_SWIGLU_BF16) {
             if (!w_up->signs || !w_up->sc || !w_up->d) return PQ_ERR_NULL;
@@ -613,6 +613,7 @@ pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w* w, const pq_sign1_w* 
         a.act_by_token = act_by_token ? 1 : 0;
         a.xb = x;
         a.out0 = out0;
+        a.out1 = out1;
         fill_debug(a, dbg);
         return from_hip(pqk::launch_gemm(pqk::kSign1, static_cast<pqk::Epi>(epilogue), a, as_stream(stream)));
     });

@@ -181,11 +181,14 @@ pq_status run(hipStream_t s) {
             std::memcpy(&u, &x[i], 4);
             xb[i] = static_cast<uint16_t>(u >> 16);
         }
-        DevBuf dxb;
-        ok(dxb.put(xb));
+        DevBuf dxb, dtqs, dtqh;
+        ok(dxb.put(xb) && dtqs.alloc(dgqs.n) && dtqh.alloc(dgqh.n));
+        pq_ok(pq_tile_layout_grid1(&gw, dtqs.as<uint8_t>(), dtqh.as<uint16_t>(), st));
+        const pq_grid1_w gwt{dtqs.as<uint8_t>(), dtqh.as<uint16_t>(), dsc_d.as<uint16_t>(), dgrid.as<int8_t>(),
+                             kE, kRows, kH};
         hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
-        pq_ok(pq_moe_gemm_dequant_tile(&gw, nullptr, &g, dxb.as<uint16_t>(), 1, PQ_EPI_F32, dout.p,
-                                       nullptr, st));
+        pq_ok(pq_moe_gemm_dequant_tile(&gwt, nullptr, &g, dxb.as<uint16_t>(), 1, PQ_EPI_F32, dout.p,
+                                       nullptr, nullptr, st));
         check_out();
     }
     // ---- sub-scaled signs: every sign positive, every sub-scale 1, anchors 1
@@ -215,12 +218,14 @@ pq_status run(hipStream_t s) {
             }
         std::vector<uint8_t> sg2(static_cast<size_t>(kE) * kRows * kH2 / 8, 0);
         std::vector<uint8_t> sc2(static_cast<size_t>(kE) * kRows * kH2 / 32, 0x11);
-        DevBuf dxb2, dsg2, dsc2;
-        ok(dxb2.put(xb2) && dsg2.put(sg2) && dsc2.put(sc2));
+        DevBuf dxb2, dsg2, dsc2, dtsg, dtsc;
+        ok(dxb2.put(xb2) && dsg2.put(sg2) && dsc2.put(sc2) && dtsg.alloc(dsg2.n) && dtsc.alloc(dsc2.n));
         const pq_sign1_w sw2{dsg2.as<uint8_t>(), dsc2.as<uint8_t>(), dsanc.as<uint16_t>(), kE, kRows, kH2};
+        pq_ok(pq_tile_layout_sign1(&sw2, dtsg.as<uint8_t>(), dtsc.as<uint8_t>(), st));
+        const pq_sign1_w sw2t{dtsg.as<uint8_t>(), dtsc.as<uint8_t>(), dsanc.as<uint16_t>(), kE, kRows, kH2};
         hip_ok(hipMemsetAsync(dout.p, 0, dout.n, s));
-        pq_ok(pq_moe_gemm_dequant_tile_sign1(&sw2, nullptr, &g, dxb2.as<uint16_t>(), 1, PQ_EPI_F32, dout.p,
-                                             nullptr, st));
+        pq_ok(pq_moe_gemm_dequant_tile_sign1(&sw2t, nullptr, &g, dxb2.as<uint16_t>(), 1, PQ_EPI_F32, dout.p,
+                                             nullptr, nullptr, st));
         hip_ok(hipStreamSynchronize(s));
         std::vector<float> out(kA * kRows);
         ok(dout.get(out));

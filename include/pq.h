@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define PQ_ABI_VERSION 1
+#define PQ_ABI_VERSION 2
 
 typedef enum pq_status {
     PQ_OK = 0,
@@ -342,15 +342,24 @@ pq_status pq_tile_layout_sign1(const pq_sign1_w *w, uint8_t *signs_tiled, uint8_
  *   w, w_up: qs and qh in the tile layout (pq_tile_layout_grid1), d and grid
  *            as in pq_grid1_w.  rows % 8 == 0 (PQ_ERR_SHAPE otherwise).
  *   x: bf16 bits, [n_tokens][cols] if act_by_token else [A][cols]; 16-byte aligned.
- *   PQ_EPI_F32:         out0 float [A][rows].
+ *   PQ_EPI_F32:         out0 float [A][rows]; out1 unused (may be NULL).
  *   PQ_EPI_SWIGLU_BF16: needs w_up; out0 bf16 bits [A][rows] of
- *                       round_to_nearest_even(silu(g) * u); rows % 32 == 0.
- * cols % 256 == 0.  dbg may be NULL (g, u, h fields honoured).
+ *                       round_to_nearest_even(silu(g) * u); rows % 32 == 0;
+ *                       out1 unused.
+ *   PQ_EPI_F32_COMBINE: the weighted combine (pq_moe_combine) fused into the
+ *                       GEMM: out0 float y [n_tokens][rows] receives
+ *                       y[a/top_k][n] += topk_w[a] * out[a][n] by fp32 atomic
+ *                       adds (y must hold zeros; the order of the top_k
+ *                       additions is unspecified, so the last bits can differ
+ *                       between runs); out1 = topk_w float [n_tokens][top_k].
+ *                       Saves writing and re-reading the [A][rows] outputs.
+ * cols % 256 == 0.  dbg may be NULL (g, u, h fields honoured; with the fused
+ * combine, g receives the per-assignment outputs out[a][n]).
  */
 pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w *w, const pq_grid1_w *w_up,
                                    const pq_groups *g, const uint16_t *x,
                                    int32_t act_by_token, int32_t epilogue, void *out0,
-                                   const pq_debug *dbg, pq_stream stream);
+                                   void *out1, const pq_debug *dbg, pq_stream stream);
 
 /*
  * The same GEMM over sub-scaled sign weights (pq_sign1_w; pxq_llama README,
@@ -364,7 +373,7 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w *w, const pq_grid1_w *w_up,
 pq_status pq_moe_gemm_dequant_tile_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                                          const pq_groups *g, const uint16_t *x,
                                          int32_t act_by_token, int32_t epilogue, void *out0,
-                                         const pq_debug *dbg, pq_stream stream);
+                                         void *out1, const pq_debug *dbg, pq_stream stream);
 
 /*
  * Weighted combine of the per-assignment expert outputs (the scatter of the

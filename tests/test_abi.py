@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_abi_version_and_status_strings(L):
     import bit_quantized_moe_q8_amd as pq
-    assert pq.abi_version() == 1
+    assert pq.abi_version() == 2
     for s in range(7):
         assert pq.status_str(s)
     assert pq.status_str(0) == "ok"
@@ -212,23 +212,25 @@ def test_gemm_validation(L):
     g = _groups(pq)
     f = L.pq_moe_gemm_dequant_tile
     gw = pq.Grid1W(A16, A16, A16, A16, 8, 64, 1024)
-    assert f(b(pq.Grid1W(A16, A16, A16, None, 8, 64, 1024)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_NULL
-    assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 64, 1000)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_SHAPE
-    assert f(b(gw), None, b(g), A1, 1, 0, A16, None, S) == pq.PQ_ERR_ALIGN
-    assert f(b(gw), b(gw), b(g), A16, 1, 1, A16, None, S) == pq.PQ_ERR_UNSUPPORTED   # q8 epilogue
-    assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 60, 1024)), None, b(g), A16, 1, 0, A16, None, S) \
+    assert f(b(pq.Grid1W(A16, A16, A16, None, 8, 64, 1024)), None, b(g), A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_NULL
+    assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 64, 1000)), None, b(g), A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_SHAPE
+    assert f(b(gw), None, b(g), A1, 1, 0, A16, None, None, S) == pq.PQ_ERR_ALIGN
+    assert f(b(gw), b(gw), b(g), A16, 1, 1, A16, None, None, S) == pq.PQ_ERR_UNSUPPORTED   # q8 epilogue
+    assert f(b(gw), None, b(g), A16, 0, 3, A16, None, None, S) == pq.PQ_ERR_NULL   # fused combine: no topk_w
+    assert f(b(gw), None, b(g), A16, 0, 3, A16, A1, None, S) == pq.PQ_ERR_ALIGN
+    assert f(b(pq.Grid1W(A16, A16, A16, A16, 8, 60, 1024)), None, b(g), A16, 1, 0, A16, None, None, S) \
         == pq.PQ_ERR_SHAPE                                                         # rows % 8 != 0
     f2 = L.pq_moe_gemm_dequant_tile_sign1
     sw = pq.Sign1W(A16, A16, A16, 8, 64, 1024)
-    assert f2(b(pq.Sign1W(A16, None, A16, 8, 64, 1024)), None, b(g), A16, 1, 0, A16, None, S) == pq.PQ_ERR_NULL
-    assert f2(b(pq.Sign1W(A16, A16, A16, 8, 64, 768)), None, b(g), A16, 1, 0, A16, None, S) \
+    assert f2(b(pq.Sign1W(A16, None, A16, 8, 64, 1024)), None, b(g), A16, 1, 0, A16, None, None, S) == pq.PQ_ERR_NULL
+    assert f2(b(pq.Sign1W(A16, A16, A16, 8, 64, 768)), None, b(g), A16, 1, 0, A16, None, None, S) \
         == pq.PQ_ERR_UNSUPPORTED                                                   # cols % 512 != 0
     assert f2(b(pq.Sign1W(A16, ctypes.c_void_p(0x10008), A16, 8, 64, 1024)), None, b(g), A16, 1, 0, A16,
-              None, S) == pq.PQ_ERR_ALIGN                                          # sc 8-byte aligned only
-    assert f2(b(sw), b(pq.Sign1W(A16, A16, A16, 8, 32, 1024)), b(g), A16, 1, 2, A16, None, S) \
+              None, None, S) == pq.PQ_ERR_ALIGN                                          # sc 8-byte aligned only
+    assert f2(b(sw), b(pq.Sign1W(A16, A16, A16, 8, 32, 1024)), b(g), A16, 1, 2, A16, None, None, S) \
         == pq.PQ_ERR_SHAPE                                                         # up shape
-    assert f2(b(sw), None, b(_groups(pq, T=0)), None, 1, 0, A16, None, S) == pq.PQ_OK
-    assert f2(b(pq.Sign1W(A16, A16, A16, 8, 36, 1024)), None, b(g), A16, 1, 0, A16, None, S) \
+    assert f2(b(sw), None, b(_groups(pq, T=0)), None, 1, 0, A16, None, None, S) == pq.PQ_OK
+    assert f2(b(pq.Sign1W(A16, A16, A16, 8, 36, 1024)), None, b(g), A16, 1, 0, A16, None, None, S) \
         == pq.PQ_ERR_SHAPE                                                         # rows % 8 != 0
 
 

@@ -21,29 +21,35 @@ from gpu_util import assert_equal, assert_tol, dev, say, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, sample=None):
+def _run(inp, sample=None, fused=False):
     cfg = inp["cfg"]
     T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
     A = T * k
-    layer = PrefillLayer(T, H, I, E, k, dev())
+    layer = PrefillLayer(T, H, I, E, k, dev(), fused_combine=fused)
     W = {n: weights_to_device(cfg["fmt"], inp[n], inp.get("grid"), tiled=True) for n in ("gate", "up", "down")}
     x = to_dev(inp["x_bf16"])
     dbg = {"g": torch.zeros((A, I), device=dev()), "u": torch.zeros((A, I), device=dev()),
            "h": torch.zeros((A, I), device=dev())}
     layer.route(to_dev(inp["logits"]))
     layer.gate_up(x, W["gate"], W["up"], dbg)
-    layer.down(W["down"])
+    # fused combine: the per-assignment outputs come from the debug output
+    out = torch.zeros((A, H), device=dev()) if fused else layer.out
+    layer.down(W["down"], {"g": out} if fused else None)
     layer.combine()
     torch.cuda.synchronize()
     idx = None if sample is None else torch.as_tensor(sample, device=dev())
     pick = (lambda t: to_host(t)) if idx is None else (lambda t: to_host(t.index_select(0, idx)))
     gpu = {"ids": to_host(layer.ids), "w": to_host(layer.w), "g": pick(dbg["g"]), "u": pick(dbg["u"]),
-           "h": pick(dbg["h"]), "hb": pick(layer.h), "hb_all": to_host(layer.h), "out": pick(layer.out),
-           "y": to_host(layer.y), "out_all": to_host(layer.out)}
-    # production launch (no debug outputs) gives the same bits
+           "h": pick(dbg["h"]), "hb": pick(layer.h), "hb_all": to_host(layer.h), "out": pick(out),
+           "y": to_host(layer.y), "out_all": to_host(out)}
+    # production launches (no debug outputs): the same h bits; y again within
+    # tolerance (the fused combine's atomic order may differ)
     layer.gate_up(x, W["gate"], W["up"])
+    layer.down(W["down"])
+    layer.combine()
     torch.cuda.synchronize()
     gpu["hb_prod"] = pick(layer.h)
+    gpu["y_prod"] = to_host(layer.y)
     return gpu
 
 
@@ -67,9 +73,12 @@ def _check(inp, gpu, sample=None):
     assert_equal(gpu["hb_prod"], gpu["hb"], "debug vs production variant")
     o_ref, to = moe.grouped_matvec_bf16(fmt, inp["down"], grid, ids, gpu["hb_all"], np.arange(A), I, rows)
     assert_tol(gpu["out"], o_ref[rows], to[rows], "out")
-    if sample is None:
-        y_ref, ty = oracle.combine(gpu["out_all"], gpu["w"], k)
-        assert_tol(gpu["y"], y_ref, ty, "y")
+    # the combine (fused or not) of the GPU's own per-assignment outputs, for
+    # every token: fp32 products and k fp32 additions in any order stay far
+    # inside 1e-5 * sum|w * out|
+    y_ref, ty = oracle.combine(gpu["out_all"], gpu["w"], k)
+    assert_tol(gpu["y"], y_ref, ty, "y")
+    assert_tol(gpu["y_prod"], y_ref, ty, "y (production launches)")
 
 
 @pytest.mark.parametrize("T,E,H,I,k,seed", [
@@ -80,14 +89,17 @@ def _check(inp, gpu, sample=None):
     (130, 1, 512, 256, 1, 5),     # one expert takes every token (3 chunks)
 ])
 @pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
-def test_prefill_layer_small(T, E, H, I, k, seed, name):
+@pytest.mark.parametrize("fused", [True, False])
+def test_prefill_layer_small(T, E, H, I, k, seed, name, fused):
     if name.startswith("sign1") and (H % 512 or I % 512):
         I = 512   # sub-scaled signs need row lengths that are multiples of 512
         H = max(512, H // 512 * 512)
-    say("prefill small", name, T, E, H, I, k)
+    say("prefill small", name, T, E, H, I, k, "fused combine" if fused else "separate combine")
     inp = wl.make_workload(name, seed=seed, T=T, E=E, H=H, I=I, top_k=k)
-    gpu = _run(inp)
+    gpu = _run(inp, fused=fused)
     _check(inp, gpu)
+    if not fused:
+        assert_equal(gpu["y_prod"], gpu["y"], "slot-order combine is deterministic")
 
 
 def _every_expert_sample(inp):
