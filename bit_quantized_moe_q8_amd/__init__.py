@@ -405,7 +405,14 @@ def decode_prep(x: torch.Tensor, logits: torch.Tensor, top_k: int, xq, xd, ids, 
 
 def decode_prep_supported(n_tokens: int, n_experts: int, top_k: int) -> bool:
     """The limits of pq_moe_decode_prep (include/pq.h)."""
-    return 1 <= n_tokens <= 16 and n_experts <= 1024 and n_tokens * top_k <= 256 and top_k <= 16
+    return (0 <= n_tokens and 1 <= top_k <= min(16, n_experts) and n_experts <= 1024
+            and n_tokens * top_k <= 1 << 20)
+
+
+def decode_prep_one_launch(n_tokens: int, n_experts: int, top_k: int) -> bool:
+    """pq_moe_decode_prep runs as one launch (one workgroup) at these sizes."""
+    return (1 <= n_tokens <= 16 and n_experts <= 1024 and n_tokens * top_k <= 256 and top_k <= 16
+            and n_tokens * n_experts <= 1024)
 
 
 def _check_up(w, w_up):

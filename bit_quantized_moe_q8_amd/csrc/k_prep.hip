@@ -56,14 +56,13 @@ hipError_t launch_quantize_q8(const float* x, int64_t n_blocks, int8_t* xq, floa
 // ---------------------------------------------------------------------------
 constexpr int kRouteMaxExperts = 1024;
 
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
-                                                    int E, int k, int32_t* __restrict__ ids,
-                                                    float* __restrict__ w) {
-    __shared__ uint64_t s_key[kRouteMaxExperts];
-    __shared__ float s_val[16];
-    __shared__ int s_idx[16];
+// Top-k routing of tokens t0, t0 + tstep, ... by one workgroup of 256
+// threads (the body of k_route_topk, shared with the fused q8 + route launch).
+__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int T, int E, int k,
+                                             int32_t* __restrict__ ids, float* __restrict__ w, int t0,
+                                             int tstep, uint64_t* s_key, float* s_val, int* s_idx) {
     const int tid = threadIdx.x;
-    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    for (int t = t0; t < T; t += tstep) {
         const float* l = logits + static_cast<int64_t>(t) * E;
         for (int e = tid; e < E; e += 256) {
             float v = l[e];
@@ -85,6 +84,39 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
         if (tid < 64) route_softmax_store(s_val, s_idx, k, tid, ids + static_cast<int64_t>(t) * k,
                                           w + static_cast<int64_t>(t) * k);
         __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
+                                                    int E, int k, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w) {
+    __shared__ uint64_t s_key[kRouteMaxExperts];
+    __shared__ float s_val[16];
+    __shared__ int s_idx[16];
+    route_tokens(logits, T, E, k, ids, w, blockIdx.x, gridDim.x, s_key, s_val, s_idx);
+}
+
+// The q8 of x and the top-k routing in one launch (the decode prep of
+// batches beyond one workgroup; the grouping follows in a launch of its own):
+// workgroups below route_wgs route tokens exactly as k_route_topk, the others
+// quantize 32-value blocks exactly as k_quantize_q8 and clear y_zero.
+__global__ __launch_bounds__(256) void k_q8_route(const float* __restrict__ x, int64_t n_blocks,
+                                                  int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                  const float* __restrict__ logits, int T, int E, int k,
+                                                  int32_t* __restrict__ ids, float* __restrict__ w,
+                                                  int route_wgs, float* __restrict__ y_zero, int64_t n_y) {
+    __shared__ uint64_t s_key[kRouteMaxExperts];
+    __shared__ float s_val[16];
+    __shared__ int s_idx[16];
+    if (static_cast<int>(blockIdx.x) < route_wgs) {   // uniform over the workgroup
+        route_tokens(logits, T, E, k, ids, w, blockIdx.x, route_wgs, s_key, s_val, s_idx);
+        return;
+    }
+    const int64_t t = static_cast<int64_t>(blockIdx.x - route_wgs) * 256 + threadIdx.x;
+    q8_lane(x, t, n_blocks, xq, xd);
+    if (y_zero) {
+        const int64_t stride = static_cast<int64_t>(gridDim.x - route_wgs) * 256;
+        for (int64_t i = t; i < n_y; i += stride) y_zero[i] = 0.0f;
     }
 }
 
@@ -387,15 +419,35 @@ hipError_t launch_decode_prep(const float* x, const float* logits, int n_tokens,
                               int n_experts, int top_k, int8_t* xq, float* xd, int32_t* ids,
                               float* w, int32_t* offsets, int32_t* sorted, int32_t* active,
                               int32_t* n_active, float* y_zero, hipStream_t s) {
-    hipLaunchKernelGGL(k_decode_prep, dim3(1), dim3(kPrepThreads), 0, s, x, logits, n_tokens,
-                       hidden, n_experts, top_k, xq, xd, ids, w, offsets, sorted, active, n_active,
-                       y_zero);
-    return hipGetLastError();
+    if (decode_prep_one_launch(n_tokens, n_experts, top_k)) {
+        hipLaunchKernelGGL(k_decode_prep, dim3(1), dim3(kPrepThreads), 0, s, x, logits, n_tokens,
+                           hidden, n_experts, top_k, xq, xd, ids, w, offsets, sorted, active, n_active,
+                           y_zero);
+        return hipGetLastError();
+    }
+    // two launches: q8 and routing side by side, then the grouping
+    if (n_tokens > 0) {
+        const int cap = cu_count() * 16;
+        const int route_wgs = n_tokens < cap ? n_tokens : cap;
+        const int64_t n_blocks = static_cast<int64_t>(n_tokens) * (hidden / 32);
+        const int64_t q8_wgs = (n_blocks * 8 + 255) / 256;
+        hipLaunchKernelGGL(k_q8_route, dim3(static_cast<unsigned>(route_wgs + (q8_wgs > 0 ? q8_wgs : 1))),
+                           dim3(256), 0, s, x, n_blocks, xq, xd, logits, n_tokens, n_experts, top_k, ids, w,
+                           route_wgs, y_zero, static_cast<int64_t>(n_tokens) * hidden);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_group(ids, n_tokens * top_k, n_experts, offsets, sorted, active, n_active, s);
 }
 
-bool decode_prep_supported(int n_tokens, int n_experts, int top_k) {
+// One workgroup does all three steps when at most one routing key per
+// thread (tokens x experts <= 1024) and one wave per token; above that the
+// two-launch path spreads the q8 and the routing over the chip (the single
+// workgroup measured no faster than separate launches at 8 tokens x 256
+// experts).
+bool decode_prep_one_launch(int n_tokens, int n_experts, int top_k) {
     return n_tokens >= 1 && n_tokens <= kPrepWaves && n_experts <= kMaxExperts &&
-           n_tokens * top_k <= kPrepMaxAssign && top_k <= 16;
+           n_tokens * top_k <= kPrepMaxAssign && top_k <= 16 && n_tokens * n_experts <= kPrepThreads;
 }
 
 // ---------------------------------------------------------------------------

@@ -427,7 +427,7 @@ pq_status pq_moe_decode_prep(const float* x, const float* logits, int32_t n_toke
         if (n_tokens < 0 || hidden < 0 || hidden % 32 != 0) return PQ_ERR_SHAPE;
         if (n_experts < 1 || n_experts > kMaxExperts) return PQ_ERR_SHAPE;
         if (top_k < 1 || top_k > kMaxTopK || top_k > n_experts) return PQ_ERR_SHAPE;
-        if (!pqk::decode_prep_supported(n_tokens, n_experts, top_k)) return PQ_ERR_UNSUPPORTED;
+        if (int64_t(n_tokens) * top_k > kMaxAssign) return PQ_ERR_SHAPE;
         if (!x || !logits || !xq || !xd || !topk_ids || !topk_w || !expert_offsets ||
             !sorted_assign || !active_experts || !n_active)
             return PQ_ERR_NULL;

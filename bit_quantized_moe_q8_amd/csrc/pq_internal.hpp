@@ -29,12 +29,14 @@ hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, i
 hipError_t launch_group(const int32_t* ids, int n_assign, int n_experts, int32_t* offsets,
                         int32_t* sorted, int32_t* active, int32_t* n_active, hipStream_t s);
 
-// Fused q8 + route + group for up to 16 tokens in one workgroup.
+// q8 + route + group: one workgroup for up to 16 tokens (the sizes
+// decode_prep_one_launch accepts), else q8 and routing in one launch and the
+// grouping in a second.
 hipError_t launch_decode_prep(const float* x, const float* logits, int n_tokens, int hidden,
                               int n_experts, int top_k, int8_t* xq, float* xd, int32_t* ids,
                               float* w, int32_t* offsets, int32_t* sorted, int32_t* active,
                               int32_t* n_active, float* y_zero, hipStream_t s);
-bool decode_prep_supported(int n_tokens, int n_experts, int top_k);
+bool decode_prep_one_launch(int n_tokens, int n_experts, int top_k);
 
 // Count of 2-bit codes equal to 3 in n_bytes of ternary qs (one workgroup).
 hipError_t launch_validate_ternary(const uint8_t* qs, int64_t n_bytes, int32_t* n_bad, hipStream_t s);

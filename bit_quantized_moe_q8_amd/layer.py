@@ -27,13 +27,12 @@ from . import (PQ_EPI_F32, PQ_EPI_F32_COMBINE, PQ_EPI_SWIGLU_BF16, PQ_EPI_SWIGLU
                moe_matvec_grid1, moe_matvec_sign1, moe_matvec_ternary, moe_route_topk, quantize_act_q8,
                tile_layout)
 
-# When the decode layer fuses the prep kernels (tokens x experts up to one
-# key per thread of the fused kernel), and the combine into the down mat-vec
-# (one token).  Launch latency dominates there; above, the separate kernels
-# spread the work over more of the chip (measured: the fused prep breaks even
-# at 8 tokens x 256 experts), and the fp32 atomic adds of the fused combine
-# start to contend.
-FUSED_PREP_MAX_KEYS = 1024
+# The decode layer's prep (q8, routing, grouping) goes through
+# pq_moe_decode_prep, which takes one launch for a few tokens and two above
+# (the q8 and the routing side by side, then the grouping), one launch fewer
+# than the separate calls.  The combine is fused into the down mat-vec at one
+# token only: launch latency dominates there, while above the fp32 atomic
+# adds of the fused combine start to contend.
 FUSED_COMBINE_MAX_TOKENS = 1
 
 
@@ -46,7 +45,7 @@ class DecodeLayer:
         self.fmt, self.T, self.H, self.I, self.E, self.k = fmt, n_tokens, hidden, inter, n_experts, top_k
         self.device = device
         if fused is None:
-            fused = n_tokens * n_experts <= FUSED_PREP_MAX_KEYS
+            fused = True
         self.fused = bool(fused) and decode_prep_supported(n_tokens, n_experts, top_k)
         if fused_combine is None:
             fused_combine = n_tokens <= FUSED_COMBINE_MAX_TOKENS

@@ -200,17 +200,18 @@ pq_status pq_group_tokens_by_expert(const int32_t *topk_ids, int32_t n_tokens, i
                                     int32_t *n_active, pq_stream stream);
 
 /*
- * Decode prep for a few tokens in one launch: pq_quantize_act_q8 of x
- * [n_tokens][hidden], pq_moe_route_topk of logits [n_tokens][n_experts] and
- * pq_group_tokens_by_expert of the result, with outputs identical to those
- * three calls (same layouts as there); if y_zero != NULL it is also set to
- * zero, float [n_tokens][hidden] (for PQ_EPI_F32_COMBINE).  One workgroup
- * (one wave per token for the selection): 1 <= n_tokens <= 16,
- * n_tokens*top_k <= 256, n_experts <= 1024, top_k <= 16, hidden % 32 == 0;
- * otherwise
- * PQ_ERR_UNSUPPORTED (use the three calls).  (Parakon Runtime README, "How it
- * works": int8 activations; llama-modchip summary, "Key highlights": top-k
- * with no dropping; pxq_llama README, "What's PXQ?": grouped experts.)
+ * Decode prep: pq_quantize_act_q8 of x [n_tokens][hidden], pq_moe_route_topk
+ * of logits [n_tokens][n_experts] and pq_group_tokens_by_expert of the
+ * result, with outputs identical to those three calls (same layouts as
+ * there); if y_zero != NULL it is also set to zero, float [n_tokens][hidden]
+ * (for PQ_EPI_F32_COMBINE).  One launch of one workgroup (one wave per token
+ * for the selection) when 1 <= n_tokens <= 16, n_tokens*top_k <= 256 and
+ * n_tokens*n_experts <= 1024; otherwise two launches: the q8 and the routing side by side in one, the
+ * grouping in the other.  n_experts <= 1024, top_k <= 16 and <= n_experts,
+ * n_tokens*top_k <= 1<<20, hidden % 32 == 0 (PQ_ERR_SHAPE otherwise).
+ * (Parakon Runtime README, "How it works": int8 activations; llama-modchip
+ * summary, "Key highlights": top-k with no dropping; pxq_llama README,
+ * "What's PXQ?": grouped experts.)
  */
 pq_status pq_moe_decode_prep(const float *x, const float *logits, int32_t n_tokens,
                              int32_t hidden, int32_t n_experts, int32_t top_k, int8_t *xq,

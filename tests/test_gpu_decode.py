@@ -468,11 +468,14 @@ def _prep_case(T, E, H, k, logits=None, seed=0):
     assert_tol(to_host(f["w"]), w, w, "prep w vs oracle")
 
 
-@pytest.mark.parametrize("T,E,H,k", [(1, 128, 2048, 8), (8, 256, 4096, 8), (16, 256, 256, 16),
-                                     (4, 1024, 512, 8), (16, 1024, 64, 16), (3, 5, 64, 5),
-                                     (1, 1, 32, 1)])
+@pytest.mark.parametrize("T,E,H,k", [(1, 128, 2048, 8), (8, 128, 4096, 8), (4, 256, 512, 8),
+                                     (1, 1024, 64, 16), (3, 5, 64, 5), (1, 1, 32, 1),
+                                     # two launches (q8 + routing, then grouping)
+                                     (8, 256, 4096, 8), (16, 256, 256, 16), (4, 1024, 512, 8),
+                                     (17, 64, 256, 2), (64, 256, 2048, 8), (300, 128, 512, 4),
+                                     (2048, 256, 4096, 8)])
 def test_decode_prep_matches_separate_calls(T, E, H, k):
-    say("decode prep", T, E, H, k)
+    say("decode prep", T, E, H, k, "one launch" if pq.decode_prep_one_launch(T, E, k) else "two launches")
     _prep_case(T, E, H, k, seed=T * 131 + E)
 
 
@@ -486,9 +489,13 @@ def test_decode_prep_ties():
     _prep_case(6, 64, 128, 8, logits=logits, seed=3)
 
 
-def test_decode_prep_rejects_large():
+def test_decode_prep_limits():
+    """Any batch within the general limits is accepted (checked before any
+    pointer); assignments beyond 1<<20 are a shape error."""
     st = pq.lib().pq_moe_decode_prep(None, None, 17, 64, 8, 2, *([None] * 9), None)
-    assert st == pq.PQ_ERR_UNSUPPORTED
+    assert st == pq.PQ_ERR_NULL
+    st = pq.lib().pq_moe_decode_prep(None, None, (1 << 20) // 2 + 1, 64, 8, 2, *([None] * 9), None)
+    assert st == pq.PQ_ERR_SHAPE
 
 
 @pytest.mark.parametrize("T,k,rows,offset", [

@@ -224,7 +224,7 @@ def test_q8_prefill_full_size_sampled(name):
     fmt, T, H, I, E, k = cfg["fmt"], cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["top_k"]
     grid = inp.get("grid")
     layer = DecodeLayer(fmt, T, H, I, E, k, dev())
-    assert not layer.fused and not layer.fused_combine
+    assert layer.fused and not layer.fused_combine   # prep in two launches, separate combine
     W = {n: weights_to_device(fmt, inp[n], grid) for n in ("gate", "up", "down")}
     layer(to_dev(inp["x"]), to_dev(inp["logits"]), W["gate"], W["up"], W["down"])
     torch.cuda.synchronize()
