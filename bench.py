@@ -16,7 +16,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 decode: q8(x) -> top-k route -> group -> fused gate/up mat-vec (SwiGLU + q8)
 -> down mat-vec -> weighted combine; prefill: route -> group -> gate/up GEMM
 (SwiGLU, bf16 h) -> down GEMM -> combine; the single matrix: q8(x) ->
-mat-vec.  Each step uses the weights of a different layer from a rotating
+mat-vec.  Prefill weights are held in the GEMM's tile layout, built once
+on the device when the pool is made (as a model loader would), outside every
+timed region.  Each step uses the weights of a different layer from a rotating
 pool sized so that the packed bytes touched between two visits of a layer
 exceed the 256 MB last-level cache several times over: weights come from
 HBM, not from cache.  Steps are captured in HIP graphs of --graph-steps layer
