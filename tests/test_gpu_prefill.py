@@ -238,3 +238,37 @@ def test_tile_layout_is_the_stated_permutation(fmt, E, N, K):
     for got, want in pairs:
         assert_equal(to_host(got).view(np.uint8).reshape(-1), want, "tile layout")
     assert T.tiled and not W.tiled
+
+
+@pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
+def test_prefill_layer_in_captured_graph(name):
+    """The prefill layer (route, group, gate/up GEMM, down GEMM, combine: the
+    step the benchmark replays) captured in a graph and replayed three times
+    with eager steps on other inputs between the replays: every replay gives
+    the eager run's ids, h and y bit for bit (no atomics on this path), and
+    the eager run matches the oracle."""
+    say("prefill layer in graph", name)
+    T, E, H, I, k = 200, 8, 512, 512, 2
+    inp = wl.make_workload(name, seed=21, T=T, E=E, H=H, I=I, top_k=k)
+    layer = PrefillLayer(T, H, I, E, k, dev())
+    W = {n: weights_to_device(inp["cfg"]["fmt"], inp[n], inp.get("grid"), tiled=True) for n in ("gate", "up", "down")}
+    x, logits = to_dev(inp["x_bf16"]), to_dev(inp["logits"])
+    other = wl.make_workload(name, seed=22, T=T, E=E, H=H, I=I, top_k=k)
+    ox, olg = to_dev(other["x_bf16"]), to_dev(other["logits"])
+    layer(x, logits, W["gate"], W["up"], W["down"])
+    torch.cuda.synchronize()
+    ref = {"ids": to_host(layer.ids), "h": to_host(layer.h.view(torch.int16)), "y": to_host(layer.y)}
+    gpu = _run(inp)          # the staged check of the same inputs against the oracle
+    _check(inp, gpu)
+    assert_equal(gpu["y_prod"], ref["y"], "eager layer call vs staged run")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x, logits, W["gate"], W["up"], W["down"])
+    for rep in range(3):
+        layer(ox, olg, W["gate"], W["up"], W["down"])   # eager step on other inputs
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_equal(to_host(layer.ids), ref["ids"], "ids (replay %d)" % rep)
+        assert_equal(to_host(layer.h.view(torch.int16)), ref["h"], "h (replay %d)" % rep)
+        assert_equal(to_host(layer.y), ref["y"], "y (replay %d)" % rep)
