@@ -428,8 +428,8 @@ pq_status pq_moe_decode_prep(const float* x, const float* logits, int32_t n_toke
         if (n_experts < 1 || n_experts > kMaxExperts) return PQ_ERR_SHAPE;
         if (top_k < 1 || top_k > kMaxTopK || top_k > n_experts) return PQ_ERR_SHAPE;
         if (int64_t(n_tokens) * top_k > kMaxAssign) return PQ_ERR_SHAPE;
-        if (!x || !logits || !xq || !xd || !topk_ids || !topk_w || !expert_offsets ||
-            !sorted_assign || !active_experts || !n_active)
+        if (!expert_offsets || !active_experts || !n_active) return PQ_ERR_NULL;
+        if (n_tokens > 0 && (!x || !logits || !xq || !xd || !topk_ids || !topk_w || !sorted_assign))
             return PQ_ERR_NULL;
         if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(logits, 4) ||
             !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||

@@ -209,6 +209,8 @@ pq_status pq_group_tokens_by_expert(const int32_t *topk_ids, int32_t n_tokens, i
  * n_tokens*n_experts <= 1024; otherwise two launches: the q8 and the routing side by side in one, the
  * grouping in the other.  n_experts <= 1024, top_k <= 16 and <= n_experts,
  * n_tokens*top_k <= 1<<20, hidden % 32 == 0 (PQ_ERR_SHAPE otherwise).
+ * n_tokens == 0 writes the empty grouping (offsets all 0, *n_active = 0);
+ * then only expert_offsets, active_experts and n_active must be non-NULL.
  * (Parakon Runtime README, "How it works": int8 activations; llama-modchip
  * summary, "Key highlights": top-k with no dropping; pxq_llama README,
  * "What's PXQ?": grouped experts.)

@@ -71,6 +71,21 @@ def test_group_validation(L):
     assert f(A16, 4, 8, 64, A1, A16, A16, A16, S) == pq.PQ_ERR_ALIGN
 
 
+def test_decode_prep_validation(L):
+    import bit_quantized_moe_q8_amd as pq
+    f = L.pq_moe_decode_prep
+
+    def args(T=4, H=256, E=64, k=8, x=A16, off=A16):
+        return (x, A16, T, H, E, k, A16, A16, A16, A16, off, A16, A16, A16, None, S)
+
+    assert f(*args(H=100)) == pq.PQ_ERR_SHAPE                # hidden % 32
+    assert f(*args(k=65)) == pq.PQ_ERR_SHAPE                 # top_k > n_experts
+    assert f(*args(T=(1 << 17) + 1)) == pq.PQ_ERR_SHAPE      # assignments > 2^20
+    assert f(*args(x=None)) == pq.PQ_ERR_NULL
+    assert f(*args(T=0, off=None)) == pq.PQ_ERR_NULL         # the grouping is written at 0 tokens too
+    assert f(*args(x=A1)) == pq.PQ_ERR_ALIGN
+
+
 def _groups(pq, E=8, T=2, k=2):
     return pq.Groups(A16, A16, A16, A16, T, k, E)
 

@@ -6,6 +6,7 @@ The SwiGLU re-quantization is checked on the GPU's own fp32 h (bit-exact),
 because q8 is discontinuous; the free-running chain is checked where no
 near-tie flipped a q8 value.
 """
+import ctypes
 import zlib
 
 import numpy as np
@@ -487,6 +488,22 @@ def test_decode_prep_ties():
     logits[3, ::2] = 2.5
     logits[4] = np.arange(64, dtype=np.float32)[::-1]
     _prep_case(6, 64, 128, 8, logits=logits, seed=3)
+
+
+def test_decode_prep_no_tokens():
+    """Zero tokens: the empty grouping (offsets all 0, no active expert)."""
+    E = 64
+    g = pq.GroupBuffers.empty(0, 4, E, dev())
+    g.expert_offsets.fill_(-1)
+    g.n_active.fill_(-1)
+    st = pq.lib().pq_moe_decode_prep(None, None, 0, 256, E, 4, None, None, None, None,
+                                     ctypes.c_void_p(g.expert_offsets.data_ptr()), None,
+                                     ctypes.c_void_p(g.active_experts.data_ptr()),
+                                     ctypes.c_void_p(g.n_active.data_ptr()), None, None)
+    assert st == pq.PQ_OK
+    torch.cuda.synchronize()
+    assert not to_host(g.expert_offsets).any()
+    assert int(to_host(g.n_active)[0]) == 0
 
 
 def test_decode_prep_limits():
