@@ -139,6 +139,12 @@ void k_matvec(ExpertArgs p) {
     __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : (FMT == kSign1) ? kSignPatterns : 1];
     __shared__ float s_gu[NMAT][MT][TR];
     __shared__ int s_apre[SPLIT ? kMaxExperts + 1 : 1];   // first group number per slot
+    // SPLIT: per slot, expert << 21 | its first assignment (expert < 1024,
+    // assignments <= 2^20), kept from the count pass so that an item's
+    // routing costs no memory round trip; a slot's assignments end where the
+    // next slot's begin (experts in between hold none), the last at the total
+    __shared__ int s_sinfo[SPLIT ? kMaxExperts + 1 : 1];
+    static_assert(kMaxExperts <= 1024, "expert ids are packed in 10 bits");
     __shared__ int s_scan[kWaves + 1];
 
     const int tid = threadIdx.x;
@@ -178,7 +184,10 @@ void k_matvec(ExpertArgs p) {
             int na = 0;
             if (s < n_active) {
                 const int e = p.active[s];
-                const int cnt = p.offsets[e + 1] - p.offsets[e];
+                const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
+                const int cnt = o1 - o0;
+                s_sinfo[s] = (e << 21) | o0;
+                if (s == n_active - 1) s_sinfo[n_active] = o1;
                 // experts left to the int8-MFMA tile kernel get no groups
                 na = (p.heavy_min > 0 && cnt >= p.heavy_min) ? 0 : (cnt + MT - 1) / MT;
             }
@@ -268,10 +277,15 @@ void k_matvec(ExpertArgs p) {
             }
             slot = __builtin_amdgcn_readfirstlane(lo);
             g = __builtin_amdgcn_readfirstlane(grp - s_apre[lo]);
+            const int si = __builtin_amdgcn_readfirstlane(s_sinfo[slot]);
+            mt.e = si >> 21;
+            mt.beg = si & ((1 << 21) - 1);
+            mt.m = (__builtin_amdgcn_readfirstlane(s_sinfo[slot + 1]) & ((1 << 21) - 1)) - mt.beg;
+        } else {
+            mt.e = load_uniform(p.active + slot);
+            mt.beg = load_uniform(p.offsets + mt.e);
+            mt.m = load_uniform(p.offsets + mt.e + 1) - mt.beg;
         }
-        mt.e = load_uniform(p.active + slot);
-        mt.beg = load_uniform(p.offsets + mt.e);
-        mt.m = load_uniform(p.offsets + mt.e + 1) - mt.beg;
         mt.base = SPLIT ? g * MT : 0;
         const int mc = min(MT, mt.m - mt.base);
 #pragma unroll

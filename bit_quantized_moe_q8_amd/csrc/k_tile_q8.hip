@@ -109,6 +109,14 @@ void k_tile_q8(ExpertArgs p) {
     __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : (FMT == kSign1) ? kSignPatterns : 1];
     __shared__ float s_gu[NMAT][(NMAT == 2) ? TR : 1][kTok + 1];
     __shared__ int s_pre[kMaxExperts + 1];   // first chunk number per slot
+    // Small batches: per slot, expert << 21 | its first assignment (expert <
+    // 1024, assignments <= 2^20), kept from the count pass so that an item's
+    // routing costs no memory round trip (its items are short); a slot's
+    // assignments end where the next slot's begin (experts in between hold
+    // none), the last at the total.
+    constexpr bool kSlotCache = kTok <= 32;
+    __shared__ int s_sinfo[kSlotCache ? kMaxExperts + 1 : 1];
+    static_assert(kMaxExperts <= 1024, "expert ids are packed in 10 bits");
     __shared__ int s_scan[kWaves + 1];
     __shared__ int s_asg[kTok];
     __shared__ int s_arow[kTok];
@@ -144,7 +152,12 @@ void k_tile_q8(ExpertArgs p) {
         int nc = 0;
         if (s < n_active) {
             const int e = p.active[s];
-            const int m = p.offsets[e + 1] - p.offsets[e];
+            const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
+            if constexpr (kSlotCache) {
+                s_sinfo[s] = (e << 21) | o0;
+                if (s == n_active - 1) s_sinfo[n_active] = o1;
+            }
+            const int m = o1 - o0;
             nc = m >= hmin ? (m + kTok - 1) / kTok : 0;
         }
         const int ex = block_exclusive_scan(nc, s_scan);
@@ -179,9 +192,17 @@ void k_tile_q8(ExpertArgs p) {
         }
         const int slot = __builtin_amdgcn_readfirstlane(lo);
         const int cbeg = (c - __builtin_amdgcn_readfirstlane(s_pre[slot])) * kTok;
-        const int e = load_uniform(p.active + slot);
-        const int beg = load_uniform(p.offsets + e);
-        const int m = load_uniform(p.offsets + e + 1) - beg;
+        int e, beg, m;
+        if constexpr (kSlotCache) {
+            const int si = __builtin_amdgcn_readfirstlane(s_sinfo[slot]);
+            e = si >> 21;
+            beg = si & ((1 << 21) - 1);
+            m = (__builtin_amdgcn_readfirstlane(s_sinfo[slot + 1]) & ((1 << 21) - 1)) - beg;
+        } else {
+            e = load_uniform(p.active + slot);
+            beg = load_uniform(p.offsets + e);
+            m = load_uniform(p.offsets + e + 1) - beg;
+        }
         const int mcount = min(kTok, m - cbeg);
         const int jn = (mcount + kSub - 1) / kSub;   // live column subtiles, 1..4
         const int n0 = tile * TR;

@@ -191,6 +191,9 @@ pq_status pq_moe_route_topk(const float *logits, int32_t n_tokens, int32_t n_exp
  *   sorted_assign [A]: every assignment id, ordered by (expert, id);
  *   active_experts [n_experts]: the experts with at least one assignment, in
  *   increasing id order; *n_active: their number.
+ * The expert kernels rely on these invariants (for a grouping made by hand
+ * as well): an expert's assignments end where the next active expert's
+ * begin.
  * topk_ids must hold values in [0, n_experts) (out-of-range ids give
  * unspecified output).  n_experts <= 1024; A <= 1<<20.
  */
