@@ -47,53 +47,88 @@ hipError_t launch_quantize_q8(const float* x, int64_t n_blocks, int8_t* xq, floa
 
 // ---------------------------------------------------------------------------
 // Router top-k + softmax over the selected logits (no dropping: llama-modchip
-// summary, "Key highlights").  One workgroup per token.  Each logit gets the
+// summary, "Key highlights").  One wave per token.  Each logit gets the
 // 64-bit key (order-preserving bits of the value, then the complement of its
 // expert id), so that a larger key means a larger logit or an equal logit
-// with a lower id; the rank of a logit is the number of larger keys, and the
-// logits with rank < k are the selection in output order.  One pass, no
-// serial arg-max rounds.  -0.0 is folded to +0.0 first (they compare equal).
+// with a lower id; -0.0 is folded to +0.0 first (they compare equal).  The
+// lanes hold the token's keys (expert lane + 64 i in slot i), and k rounds of
+// a wave-wide maximum pick the selection in descending key order, the lane
+// holding the winner clearing it.  The selected value comes back from its
+// key (the fold changes no output: the softmax takes differences of values).
 // ---------------------------------------------------------------------------
 constexpr int kRouteMaxExperts = 1024;
+constexpr int kRouteTokensPerWg = 256 / kWave;   // one token per wave
 
-// Top-k routing of tokens t0, t0 + tstep, ... by one workgroup of 256
-// threads (the body of k_route_topk, shared with the fused q8 + route launch).
-__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int T, int E, int k,
-                                             int32_t* __restrict__ ids, float* __restrict__ w, int t0,
-                                             int tstep, uint64_t* s_key, float* s_val, int* s_idx) {
-    const int tid = threadIdx.x;
-    for (int t = t0; t < T; t += tstep) {
-        const float* l = logits + static_cast<int64_t>(t) * E;
-        for (int e = tid; e < E; e += 256) {
-            float v = l[e];
-            if (v == 0.0f) v = 0.0f;
-            s_key[e] = route_key(v, e);
+template <int NK>
+__device__ __forceinline__ void route_token_wave(const float* __restrict__ l, int E, int k, int lane,
+                                                 int32_t* __restrict__ ids, float* __restrict__ w) {
+    uint64_t key[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        const int e = lane + kWave * i;
+        float v = e < E ? l[e] : 0.0f;
+        if (v == 0.0f) v = 0.0f;
+        key[i] = e < E ? route_key(v, e) : 0ull;   // real keys are nonzero
+    }
+    uint64_t mine = 0;   // lane j < k: the key of selection j
+    for (int r = 0; r < k; ++r) {
+        uint64_t m = key[0];
+#pragma unroll
+        for (int i = 1; i < NK; ++i) m = key[i] > m ? key[i] : m;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t o = __shfl_xor(m, off);
+            m = o > m ? o : m;
         }
-        __syncthreads();
-        for (int e = tid; e < E; e += 256) {
-            const uint64_t me = s_key[e];
-            int rank = 0;
-#pragma unroll 8
-            for (int j = 0; j < E; ++j) rank += (s_key[j] > me) ? 1 : 0;
-            if (rank < k) {
-                s_val[rank] = l[e];
-                s_idx[rank] = e;
-            }
+        if (lane == r) mine = m;
+        const int e = static_cast<int>(~static_cast<uint32_t>(m));
+        if ((e & (kWave - 1)) == lane) {
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+                if (i == e / kWave) key[i] = 0;
         }
-        __syncthreads();
-        if (tid < 64) route_softmax_store(s_val, s_idx, k, tid, ids + static_cast<int64_t>(t) * k,
-                                          w + static_cast<int64_t>(t) * k);
-        __syncthreads();
+    }
+    // softmax over the k selected (the summation order of route_softmax_store)
+    const uint32_t hi = static_cast<uint32_t>(mine >> 32);
+    const float v = __builtin_bit_cast(float, (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+    const bool on = lane < k;
+    const float v0 = __shfl(v, 0);
+    const float ex = on ? expf(v - v0) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (on) {
+        ids[lane] = static_cast<int32_t>(~static_cast<uint32_t>(mine));
+        w[lane] = ex / sum;
     }
 }
+
+// Top-k routing of the tokens of token groups g0, g0 + gstep, ... (four
+// tokens per group, one per wave) by one workgroup of 256 threads: the body
+// of k_route_topk, shared with the fused q8 + route launch.
+__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int T, int E, int k,
+                                             int32_t* __restrict__ ids, float* __restrict__ w, int g0,
+                                             int gstep) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    for (int g = g0; g * kRouteTokensPerWg < T; g += gstep) {
+        const int t = g * kRouteTokensPerWg + wv;
+        if (t >= T) continue;   // uniform over the wave
+        const float* l = logits + static_cast<int64_t>(t) * E;
+        int32_t* it = ids + static_cast<int64_t>(t) * k;
+        float* wt = w + static_cast<int64_t>(t) * k;
+        if (E <= 64) route_token_wave<1>(l, E, k, lane, it, wt);
+        else if (E <= 128) route_token_wave<2>(l, E, k, lane, it, wt);
+        else if (E <= 256) route_token_wave<4>(l, E, k, lane, it, wt);
+        else if (E <= 512) route_token_wave<8>(l, E, k, lane, it, wt);
+        else route_token_wave<16>(l, E, k, lane, it, wt);
+    }
+}
+static_assert(kRouteMaxExperts == 16 * kWave, "16 keys per lane cover every expert");
 
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
-    __shared__ uint64_t s_key[kRouteMaxExperts];
-    __shared__ float s_val[16];
-    __shared__ int s_idx[16];
-    route_tokens(logits, T, E, k, ids, w, blockIdx.x, gridDim.x, s_key, s_val, s_idx);
+    route_tokens(logits, T, E, k, ids, w, blockIdx.x, gridDim.x);
 }
 
 // The q8 of x and the top-k routing in one launch (the decode prep of
@@ -105,11 +140,8 @@ __global__ __launch_bounds__(256) void k_q8_route(const float* __restrict__ x, i
                                                   const float* __restrict__ logits, int T, int E, int k,
                                                   int32_t* __restrict__ ids, float* __restrict__ w,
                                                   int route_wgs, float* __restrict__ y_zero, int64_t n_y) {
-    __shared__ uint64_t s_key[kRouteMaxExperts];
-    __shared__ float s_val[16];
-    __shared__ int s_idx[16];
     if (static_cast<int>(blockIdx.x) < route_wgs) {   // uniform over the workgroup
-        route_tokens(logits, T, E, k, ids, w, blockIdx.x, route_wgs, s_key, s_val, s_idx);
+        route_tokens(logits, T, E, k, ids, w, blockIdx.x, route_wgs);
         return;
     }
     const int64_t t = static_cast<int64_t>(blockIdx.x - route_wgs) * 256 + threadIdx.x;
@@ -120,13 +152,18 @@ __global__ __launch_bounds__(256) void k_q8_route(const float* __restrict__ x, i
     }
 }
 
+// Workgroups of the routing: one per four tokens, at most 16 per CU.
+static int route_workgroups(int n_tokens) {
+    const int groups = (n_tokens + kRouteTokensPerWg - 1) / kRouteTokensPerWg;
+    const int cap = cu_count() * 16;
+    return groups < cap ? groups : cap;
+}
+
 hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, int top_k,
                              int32_t* ids, float* w, hipStream_t s) {
     if (n_tokens == 0) return hipSuccess;
-    const int cap = cu_count() * 16;
-    const unsigned grid = static_cast<unsigned>(n_tokens < cap ? n_tokens : cap);
-    hipLaunchKernelGGL(k_route_topk, dim3(grid), dim3(256), 0, s, logits, n_tokens, n_experts,
-                       top_k, ids, w);
+    hipLaunchKernelGGL(k_route_topk, dim3(static_cast<unsigned>(route_workgroups(n_tokens))), dim3(256), 0, s,
+                       logits, n_tokens, n_experts, top_k, ids, w);
     return hipGetLastError();
 }
 
@@ -257,8 +294,9 @@ hipError_t launch_group(const int32_t* ids, int n_assign, int n_experts, int32_t
 // and the stable grouping in one workgroup (one launch instead of three; at
 // a handful of tokens each of those is a few microseconds of launch and
 // ramp for almost no work).  Results are identical to the three kernels
-// above: the same q8 lanes, the same rank-by-key selection and softmax, and
-// a grouping that is unique by definition.  Optionally zeroes y (for the
+// above: the same q8 lanes, the same keys (so the same selection, here
+// ranked by counting larger keys) and softmax, and a grouping that is unique
+// by definition.  Optionally zeroes y (for the
 // accumulating combine epilogue of the down mat-vec).
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 1024;
@@ -427,8 +465,7 @@ hipError_t launch_decode_prep(const float* x, const float* logits, int n_tokens,
     }
     // two launches: q8 and routing side by side, then the grouping
     if (n_tokens > 0) {
-        const int cap = cu_count() * 16;
-        const int route_wgs = n_tokens < cap ? n_tokens : cap;
+        const int route_wgs = route_workgroups(n_tokens);
         const int64_t n_blocks = static_cast<int64_t>(n_tokens) * (hidden / 32);
         const int64_t q8_wgs = (n_blocks * 8 + 255) / 256;
         hipLaunchKernelGGL(k_q8_route, dim3(static_cast<unsigned>(route_wgs + (q8_wgs > 0 ? q8_wgs : 1))),
