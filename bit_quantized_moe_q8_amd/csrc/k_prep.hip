@@ -169,35 +169,39 @@ hipError_t launch_route_topk(const float* logits, int n_tokens, int n_experts, i
 
 // ---------------------------------------------------------------------------
 // Stable grouping by expert (grouped MoE path: pxq_llama README, "What's
-// PXQ?").  One workgroup of 8 waves.  Wave w owns the contiguous assignment
-// range [w*C, (w+1)*C):
+// PXQ?").  One workgroup of W waves (8, or 16 for large batches).  Wave w
+// owns the contiguous assignment range [w*C, (w+1)*C):
 //   1. per-wave histograms hist[w][e] in LDS;
-//   2. per expert: exclusive prefix over waves, then an exclusive scan over
-//      experts gives expert_offsets, and hist[w][e] becomes the first output
-//      slot of wave w's assignments of expert e;
+//   2. per expert: exclusive prefix over waves (the W counts read into
+//      registers at once), then an exclusive scan over experts gives
+//      expert_offsets, and hist[w][e] becomes the first output slot of wave
+//      w's assignments of expert e;
 //   3. each wave walks its range 64 at a time in order; lanes with equal keys
 //      are found with one ballot per key bit, the rank among them is a
 //      popcount of the lower lanes, and the highest lane of each key advances
 //      hist[w][e].  Ranks follow assignment order, so the sort is stable.
+// Step 3 is a chain of dependent ballots and LDS updates per row of 64, so a
+// large batch is spread over 16 waves (half the rows per wave).
 // ---------------------------------------------------------------------------
-constexpr int kGroupWaves = 8;
-constexpr int kGroupThreads = kGroupWaves * 64;
 constexpr int kGroupMaxExperts = 1024;
 constexpr int kGroupBatch = 8;   // rows of 64 ids loaded per round trip
+constexpr int kGroupWideMinAssign = 4096;   // 16 waves from this many assignments
 
-__global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ ids, int A,
-                                                         int E, int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ sorted,
-                                                         int32_t* __restrict__ active,
-                                                         int32_t* __restrict__ n_active) {
-    __shared__ int hist[kGroupWaves * kGroupMaxExperts];
-    __shared__ int wave_tot[kGroupWaves];
+template <int W>
+__global__ __launch_bounds__(W * kWave) void k_group(const int32_t* __restrict__ ids, int A, int E,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted,
+                                                     int32_t* __restrict__ active,
+                                                     int32_t* __restrict__ n_active) {
+    constexpr int NT = W * kWave;
+    __shared__ int hist[W * kGroupMaxExperts];
+    __shared__ int wave_tot[W];
     __shared__ int carry[2];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-    for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) hist[i] = 0;
+    for (int i = tid; i < W * E; i += NT) hist[i] = 0;
     __syncthreads();
-    const int chunk = (A + kGroupWaves - 1) / kGroupWaves;
+    const int chunk = (A + W - 1) / W;
     const int beg = min(wave * chunk, A), end = min(beg + chunk, A);
     // kGroupBatch rows of 64 ids are loaded together (independent loads in
     // flight) before they are counted, so a long range costs a few memory
@@ -215,15 +219,19 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
     }
     __syncthreads();
 
-    // Experts e = tid + 512*half, processed in two halves to cover E <= 1024.
+    // Experts e = tid + NT*part, in parts of NT to cover E <= 1024.
     int run_off = 0, run_act = 0;
-    for (int half = 0; half < 2; ++half) {
-        const int e = tid + half * kGroupThreads;
+    for (int part = 0; part * NT < E; ++part) {
+        const int e = tid + part * NT;
+        int hv[W];
         int cnt = 0;
         if (e < E) {
-            for (int w = 0; w < kGroupWaves; ++w) {
-                const int h = hist[w * E + e];
-                hist[w * E + e] = cnt;
+#pragma unroll
+            for (int w = 0; w < W; ++w) hv[w] = hist[w * E + e];
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const int h = hv[w];
+                hv[w] = cnt;
                 cnt += h;
             }
         }
@@ -231,10 +239,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
         const int act = run_act + block_exclusive_scan(cnt > 0 ? 1 : 0, wave_tot);
         if (e < E) {
             offsets[e] = off;
-            for (int w = 0; w < kGroupWaves; ++w) hist[w * E + e] += off;
+#pragma unroll
+            for (int w = 0; w < W; ++w) hist[w * E + e] = hv[w] + off;
             if (cnt > 0) active[act] = e;
         }
-        if (tid == kGroupThreads - 1) {
+        if (tid == NT - 1) {
             carry[0] = off + cnt;
             carry[1] = act + (cnt > 0 ? 1 : 0);
         }
@@ -284,8 +293,12 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
 
 hipError_t launch_group(const int32_t* ids, int n_assign, int n_experts, int32_t* offsets,
                         int32_t* sorted, int32_t* active, int32_t* n_active, hipStream_t s) {
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), 0, s, ids, n_assign, n_experts,
-                       offsets, sorted, active, n_active);
+    if (n_assign >= kGroupWideMinAssign)
+        hipLaunchKernelGGL(k_group<16>, dim3(1), dim3(16 * kWave), 0, s, ids, n_assign, n_experts, offsets,
+                           sorted, active, n_active);
+    else
+        hipLaunchKernelGGL(k_group<8>, dim3(1), dim3(8 * kWave), 0, s, ids, n_assign, n_experts, offsets,
+                           sorted, active, n_active);
     return hipGetLastError();
 }
 
