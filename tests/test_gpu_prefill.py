@@ -20,6 +20,9 @@ from gpu_util import assert_equal, assert_tol, dev, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
+# rows of one expert's group that one GEMM work item takes (its chunk)
+CHUNK = 96
+
 
 def _run(inp, sample=None, fused=False):
     cfg = inp["cfg"]
@@ -83,10 +86,11 @@ def _check(inp, gpu, sample=None):
 
 @pytest.mark.parametrize("T,E,H,I,k,seed", [
     (48, 8, 512, 256, 2, 1),      # every expert ~12 rows
-    (200, 4, 256, 256, 2, 2),     # ~100 rows per expert: two 64-row chunks, ragged second
+    (200, 4, 256, 256, 2, 2),     # ~100 rows per expert: two chunks, ragged second
     (37, 16, 768, 512, 4, 3),     # K = 3 blocks for gate/up, 2 for down
     (5, 64, 1024, 256, 3, 4),     # most experts empty, single rows
-    (130, 1, 512, 256, 1, 5),     # one expert takes every token (3 chunks)
+    (130, 1, 512, 256, 1, 5),     # one expert takes every token (two chunks)
+    (200, 1, 512, 256, 1, 6),     # one expert, three chunks (96 + 96 + 8 rows)
 ])
 @pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
 @pytest.mark.parametrize("fused", [True, False])
@@ -104,8 +108,8 @@ def test_prefill_layer_small(T, E, H, I, k, seed, name, fused):
 
 def _every_expert_sample(inp):
     """Assignments that cover every expert with rows: the first row of its
-    last 64-row chunk (the GEMM's work unit), its last row, and one row drawn
-    at random from its group; sorted, unique."""
+    last chunk (the GEMM's work unit), its last row, and one row drawn at
+    random from its group; sorted, unique."""
     cfg = inp["cfg"]
     ids, _ = oracle.route_topk(inp["logits"], cfg["top_k"])
     off, srt, act = oracle.group(ids, cfg["E"])
@@ -113,15 +117,15 @@ def _every_expert_sample(inp):
     pick = []
     for e in act:
         b, n = int(off[e]), int(off[e + 1] - off[e])
-        pick += [srt[b + (n - 1) // 64 * 64], srt[b + n - 1], srt[b + int(rng.integers(n))]]
+        pick += [srt[b + (n - 1) // CHUNK * CHUNK], srt[b + n - 1], srt[b + int(rng.integers(n))]]
     return np.unique(np.asarray(pick)), act
 
 
 @pytest.mark.parametrize("name", ["grid1_moe_prefill_t2048", "sign1_moe_prefill_t2048"])
 def test_prefill_layer_full_size_sampled(name):
     """2048 tokens, hidden 4096, intermediate 1536, 256 experts, top-8: all
-    experts run on the GPU; for every expert the first row of its last 64-row
-    chunk, its last row and a random row are checked in every column (G, U,
+    experts run on the GPU; for every expert the first row of its last chunk,
+    its last row and a random row are checked in every column (G, U,
     h, out), so an expert-index or chunk-offset error anywhere shows."""
     say("prefill full size", name)
     inp = wl.make_workload(name)
@@ -150,6 +154,48 @@ def test_gemm_partial_column_tiles(N, K, T, E, k):
     A = T * k
     y_ref, t_ref = moe.grouped_matvec_bf16("grid1", planes, grid, ids, x, np.arange(A) // k, K)
     assert_tol(to_host(out), y_ref, t_ref, "out")
+
+
+@pytest.mark.parametrize("pattern", ["zeros", "equal", "wide"])
+def test_gemm_grid1_scale_patterns(pattern):
+    """The GEMM applies each 256-weight block's scale to one running
+    accumulator (rescaled by the ratio of consecutive nonzero scales, weights
+    of zero-scale blocks masked): block scales of zero (first block, runs of
+    zeros, whole rows), equal consecutive scales, and scales spread over the
+    fp16 range, against the oracle at the stated bound."""
+    say("gemm grid1 scales", pattern)
+    N, K, T, E, k, seed = 48, 2048, 120, 3, 2, 31
+    planes = wl.stack_experts("grid1", seed, "w", E, N, K)
+    rng = np.random.default_rng(seed)
+    d = planes["d"].view(np.float16).astype(np.float32).reshape(E, N, K // 256)
+    if pattern == "zeros":
+        d[rng.random(d.shape) < 0.3] = 0.0
+        d[:, 0:4, 0] = 0.0          # the first block
+        d[:, 4:8, 2:6] = 0.0        # a run of blocks
+        d[:, 8:16, :] = 0.0         # whole rows
+        d[:, 16:20, 1:] = 0.0       # only the first block nonzero
+    elif pattern == "equal":
+        d[:, :24, :] = d[:, :24, :1]           # one scale per row
+        d[:, 24:, 2::2] = d[:, 24:, 1:-1:2]    # pairs of equal neighbours
+    else:
+        d = (2.0 ** rng.integers(-20, 12, size=d.shape) * rng.uniform(1, 2, size=d.shape)).astype(np.float32)
+        d *= np.where(rng.random(d.shape) < 0.2, -1.0, 1.0)
+    planes["d"] = d.astype(np.float16).reshape(planes["d"].shape).view(planes["d"].dtype)
+    grid = wl.codebook(seed)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = wl.activations_bf16(seed, T, K)
+    g = pq.group_tokens_by_expert(to_dev(ids), E)
+    W = weights_to_device("grid1", planes, grid, tiled=True)
+    out = pq.moe_gemm_dequant_tile(W, None, g, to_dev(x), True, pq.PQ_EPI_F32)
+    torch.cuda.synchronize()
+    A = T * k
+    y_ref, t_ref = moe.grouped_matvec_bf16("grid1", planes, grid, ids, x, np.arange(A) // k, K)
+    got = to_host(out)
+    assert_tol(got, y_ref, t_ref, "out")
+    if pattern == "zeros":
+        rows_zero = np.zeros((A, N), bool)
+        rows_zero[:, 8:16] = True
+        assert np.all(got[rows_zero] == 0.0)
 
 
 @pytest.mark.parametrize("N,K,T,E,k", [(104, 512, 40, 3, 2), (296, 1024, 9, 5, 2), (8, 512, 3, 2, 1),
