@@ -15,8 +15,8 @@ The headline (the top-level metric/value/roofline) is the largest of them, the
 A step is one pass of the whole hot path over one batch of synthetic input:
 decode: q8(x) -> top-k route -> group -> fused gate/up mat-vec (SwiGLU + q8)
 -> down mat-vec -> weighted combine; prefill: route -> group -> gate/up GEMM
-(SwiGLU, bf16 h) -> down GEMM -> combine; the single matrix: q8(x) ->
-mat-vec.  Prefill weights are held in the GEMM's tile layout, built once
+(SwiGLU, bf16 h) -> down GEMM -> combine; the single matrix: q8(x) and
+the mat-vec in one launch.  Prefill weights are held in the GEMM's tile layout, built once
 on the device when the pool is made (as a model loader would), outside every
 timed region.  Each step uses the weights of a different layer from a rotating
 pool sized so that the packed bytes touched between two visits of a layer
@@ -442,8 +442,9 @@ def bench_layer_workload(name, args, peaks):
 
 
 def bench_single_matrix(name, args, peaks):
-    """The single 1024x1024 ternary mat-vec: per call (q8 + one-token mat-vec,
-    one distinct matrix per step from a 1.1 GB pool) and the streaming rate of
+    """The single 1024x1024 ternary mat-vec: per call (q8 and the mat-vec in
+    one launch, pq_matvec_x32_ternary; one distinct matrix per step from a
+    1.1 GB pool) and the streaming rate of
     the mat-vec over stacked launches of 1024 matrices each (1024 tokens, one
     matrix per token)."""
     import numpy as np
@@ -464,23 +465,19 @@ def bench_single_matrix(name, args, peaks):
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     pool = pq.TernaryWeights(**wl.torch_ternary_planes(gen, P, N, K, dev))
-    single = [pq.TernaryWeights(pool.qs[i:i + 1], pool.d[i:i + 1]) for i in range(P)]
-    xs = [torch.from_numpy(wl.activations_f32(seed, 1, K, index=i)).to(dev) for i in range(64)]
-    g1 = pq.group_tokens_by_expert(torch.zeros((1, 1), dtype=torch.int32, device=dev), 1)
-    xq = torch.empty((1, K), dtype=torch.int8, device=dev)
-    xd = torch.empty((1, K // 32), dtype=torch.float32, device=dev)
-    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    xs = [torch.from_numpy(wl.activations_f32(seed, 1, K, index=i)).to(dev).view(-1) for i in range(64)]
+    y = torch.empty((N,), dtype=torch.float32, device=dev)
 
     def step(i):
-        pq.quantize_act_q8(xs[i % 64], xq, xd)
-        pq.moe_matvec_ternary(single[i], None, g1, xq, xd, True, pq.PQ_EPI_F32, y)
+        # matrix i of the pool, q8 of x inside the same launch
+        pq.matvec_x32(pool, xs[i % 64], i, y)
 
     K_, W = args.steps, args.warmup
     runner = StepRunner(step, P, M, not args.no_graph)
     ms_total, _ = time_steps(runner, K_, W)
     ms_step = ms_total / K_
     gbs = K_ * per_matrix / (ms_total * 1e-3) / 1e9
-    log("  per call: %.2f us (q8 + mat-vec), %.1f GB/s packed" % (ms_step * 1e3, gbs))
+    log("  per call: %.2f us (q8 and mat-vec in one launch), %.1f GB/s packed" % (ms_step * 1e3, gbs))
 
     # stacked: launch j runs matrices [j*S, (j+1)*S), token t on matrix t
     stacks = [pq.TernaryWeights(pool.qs[j * S:(j + 1) * S], pool.d[j * S:(j + 1) * S]) for j in range(P // S)]
@@ -529,9 +526,9 @@ def bench_single_matrix(name, args, peaks):
            "value": round(gbs, 2), "unit": "GB/s", "dtype": "int8", "packed_gbs": round(gbs, 2),
            "stacked_gbs": round(ach, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
            "packed_bytes_per_step": per_matrix, "tokens_per_s": round(1.0 / (ms_step * 1e-3), 1),
-           "dispatch": {"call": pq.plan(pq.PQ_CALL_MATVEC, "ternary", 1, 1, 1, N, K), "stacked": plan},
+           "dispatch": {"call": "pq_matvec_x32_ternary (one launch)", "stacked": plan},
            "roofline": roofline, "cpu_baseline": cpu}
-    del pool, single, stacks, runner
+    del pool, stacks, runner
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res

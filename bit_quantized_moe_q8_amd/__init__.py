@@ -118,6 +118,9 @@ def _load():
         "pq_peak_mfma_bf16": [i32, i32, p, p, p, p],
         "pq_tile_layout_grid1": [ctypes.POINTER(Grid1W), p, p, p],
         "pq_tile_layout_sign1": [ctypes.POINTER(Sign1W), p, p, p],
+        "pq_matvec_x32_ternary": [ctypes.POINTER(TernaryW), i32, p, p, p],
+        "pq_matvec_x32_grid1": [ctypes.POINTER(Grid1W), i32, p, p, p],
+        "pq_matvec_x32_sign1": [ctypes.POINTER(Sign1W), i32, p, p, p],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -479,6 +482,28 @@ def moe_matvec_sign1(w: Sign1Weights, w_up, groups: GroupBuffers, xq, xd, act_by
                      epilogue: int = PQ_EPI_F32, out0=None, out1=None, dbg: dict = None):
     """pq_moe_matvec_sign1 (see include/pq.h)."""
     return _matvec("pq_moe_matvec_sign1", w, w_up, groups, xq, xd, act_by_token, epilogue, out0, out1, dbg)
+
+
+def matvec_x32(w, x, expert: int = 0, y=None):
+    """pq_matvec_x32_{ternary,grid1,sign1} (see include/pq.h): y [rows] =
+    W[expert] . q8(x) for one fp32 row x [cols], in one launch."""
+    fn_name = {"TernaryWeights": "pq_matvec_x32_ternary", "Grid1Weights": "pq_matvec_x32_grid1",
+               "Sign1Weights": "pq_matvec_x32_sign1"}.get(type(w).__name__)
+    if fn_name is None:
+        raise ValueError("expected TernaryWeights, Grid1Weights or Sign1Weights")
+    _need_layout(w, False, fn_name)
+    E, rows, cols = w.shape
+    if not 0 <= int(expert) < E:
+        raise ValueError("expert %d outside [0, %d)" % (expert, E))
+    _dt(x, torch.float32)
+    _need(x, "x", cols)
+    if y is None:
+        y = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _need(y, "y", rows, *_F32)
+    ws = w.cstruct()
+    rc = getattr(_lib, fn_name)(ctypes.byref(ws), int(expert), _ptr(x), _ptr(y), _stream())
+    _check(fn_name, rc)
+    return y
 
 
 def moe_tile_q8_ternary(w: TernaryWeights, w_up, groups: GroupBuffers, xq, xd, act_by_token: bool,

@@ -110,7 +110,11 @@ constexpr int kSignPatterns = 256;
 // pairwise order ((S0 + S1) + (S2 + S3)) that the single-group lane tree
 // (seg_sum over the whole row) uses for the same chunks, so the totals are
 // bit-identical to KS = 1 and to the grouped mat-vec.
-template <int FMT, int LPR, int EPI, bool ABT, bool ROUTE, int NK = 1, int KS = 1>
+//
+// QX (one matrix, F32 epilogue): no routing or grouping; the workgroup
+// quantizes the fp32 row ra.x itself as ROUTE does and multiplies it by
+// expert p.expert0, so a single mat-vec from fp32 activations is one launch.
+template <int FMT, int LPR, int EPI, bool ABT, bool ROUTE, int NK = 1, int KS = 1, bool QX = false>
 __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, RouteArgs ra) {
     using CK = Chunk<FMT>;
     constexpr int NT = kThreads * KS;                 // threads of the workgroup
@@ -129,6 +133,8 @@ __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, Rou
     constexpr int ACT_DW = CK::kWeights / 4;          // activation dwords per chunk
     constexpr int kMaxCols = 64 * CK::kWeights;       // widest row the launcher accepts
     static_assert(!ROUTE || (ABT && EPI == kEpiSwigluQ8), "routing only in the gate/up kernel");
+    static_assert(!QX || (ABT && !ROUTE && EPI == kEpiF32), "in-kernel q8 of one matrix: F32 only");
+    constexpr bool kX32 = ROUTE || QX;   // fp32 activations quantized in the kernel
 
     // grid1: the codebook; sign1: the 256 byte patterns of +-1
     __shared__ uint2 s_grid[(FMT == kGrid1) ? kGridEntries : (FMT == kSign1) ? kSignPatterns : 1];
@@ -138,8 +144,8 @@ __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, Rou
     __shared__ int s_part[(ROUTE && NK <= 4) ? 2 : 1][(ROUTE && NK <= 4) ? 2 * kWave : 1];
     __shared__ float s_tv[ROUTE ? 16 : 1];
     __shared__ int s_ti[ROUTE ? 16 : 1];
-    __shared__ uint4 s_xq[ROUTE ? kMaxCols / 16 : 1];
-    __shared__ float s_xd[ROUTE ? kMaxCols / 32 : 1];
+    __shared__ uint4 s_xq[kX32 ? kMaxCols / 16 : 1];
+    __shared__ float s_xd[kX32 ? kMaxCols / 32 : 1];
 
     const int tid = threadIdx.x;
     const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -188,12 +194,10 @@ __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, Rou
         for (int s = 0; s < SUBS; ++s) xs[s] = xdp[s];
     };
     int n_active, e, a0;
-    constexpr int kXP = ROUTE ? (kMaxCols / 4 + NT - 1) / NT : 1;   // float4 passes of the q8
+    constexpr int kXP = kX32 ? (kMaxCols / 4 + NT - 1) / NT : 1;   // float4 passes of the q8
     float4 xv[kXP];
-    if constexpr (ROUTE) {
-        // ---- the fp32 activations (kept for the q8 below) and the logits:
-        // expert l + 64 i in lane l, as an order-preserving 32-bit key
-        // (0 = absent; no finite logit maps to 0)
+    if constexpr (kX32) {
+        // ---- the fp32 activations (kept for the q8 below)
         const float4* x4 = reinterpret_cast<const float4*>(ra.x);
         const int n4 = cols / 4;
 #pragma unroll
@@ -201,6 +205,10 @@ __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, Rou
             const int i = u * NT + tid;
             xv[u] = i < n4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    }
+    if constexpr (ROUTE) {
+        // ---- the logits: expert l + 64 i in lane l, as an order-preserving
+        // 32-bit key (0 = absent; no finite logit maps to 0)
         const int E = p.n_experts, k = p.top_k;
         const bool lists = blockIdx.x == 0 && blockIdx.y == 0;
         if constexpr (NK <= 4) {
@@ -299,6 +307,11 @@ __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, Rou
         // slot = rank: the grid holds exactly top_k slots
         n_active = k;
         a0 = slot;
+    } else if constexpr (QX) {
+        // one matrix, one assignment (its output row 0)
+        n_active = 1;
+        e = p.expert0;
+        a0 = 0;
     } else {
         // by token at one token: every assignment reads row 0
         if constexpr (ABT) load_act(0);
@@ -308,7 +321,7 @@ __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, Rou
         a0 = load_uniform(p.sorted + slot);
         if (slot >= n_active) return;
     }
-    const bool dense = ROUTE || n_active == p.top_k;
+    const bool dense = kX32 || n_active == p.top_k;
 
     // ---- every weight row of the tile
     const uint32_t qs_row = (FMT == kTernary) ? cols / 4 : cols / 8;
@@ -346,7 +359,7 @@ __global__ __launch_bounds__(kThreads * KS) void k_matvec_tok1(ExpertArgs p, Rou
         }
     }
 
-    if constexpr (ROUTE) {
+    if constexpr (kX32) {
         // ---- q8 of the activations into LDS while the weights are in flight
         const int n4 = cols / 4;
 #pragma unroll
@@ -660,7 +673,40 @@ hipError_t launch_route_fmt(const ExpertArgs& a, const RouteArgs& r, hipStream_t
     }
 }
 
+template <int FMT, int LPR>
+hipError_t launch_x32_one(const ExpertArgs& a, const float* x, hipStream_t s) {
+    constexpr int KS = tok1_kslices<LPR>();   // as the one-token kernel: the same sums
+    RouteArgs ra{};
+    ra.x = x;
+    const unsigned tiles = static_cast<unsigned>((a.rows + kTile - 1) / kTile);
+    hipLaunchKernelGGL((k_matvec_tok1<FMT, LPR, kEpiF32, true, false, 1, KS, true>), dim3(tiles, 1),
+                       dim3(kThreads * KS), 0, s, a, ra);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_x32_fmt(const ExpertArgs& a, const float* x, hipStream_t s) {
+    switch (a.cols / Chunk<FMT>::kWeights) {
+        case 2: return launch_x32_one<FMT, 2>(a, x, s);
+        case 4: return launch_x32_one<FMT, 4>(a, x, s);
+        case 8: return launch_x32_one<FMT, 8>(a, x, s);
+        case 12: return launch_x32_one<FMT, 12>(a, x, s);
+        case 16: return launch_x32_one<FMT, 16>(a, x, s);
+        case 24: return launch_x32_one<FMT, 24>(a, x, s);
+        case 32: return launch_x32_one<FMT, 32>(a, x, s);
+        case 48: return launch_x32_one<FMT, 48>(a, x, s);
+        case 64: return launch_x32_one<FMT, 64>(a, x, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_matvec_x32(Fmt fmt, const ExpertArgs& a, const float* x, hipStream_t s) {
+    if (fmt == kTernary) return launch_x32_fmt<kTernary>(a, x, s);
+    if (fmt == kSign1) return launch_x32_fmt<kSign1>(a, x, s);
+    return launch_x32_fmt<kGrid1>(a, x, s);
+}
 
 hipError_t launch_decode1_gate_up(Fmt fmt, const ExpertArgs& a, const RouteArgs& r, hipStream_t s) {
     if (fmt == kTernary) return launch_route_fmt<kTernary>(a, r, s);

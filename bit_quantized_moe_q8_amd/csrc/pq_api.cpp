@@ -457,6 +457,32 @@ pq_status pq_moe_matvec_ternary(const pq_ternary_w* w, const pq_ternary_w* w_up,
     });
 }
 
+// The single mat-vec from fp32 activations: checks shared by the formats
+// (the weights' own pointers are checked by the caller).
+pq_status x32_check(int32_t n_experts, int32_t rows, int32_t cols, int32_t expert, const float* x, float* y,
+                    pqk::Fmt fmt) {
+    if (!x || !y) return PQ_ERR_NULL;
+    if (n_experts < 1 || expert < 0 || expert >= n_experts) return PQ_ERR_SHAPE;
+    if (rows < 1 || cols < 256 || cols % 256 != 0) return PQ_ERR_SHAPE;
+    if (int64_t(rows) * cols > (int64_t(1) << 31)) return PQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(y, 4)) return PQ_ERR_ALIGN;
+    if (!pqk::matvec_supported(fmt, cols)) return PQ_ERR_UNSUPPORTED;
+    return PQ_OK;
+}
+
+pqk::ExpertArgs x32_args(int32_t n_experts, int32_t rows, int32_t cols, int32_t expert, float* y) {
+    pqk::ExpertArgs a{};
+    a.rows = rows;
+    a.cols = cols;
+    a.n_experts = n_experts;
+    a.n_tokens = 1;
+    a.top_k = 1;
+    a.act_by_token = 1;
+    a.expert0 = expert;
+    a.out0 = y;
+    return a;
+}
+
 pq_status pq_moe_matvec_grid1(const pq_grid1_w* w, const pq_grid1_w* w_up, const pq_groups* g,
                               const int8_t* xq, const float* xd, int32_t act_by_token,
                               int32_t epilogue, void* out0, void* out1, const pq_debug* dbg,
@@ -482,6 +508,52 @@ pq_status pq_moe_matvec_sign1(const pq_sign1_w* w, const pq_sign1_w* w_up, const
                                         pqk::matvec_supported, a, &run);
         if (st != PQ_OK || !run) return st;
         return launch_matvec_any(pqk::kSign1, epilogue, a, dbg, stream);
+    });
+}
+
+pq_status pq_matvec_x32_ternary(const pq_ternary_w* w, int32_t expert, const float* x, float* y,
+                                pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->qs || !w->d) return PQ_ERR_NULL;
+        const pq_status st = x32_check(w->n_experts, w->rows, w->cols, expert, x, y, pqk::kTernary);
+        if (st != PQ_OK) return st;
+        if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+        pqk::ExpertArgs a = x32_args(w->n_experts, w->rows, w->cols, expert, y);
+        a.qs[0] = w->qs;
+        a.d[0] = w->d;
+        return from_hip(pqk::launch_matvec_x32(pqk::kTernary, a, x, as_stream(stream)));
+    });
+}
+
+pq_status pq_matvec_x32_grid1(const pq_grid1_w* w, int32_t expert, const float* x, float* y,
+                              pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->qs || !w->qh || !w->d || !w->grid) return PQ_ERR_NULL;
+        const pq_status st = x32_check(w->n_experts, w->rows, w->cols, expert, x, y, pqk::kGrid1);
+        if (st != PQ_OK) return st;
+        if (!aligned(w->qs, 16) || !aligned(w->qh, 8) || !aligned(w->d, 2) || !aligned(w->grid, 16))
+            return PQ_ERR_ALIGN;
+        pqk::ExpertArgs a = x32_args(w->n_experts, w->rows, w->cols, expert, y);
+        a.qs[0] = w->qs;
+        a.qh[0] = w->qh;
+        a.d[0] = w->d;
+        a.grid = w->grid;
+        return from_hip(pqk::launch_matvec_x32(pqk::kGrid1, a, x, as_stream(stream)));
+    });
+}
+
+pq_status pq_matvec_x32_sign1(const pq_sign1_w* w, int32_t expert, const float* x, float* y,
+                              pq_stream stream) {
+    return guarded([&]() -> pq_status {
+        if (!w || !w->signs || !w->sc || !w->d) return PQ_ERR_NULL;
+        const pq_status st = x32_check(w->n_experts, w->rows, w->cols, expert, x, y, pqk::kSign1);
+        if (st != PQ_OK) return st;
+        if (!aligned(w->signs, 16) || !aligned(w->sc, 4) || !aligned(w->d, 2)) return PQ_ERR_ALIGN;
+        pqk::ExpertArgs a = x32_args(w->n_experts, w->rows, w->cols, expert, y);
+        a.qs[0] = w->signs;
+        a.sc[0] = w->sc;
+        a.d[0] = w->d;
+        return from_hip(pqk::launch_matvec_x32(pqk::kSign1, a, x, as_stream(stream)));
     });
 }
 

@@ -73,6 +73,8 @@ struct ExpertArgs {
     // Experts with at least this many assignments are left to the int8-MFMA
     // tile kernel (which takes exactly those); 0: the mat-vec takes all.
     int heavy_min;
+    // The matrix of the single mat-vec from fp32 activations.
+    int expert0;
 };
 
 // Kernels (PQ_PLAN_* flags) of a q8 expert call of the mat-vec family on
@@ -104,6 +106,11 @@ struct RouteArgs {
 };
 hipError_t launch_decode1_gate_up(Fmt fmt, const ExpertArgs& a, const RouteArgs& r, hipStream_t s);
 bool matvec_supported(Fmt fmt, int cols);
+
+// One mat-vec from fp32 activations x [cols] in one launch: the one-token
+// kernel quantizing x itself (F32 epilogue into a.out0 [rows], matrix
+// a.expert0).
+hipError_t launch_matvec_x32(Fmt fmt, const ExpertArgs& a, const float* x, hipStream_t s);
 
 // Grouped int8-MFMA tile over q8 activations: the mat-vec's arithmetic and
 // epilogues for the experts with at least a.heavy_min (>= 1) assignments.

@@ -280,6 +280,26 @@ pq_status pq_moe_matvec_sign1(const pq_sign1_w *w, const pq_sign1_w *w_up,
                               void *out1, const pq_debug *dbg, pq_stream stream);
 
 /*
+ * One mat-vec from fp32 activations in a single launch (the fused decode
+ * mat-vec of the Parakon Runtime README, "How it works", reading the packed
+ * blocks against int8 activations, with the q8 step inside the launch):
+ *   y float [rows] = W[expert] . q8(x),  x float [cols],
+ * x quantized per 32 by the rule of pq_quantize_act_q8 (the same codes and
+ * scales, computed again by every workgroup into its LDS), then the one-token
+ * arithmetic of pq_moe_matvec_* with PQ_EPI_F32, so y is bit-identical to
+ * pq_quantize_act_q8 followed by that call for one token routed to `expert`.
+ * 0 <= expert < w->n_experts (PQ_ERR_SHAPE otherwise); cols as for
+ * pq_moe_matvec_* of the format (PQ_ERR_UNSUPPORTED otherwise); x 16-byte,
+ * y 4-byte aligned; x finite.  Nothing but y is written; y may not overlap x.
+ */
+pq_status pq_matvec_x32_ternary(const pq_ternary_w *w, int32_t expert, const float *x, float *y,
+                                pq_stream stream);
+pq_status pq_matvec_x32_grid1(const pq_grid1_w *w, int32_t expert, const float *x, float *y,
+                              pq_stream stream);
+pq_status pq_matvec_x32_sign1(const pq_sign1_w *w, int32_t expert, const float *x, float *y,
+                              pq_stream stream);
+
+/*
  * Grouped int8-MFMA tile over q8 activations (a tiled kernel for large
  * batches: Parakon Runtime README, "How it works"; an int8 prefill tile:
  * pxq_llama README, "Updates - 2026-07-19").  Arguments, layouts, epilogues

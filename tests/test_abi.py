@@ -147,6 +147,35 @@ def test_sign1_validation(L):
     assert f(b(ok_w), None, b(_groups(pq, T=0)), None, None, 1, 0, A16, None, None, S) == pq.PQ_OK
 
 
+def test_matvec_x32_validation(L):
+    import bit_quantized_moe_q8_amd as pq
+    b = ctypes.byref
+    t, gr, sg = L.pq_matvec_x32_ternary, L.pq_matvec_x32_grid1, L.pq_matvec_x32_sign1
+    ok_t = pq.TernaryW(A16, A16, 2, 64, 1024)
+    # NULL weights, x or y
+    assert t(None, 0, A16, A16, S) == pq.PQ_ERR_NULL
+    assert t(b(pq.TernaryW(None, A16, 2, 64, 1024)), 0, A16, A16, S) == pq.PQ_ERR_NULL
+    assert t(b(ok_t), 0, None, A16, S) == pq.PQ_ERR_NULL
+    assert t(b(ok_t), 0, A16, None, S) == pq.PQ_ERR_NULL
+    # expert outside [0, n_experts)
+    assert t(b(ok_t), 2, A16, A16, S) == pq.PQ_ERR_SHAPE
+    assert t(b(ok_t), -1, A16, A16, S) == pq.PQ_ERR_SHAPE
+    # cols not a multiple of 256, rows < 1
+    assert t(b(pq.TernaryW(A16, A16, 2, 64, 1000)), 0, A16, A16, S) == pq.PQ_ERR_SHAPE
+    assert t(b(pq.TernaryW(A16, A16, 2, 0, 1024)), 0, A16, A16, S) == pq.PQ_ERR_SHAPE
+    # misaligned x (16 bytes), codes
+    assert t(b(ok_t), 0, ctypes.c_void_p(0x10004), A16, S) == pq.PQ_ERR_ALIGN
+    assert t(b(pq.TernaryW(A1, A16, 2, 64, 1024)), 0, A16, A16, S) == pq.PQ_ERR_ALIGN
+    # an unsupported (valid) width: cols/64 = 20
+    assert t(b(pq.TernaryW(A16, A16, 2, 64, 1280)), 0, A16, A16, S) == pq.PQ_ERR_UNSUPPORTED
+    assert gr(b(pq.Grid1W(A16, A16, A16, None, 1, 64, 1024)), 0, A16, A16, S) == pq.PQ_ERR_NULL
+    assert gr(b(pq.Grid1W(A16, A16, A16, A1, 1, 64, 1024)), 0, A16, A16, S) == pq.PQ_ERR_ALIGN
+    assert gr(b(pq.Grid1W(A16, A16, A16, A16, 1, 64, 2560)), 0, A16, A16, S) == pq.PQ_ERR_UNSUPPORTED
+    assert sg(b(pq.Sign1W(A16, None, A16, 1, 64, 1024)), 0, A16, A16, S) == pq.PQ_ERR_NULL
+    assert sg(b(pq.Sign1W(A16, A1, A16, 1, 64, 1024)), 0, A16, A16, S) == pq.PQ_ERR_ALIGN
+    assert sg(b(pq.Sign1W(A16, A16, A16, 1, 64, 1024)), 1, A16, A16, S) == pq.PQ_ERR_SHAPE
+
+
 def test_tile_q8_validation(L):
     """The int8-MFMA tile entry points share the mat-vec's checks but accept
     any cols that is a multiple of 256 (e.g. 1280, which the mat-vec rejects)."""

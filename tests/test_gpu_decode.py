@@ -174,6 +174,47 @@ def test_ternary_matvec_1024_single_matrix():
     assert_equal(to_host(out2), to_host(out), "debug vs production variant")
 
 
+@pytest.mark.parametrize("fmt,E,N,K,expert", [
+    ("ternary", 1, 1024, 1024, 0),    # the single-matrix workload's shape
+    ("ternary", 3, 100, 256, 2),      # smallest K, ragged rows
+    ("ternary", 2, 72, 2048, 1),      # K split over four wave groups
+    ("ternary", 2, 40, 4096, 0),      # the widest ternary row
+    ("ternary", 2, 33, 768, 1),       # 12 lanes per row
+    ("grid1", 2, 64, 4096, 1),
+    ("grid1", 1, 40, 1536, 0),
+    ("grid1", 1, 16, 8192, 0),        # the widest grid1 row
+    ("sign1", 2, 72, 2048, 1),
+    ("sign1", 1, 40, 6144, 0),
+])
+def test_matvec_x32_single_launch(fmt, E, N, K, expert):
+    """pq_matvec_x32_*: one launch that quantizes the fp32 row itself; y
+    bit-identical to pq_quantize_act_q8 + the one-token mat-vec of the same
+    expert, and within the stated bound of the oracle (q8 by the oracle's
+    rule, then the q8 mat-vec)."""
+    say("matvec x32", fmt, E, N, K, expert)
+    seed = zlib.crc32(repr((fmt, E, N, K)).encode()) % 1000
+    planes = wl.stack_experts(fmt, seed, "w", E, N, K)
+    grid = wl.codebook(seed) if fmt == "grid1" else None
+    x = wl.activations_f32(seed, 1, K)
+    W = weights_to_device(fmt, planes, grid)
+    xd_dev = to_dev(x)
+    y = pq.matvec_x32(W, xd_dev.view(-1), expert)
+    # the two-launch pair: q8, then the one-token kernel for one token routed to `expert`
+    xq_d, xdd = pq.quantize_act_q8(xd_dev)
+    g = pq.group_tokens_by_expert(to_dev(np.full((1, 1), expert, np.int32)), E)
+    mv = {"ternary": pq.moe_matvec_ternary, "grid1": pq.moe_matvec_grid1, "sign1": pq.moe_matvec_sign1}[fmt]
+    out, _ = mv(W, None, g, xq_d, xdd, True, pq.PQ_EPI_F32)
+    torch.cuda.synchronize()
+    assert_equal(to_host(y), to_host(out)[0], "single launch vs q8 + mat-vec")
+    xq, xd = oracle.quantize_q8(x)
+    y_ref, t_ref, _ = moe.grouped_matvec_q8(fmt, planes, grid, np.full((1, 1), expert, np.int32), xq, xd,
+                                            np.zeros(1, np.int64), K, False)
+    assert_tol(to_host(y), y_ref[0], t_ref[0], "y")
+    # a second call into the same output gives the same bits
+    y2 = pq.matvec_x32(W, xd_dev.view(-1), expert, y=torch.full_like(y, 7.0))
+    assert_equal(to_host(y2), to_host(y), "repeat")
+
+
 @pytest.mark.parametrize("fmt,E,N,K,T,k,abt", [
     ("ternary", 4, 96, 256, 1, 2, True),      # smallest K, ragged rows (3 tiles)
     ("ternary", 8, 100, 768, 3, 2, True),     # 12 lanes per row, ragged tail tile
