@@ -392,7 +392,7 @@ def bench_layer_workload(name, args, peaks):
     kfiles = (["k_gemm.hip"] if plan & pq.PQ_PLAN_GEMM else
               ["k_matvec1.hip"] if plan & pq.PQ_PLAN_DECODE1_ROUTED else
               (["k_matvec.hip"] if plan & (pq.PQ_PLAN_MATVEC | pq.PQ_PLAN_MATVEC_PAIRS) else []) +
-              (["k_tile_q8.hip"] if plan & pq.PQ_PLAN_TILE_Q8 else []))
+              (["k_tile_q8.hip", "k_tile_q8.hpp"] if plan & pq.PQ_PLAN_TILE_Q8 else []))
     traffic = measured_traffic(name, kfiles + ["pq_device.hpp", "pq_internal.hpp"])
     if prefill or q8_prefill:
         ops = 2.0 * T * k * 2 * I * H
@@ -410,6 +410,9 @@ def bench_layer_workload(name, args, peaks):
         kbytes = sum(n_active[i % L] * 2 * per_matrix for i in range(R)) / R
         ach = kbytes / (avg_ms * 1e-3) / 1e9
         kname = ("k_matvec_tok1 (one token: routing, q8, gate/up, SwiGLU+q8 epilogue)" if decode1
+                 else "k_matvec_mixed (gate/up in one launch, SwiGLU+q8 epilogue: experts with 8+ "
+                      "assignments on the int8-MFMA tile, the rest on the mat-vec)"
+                 if plan & pq.PQ_PLAN_MIXED
                  else "k_tile_q8 + k_matvec (gate/up, SwiGLU+q8 epilogue; experts with 8+ "
                       "assignments on the int8-MFMA tile, the rest on the mat-vec)"
                  if plan & pq.PQ_PLAN_TILE_Q8 else "k_matvec (gate/up, SwiGLU+q8 epilogue)")

@@ -23,7 +23,7 @@ PQ_EPI_F32, PQ_EPI_SWIGLU_Q8, PQ_EPI_SWIGLU_BF16, PQ_EPI_F32_COMBINE = 0, 1, 2, 
 PQ_FMT = {"ternary": 0, "grid1": 1, "sign1": 2}
 PQ_CALL_MATVEC, PQ_CALL_TILE_Q8, PQ_CALL_GEMM, PQ_CALL_DECODE1_GATE_UP = 0, 1, 2, 3
 (PQ_PLAN_MATVEC, PQ_PLAN_MATVEC_PAIRS, PQ_PLAN_MATVEC_TOK1, PQ_PLAN_TILE_Q8, PQ_PLAN_GEMM,
- PQ_PLAN_DECODE1_ROUTED, PQ_PLAN_DEBUG) = 1, 2, 4, 8, 16, 32, 64
+ PQ_PLAN_DECODE1_ROUTED, PQ_PLAN_DEBUG, PQ_PLAN_MIXED) = 1, 2, 4, 8, 16, 32, 64, 128
 
 EXPORTS = (
     "pq_quantize_act_q8", "pq_moe_route_topk", "pq_group_tokens_by_expert", "pq_moe_decode_prep",

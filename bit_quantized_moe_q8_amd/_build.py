@@ -23,8 +23,10 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 # The int8 MFMA tile converts every MFMA result with VALU instructions, which
-# cannot read accumulation registers: results go straight to VGPRs.
-FILE_FLAGS = {"k_tile_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# cannot read accumulation registers: results go straight to VGPRs (the
+# mat-vec file holds the tile's body too, for the skewed-decode launch).
+FILE_FLAGS = {"k_tile_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "k_matvec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _stale(src: str, obj: str) -> bool:

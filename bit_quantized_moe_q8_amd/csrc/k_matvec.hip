@@ -60,6 +60,7 @@
 // xd * isum), then the cross-lane sum.
 #include "pq_device.hpp"
 #include "pq_internal.hpp"
+#include "k_tile_q8.hpp"
 
 namespace pqk {
 
@@ -120,10 +121,11 @@ constexpr int tall_shift() {
 // shapes than the two their natural 171 VGPRs allow; four spills too much.
 constexpr int kGrid1WavesPerSimd = 3;
 
-template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((FMT != kTernary && MT == 1 && !DBG) ? kGrid1WavesPerSimd : 1)))
-void k_matvec(ExpertArgs p) {
+// The kernel body for workgroup `bid` of `nblk` (the grouped mat-vec's own
+// launch, or the workgroups after the tile's in the skewed-decode launch),
+// with DEPTH row iterations of weight loads in flight per wave.
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG, int DEPTH>
+__device__ __forceinline__ void matvec_body(const ExpertArgs& p, int bid, int nblk) {
     using FI = FmtInfo<FMT>;
     constexpr int LS = RowGeom<LPR>::LS;
     constexpr int RPW = kWave / LS;               // row slots per wave
@@ -132,7 +134,7 @@ void k_matvec(ExpertArgs p) {
     constexpr int TR = kTileRows << TS;                 // output rows per tile
     constexpr int P = TR * NMAT;                        // physical rows per tile
     constexpr int ITERS = (P + ROWS_IT - 1) / ROWS_IT;  // row iterations per tile
-    constexpr int D = ITERS < kDepth ? ITERS : kDepth;
+    constexpr int D = ITERS < DEPTH ? ITERS : DEPTH;
     constexpr int SUBS = FI::kSubs;
     constexpr int ACT_DW = FI::kChunkWeights / 4;  // activation dwords per chunk
 
@@ -293,8 +295,8 @@ void k_matvec(ExpertArgs p) {
     };
 
     Meta cur;
-    if (static_cast<int>(blockIdx.x) < n_items) fetch_meta(blockIdx.x, cur);
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    if (bid < n_items) fetch_meta(bid, cur);
+    for (int item = bid; item < n_items; item += nblk) {
         const int e = cur.e, tile = cur.tile, beg = cur.beg, m = cur.m;
         const int n0 = tile * TR;
         int base = cur.base;
@@ -306,7 +308,7 @@ void k_matvec(ExpertArgs p) {
 #pragma unroll
         for (int i = 0; i < D; ++i) buf[i] = load_row(e, n0, i);
 
-        const int next_item = item + gridDim.x;
+        const int next_item = item + nblk;
         Meta nxt = cur;
         bool first_pass = true;
         for (;;) {
@@ -525,6 +527,32 @@ void k_matvec(ExpertArgs p) {
 }
 
 template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu((FMT != kTernary && MT == 1 && !DBG) ? kGrid1WavesPerSimd : 1)))
+void k_matvec(ExpertArgs p) {
+    matvec_body<FMT, LPR, MT, EPI, SPLIT, TS, DBG, kDepth>(p, blockIdx.x, gridDim.x);
+}
+
+// Skewed decode batches (ternary): the heavy experts' int8-MFMA tile items
+// (chunks of up to 32 assignments) in the first n_tile workgroups and the
+// other experts' mat-vec items (pairs of assignments) in the rest, one launch
+// instead of two back to back, so the tile's few long item chains run beside
+// the mat-vec stream.  The tile's registers set the occupancy (three waves
+// per SIMD instead of the mat-vec's five; twice the weight loads in flight
+// per mat-vec wave measured no faster).
+
+template <int LPR, int EPI, int TS, bool DBG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DBG ? 1 : 3)))
+void k_matvec_mixed(ExpertArgs p, int n_tile) {
+    static_assert(kThreads == tq8::kThreads, "one workgroup shape for both parts");
+    if (static_cast<int>(blockIdx.x) < n_tile)
+        tq8::tile_q8_body<kTernary, EPI, DBG, 32>(p, blockIdx.x, n_tile);
+    else
+        matvec_body<kTernary, LPR, 2, EPI, true, TS, DBG, kDepth>(p, blockIdx.x - n_tile,
+                                                                         gridDim.x - n_tile);
+}
+
+template <int FMT, int LPR, int MT, int EPI, bool SPLIT, int TS, bool DBG>
 hipError_t launch_one(const ExpertArgs& a, int64_t groups, hipStream_t s) {
     auto kernel = k_matvec<FMT, LPR, MT, EPI, SPLIT, TS, DBG>;
     // Persistent grid of up to 8 workgroups per CU (more than are resident:
@@ -603,7 +631,68 @@ hipError_t launch_fmt(Epi epi, const ExpertArgs& a, bool pairs, hipStream_t s) {
     }
 }
 
+// The skewed-decode launch (k_matvec_mixed): the tile's grid first (at most
+// one workgroup per compute unit: its item count is only bounded on the
+// host, and its spare workgroups would hold slots the mat-vec's need), then
+// the mat-vec's (the same grid and tall-tile choice as its own launch).
+template <int LPR, int EPI, bool DBG, int TS>
+hipError_t launch_mixed_ts(const ExpertArgs& a, int64_t groups, hipStream_t s) {
+    const int64_t tg = tq8::tile_grid<EPI, 32>(a), cus = cu_count();
+    const int64_t n_tile = tg < cus ? tg : cus;
+    const int tr = kTileRows << TS;
+    const int64_t max_items = groups * ((a.rows + tr - 1) / tr);
+    const int64_t cap = static_cast<int64_t>(cu_count()) * 8;
+    int64_t gm = max_items < cap ? max_items : cap;
+    if (gm < 1) gm = 1;
+    hipLaunchKernelGGL((k_matvec_mixed<LPR, EPI, TS, DBG>), dim3(static_cast<unsigned>(n_tile + gm)), dim3(kThreads),
+                       0, s, a, static_cast<int>(n_tile));
+    return hipGetLastError();
+}
+
+template <int LPR, int EPI, bool DBG>
+hipError_t launch_mixed_dbg(const ExpertArgs& a, hipStream_t s) {
+    constexpr int NMAT = (EPI == kEpiSwigluQ8) ? 2 : 1;
+    constexpr int TALL = tall_shift<LPR, NMAT>();
+    const int64_t A = static_cast<int64_t>(a.n_tokens) * a.top_k;
+    const int64_t slots = A < a.n_experts ? A : a.n_experts;
+    const int64_t groups = (A + 1) / 2 + slots;   // pairs of assignments
+    if constexpr (TALL > 0) {
+        const int tr = kTileRows << TALL;
+        if (groups * ((a.rows + tr - 1) / tr) >= 4 * static_cast<int64_t>(cu_count()))
+            return launch_mixed_ts<LPR, EPI, DBG, TALL>(a, groups, s);
+    }
+    return launch_mixed_ts<LPR, EPI, DBG, 0>(a, groups, s);
+}
+
+template <int LPR>
+hipError_t launch_mixed_lpr(Epi epi, const ExpertArgs& a, hipStream_t s) {
+    if (epi == kEpiF32)
+        return a.debug ? launch_mixed_dbg<LPR, kEpiF32, true>(a, s) : launch_mixed_dbg<LPR, kEpiF32, false>(a, s);
+    return a.debug ? launch_mixed_dbg<LPR, kEpiSwigluQ8, true>(a, s) : launch_mixed_dbg<LPR, kEpiSwigluQ8, false>(a, s);
+}
+
+
+hipError_t launch_mixed(Epi epi, const ExpertArgs& a, hipStream_t s) {
+    switch (a.cols / FmtInfo<kTernary>::kChunkWeights) {
+        case 12: return launch_mixed_lpr<12>(epi, a, s);
+        case 32: return launch_mixed_lpr<32>(epi, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+// Whether the skewed-decode launch covers a call (ternary, fp32 or SwiGLU
+// epilogue, tile chunks of 32, and the row lengths it is built for: 768 and
+// 2048 weights, the down and gate/up rows of the ternary decode FFN; each
+// row length is 4-8 more kernels of both bodies to compile); otherwise the
+// tile and the mat-vec run as two launches.
+bool mixed_planned(Fmt fmt, Epi epi, int n_tokens, int top_k, int cols) {
+    const int64_t A = static_cast<int64_t>(n_tokens) * top_k;
+    if (fmt != kTernary || (epi != kEpiF32 && epi != kEpiSwigluQ8) || A > tq8::kSmallChunkMaxAssign) return false;
+    const int lpr = cols / FmtInfo<kTernary>::kChunkWeights;
+    return cols % FmtInfo<kTernary>::kChunkWeights == 0 && (lpr == 12 || lpr == 32);
+}
 
 bool matvec_supported(Fmt fmt, int cols) {
     const int cw = (fmt == kTernary) ? 64 : 128;   // grid1 and sign1: 128
@@ -623,6 +712,8 @@ hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s) {
     m.heavy_min = 0;
     if (plan & PQ_PLAN_TILE_Q8) {
         m.heavy_min = kHeavyMin;
+        if ((plan & PQ_PLAN_MATVEC_PAIRS) && mixed_planned(fmt, epi, m.n_tokens, m.top_k, m.cols))
+            return launch_mixed(epi, m, s);
         const hipError_t err = launch_tile_q8(fmt, epi, m, s);
         if (err != hipSuccess) return err;
     }

@@ -813,9 +813,14 @@ int32_t pq_plan(int32_t call, int32_t fmt, int32_t n_tokens, int32_t top_k, int3
         if (rows < 1 || cols < 256 || cols % 256 != 0) return -PQ_ERR_SHAPE;
         const int dbg = debug ? PQ_PLAN_DEBUG : 0;
         switch (call) {
-            case PQ_CALL_MATVEC:
+            case PQ_CALL_MATVEC: {
                 if (!pqk::matvec_supported(f, cols)) return -PQ_ERR_UNSUPPORTED;
-                return pqk::plan_matvec(n_tokens, top_k, n_experts, cols, debug != 0);
+                int p = pqk::plan_matvec(n_tokens, top_k, n_experts, cols, debug != 0);
+                if ((p & PQ_PLAN_TILE_Q8) && (p & PQ_PLAN_MATVEC_PAIRS) &&
+                    pqk::mixed_planned(f, static_cast<pqk::Epi>(epilogue), n_tokens, top_k, cols))
+                    p |= PQ_PLAN_MIXED;
+                return p;
+            }
             case PQ_CALL_TILE_Q8:
                 if (!pqk::tile_q8_supported(cols)) return -PQ_ERR_UNSUPPORTED;
                 return n_tokens ? (PQ_PLAN_TILE_Q8 | dbg) : 0;

@@ -82,6 +82,10 @@ struct ExpertArgs {
 // launcher of that family and pq_plan share.
 int plan_matvec(int n_tokens, int top_k, int n_experts, int cols, bool debug);
 
+// Whether a mat-vec call whose plan has PQ_PLAN_TILE_Q8 | PQ_PLAN_MATVEC_PAIRS
+// runs both in one launch (PQ_PLAN_MIXED).
+bool mixed_planned(Fmt fmt, Epi epi, int n_tokens, int top_k, int cols);
+
 // Decode mat-vec; returns hipErrorInvalidValue when no kernel matches cols.
 hipError_t launch_matvec(Fmt fmt, Epi epi, const ExpertArgs& a, hipStream_t s);
 

@@ -99,7 +99,8 @@ enum {
     PQ_PLAN_TILE_Q8 = 8,         /* int8-MFMA tile (every expert, or with MATVEC_PAIRS those of 8+ assignments) */
     PQ_PLAN_GEMM = 16,           /* bf16 dequant-per-tile MFMA GEMM */
     PQ_PLAN_DECODE1_ROUTED = 32, /* one-token gate/up that routes and quantizes itself */
-    PQ_PLAN_DEBUG = 64           /* the kernels' debug variants (dbg != NULL) */
+    PQ_PLAN_DEBUG = 64,          /* the kernels' debug variants (dbg != NULL) */
+    PQ_PLAN_MIXED = 128          /* with TILE_Q8 | MATVEC_PAIRS: both in one launch (ternary, rows of 768 or 2048) */
 };
 
 /* hipStream_t, passed as an opaque pointer; NULL = null stream. */

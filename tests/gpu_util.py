@@ -120,7 +120,7 @@ def q8h_check(hq_gpu, hd_gpu, g_ref, u_ref, tg, tu, what="q8(h)"):
 _PLAN_NAMES = {pq.PQ_PLAN_MATVEC: "matvec", pq.PQ_PLAN_MATVEC_PAIRS: "matvec-pairs",
                pq.PQ_PLAN_MATVEC_TOK1: "matvec-tok1", pq.PQ_PLAN_TILE_Q8: "tile-q8",
                pq.PQ_PLAN_GEMM: "gemm", pq.PQ_PLAN_DECODE1_ROUTED: "decode1-routed",
-               pq.PQ_PLAN_DEBUG: "debug"}
+               pq.PQ_PLAN_DEBUG: "debug", pq.PQ_PLAN_MIXED: "mixed"}
 
 
 def plan_str(flags):

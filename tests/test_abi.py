@@ -324,7 +324,7 @@ def test_plan_of_each_workload():
         assert pq.plan(P.PQ_CALL_MATVEC, fmt, 8, 8, 256, 1536, 4096, P.PQ_EPI_SWIGLU_Q8) == P.PQ_PLAN_MATVEC
     # 64 skewed tokens: pairs of assignments, heavy experts on the tile
     assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 64, 8, 256, 768, 2048, P.PQ_EPI_SWIGLU_Q8) == \
-        P.PQ_PLAN_MATVEC_PAIRS | P.PQ_PLAN_TILE_Q8
+        P.PQ_PLAN_MATVEC_PAIRS | P.PQ_PLAN_TILE_Q8 | P.PQ_PLAN_MIXED
     # fewer than 8 tokens but more assignments than experts: pairs, no tile
     assert pq.plan(P.PQ_CALL_MATVEC, "ternary", 4, 2, 3, 256, 512) == P.PQ_PLAN_MATVEC_PAIRS
     # 2048 tokens with q8 activations: the mat-vec entry hands every expert
