@@ -403,6 +403,16 @@ def test_binding_rejects_undersized_buffers():
     bad_d = pq.TernaryWeights(W.qs, torch.zeros((16, 64, 2), dtype=torch.int16))
     with pytest.raises(ValueError, match="d has shape"):
         pq.moe_matvec_ternary(bad_d, None, g, xq12, xd12, False, pq.PQ_EPI_F32, torch.zeros((12, 64), dtype=f32))
+    # single mat-vec from fp32 activations: expert range, x and y sizes, dtype
+    x256 = torch.zeros(256, dtype=f32)
+    with pytest.raises(ValueError, match="expert"):
+        pq.matvec_x32(W, x256, 16)
+    with pytest.raises(ValueError, match="x holds"):
+        pq.matvec_x32(W, torch.zeros(255, dtype=f32), 0)
+    with pytest.raises(ValueError, match="y holds"):
+        pq.matvec_x32(W, x256, 0, torch.zeros(63, dtype=f32))
+    with pytest.raises(TypeError):
+        pq.matvec_x32(W, torch.zeros(256, dtype=torch.float16), 0)
     # GEMM and combine
     Wg = pq.Grid1Weights(torch.zeros((16, 64, 32), dtype=torch.uint8), torch.zeros((16, 64, 8), dtype=torch.int16),
                          torch.zeros((16, 64, 1), dtype=torch.int16), torch.zeros((2048, 8), dtype=i8), tiled=True)
