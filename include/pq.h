@@ -364,8 +364,11 @@ pq_status pq_tile_layout_sign1(const pq_sign1_w *w, uint8_t *signs_tiled, uint8_
  * Prefill: grouped dequant-per-tile GEMM over grid1 weights with bf16
  * activations on MFMA (Parakon Runtime README, "How it works": prompt
  * processing at large batch sizes uses a dequant-per-tile GEMM path).  Packed
- * blocks are decoded to bf16 {-1,0,+1} on chip only; each 256-column block is
- * accumulated in fp32 and scaled by its fp16 scale in fp32.
+ * blocks are decoded to bf16 {-1,0,+1} on chip only; the exact products are
+ * accumulated in fp32 and each 256-column block's fp16 scale is applied in
+ * fp32 (to one running accumulator per output, rescaled by the ratio of
+ * consecutive nonzero block scales: within about 3e-6 * sum|terms| of
+ * scaling each block sum on its own, inside the fp32 tolerance).
  *   w, w_up: qs and qh in the tile layout (pq_tile_layout_grid1), d and grid
  *            as in pq_grid1_w.  rows % 8 == 0 (PQ_ERR_SHAPE otherwise).
  *   x: bf16 bits, [n_tokens][cols] if act_by_token else [A][cols]; 16-byte aligned.
@@ -391,9 +394,9 @@ pq_status pq_moe_gemm_dequant_tile(const pq_grid1_w *w, const pq_grid1_w *w_up,
 /*
  * The same GEMM over sub-scaled sign weights (pq_sign1_w; pxq_llama README,
  * "What's PXQ?", PXQ1): each weight is decoded on chip to the bf16 of
- * sign * sc (exact, |w| <= 15) and every 256-column block is scaled by the
- * row's fp16 anchor in fp32, so out = sum_b d[n] * sum_{k in b} x[k] * sign *
- * sc, within the fp32 tolerance of the definition.  signs and sc in the tile
+ * sign * sc (exact, |w| <= 15) and the fp32 sum over the row is scaled by the
+ * row's fp16 anchor (the scale of every block), so out = sum_b d[n] *
+ * sum_{k in b} x[k] * sign * sc, within the fp32 tolerance of the definition.  signs and sc in the tile
  * layout (pq_tile_layout_sign1), d as in pq_sign1_w.  cols % 512 == 0; signs
  * and sc 16-byte aligned; otherwise as pq_moe_gemm_dequant_tile.
  */
