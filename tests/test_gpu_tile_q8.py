@@ -158,7 +158,9 @@ def test_tile_q8_combine(fmt, E, H, I, T, k):
 
 
 @pytest.mark.parametrize("fmt,K,E,T", [("ternary", 768, 16, 40), ("grid1", 1024, 16, 40), ("ternary", 512, 1024, 600),
-                                       ("sign1", 1024, 16, 40), ("sign1", 2048, 256, 300)])
+                                       ("sign1", 1024, 16, 40), ("sign1", 2048, 256, 300),
+                                       ("ternary", 2048, 64, 1024),    # 2048 assignments: the one-launch limit
+                                       ("ternary", 768, 64, 1100)])    # 2200: tile (chunks of 64) then mat-vec
 def test_matvec_hands_heavy_experts_to_tile(fmt, K, E, T):
     """Through pq_moe_matvec_*: T tokens, top-2 of E experts (more
     assignments than experts, so the split grouping runs), every token's
@@ -169,7 +171,7 @@ def test_matvec_hands_heavy_experts_to_tile(fmt, K, E, T):
     N, k = 96, 2
     assert T * k > E
     # ternary rows of 768 or 2048: the tile and the mat-vec items in one launch
-    mixed = pq.PQ_PLAN_MIXED if fmt == "ternary" and K in (768, 2048) else 0
+    mixed = pq.PQ_PLAN_MIXED if fmt == "ternary" and K in (768, 2048) and T * k <= 2048 else 0
     assert_plan(pq.PQ_PLAN_MATVEC_PAIRS | pq.PQ_PLAN_TILE_Q8 | mixed, pq.PQ_CALL_MATVEC, fmt, T, k, E, N, K)
     seed = _seed("dispatch", fmt, K, E)
     rng = np.random.default_rng(seed)
