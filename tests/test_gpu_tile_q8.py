@@ -247,14 +247,19 @@ def test_q8_prefill_full_size_sampled(name):
     assert_tol(to_host(layer.y)[toks], y_ref, ty, "y")
 
 
-def test_heavy_split_layer_in_captured_graph():
+@pytest.mark.parametrize("H,I", [(512, 256), (2048, 768)])
+def test_heavy_split_layer_in_captured_graph(H, I):
     """A layer step whose mat-vec entry points launch the tile kernel for a
-    heavy expert and the mat-vec for the rest, captured in a graph, replays
-    to the eager step's bits, three times, with eager work on the same
-    buffers between the replays."""
+    heavy expert and the mat-vec for the rest (rows of 2048 and 768: both in
+    one launch), captured in a graph, replays to the eager step's bits,
+    three times, with eager work on the same buffers between the replays."""
     from bit_quantized_moe_q8_amd.layer import DecodeLayer
-    say("heavy split layer in graph")
-    fmt, T, H, I, E, k = "ternary", 16, 512, 256, 8, 2
+    say("heavy split layer in graph", H, I)
+    fmt, T, E, k = "ternary", 16, 8, 2
+    mixed = pq.PQ_PLAN_MIXED if (H, I) == (2048, 768) else 0
+    assert_plan(pq.PQ_PLAN_MATVEC_PAIRS | pq.PQ_PLAN_TILE_Q8 | mixed, pq.PQ_CALL_MATVEC, fmt, T, k, E, I, H,
+                pq.PQ_EPI_SWIGLU_Q8)
+    assert_plan(pq.PQ_PLAN_MATVEC_PAIRS | pq.PQ_PLAN_TILE_Q8 | mixed, pq.PQ_CALL_MATVEC, fmt, T, k, E, H, I)
     rng = np.random.default_rng(5)
     logits = rng.standard_normal((T, E)).astype(np.float32)
     logits[:, 0] += 8.0          # expert 0 in every token's top-2: 16 assignments
